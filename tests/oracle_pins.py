@@ -1,0 +1,407 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Every pin is a function ``pin_<name>(o)`` taking an ``oracle.Oracle`` and
+raising AssertionError when the oracle disagrees with:
+  * values the pages print (the camera-distance worked example),
+  * closed forms that follow from the pages' statements (corner registration
+    at the closed-form distance, the half-texel mapping, border clamping of
+    the source index, on-axis points at the image centre, the -Z view),
+  * brute force (bilinear weights as tent functions summed over every pixel),
+  * library routines the special cases reduce to (torch grid_sample on CPU,
+    numpy float64 matmul, torch's bfloat16 rounding).
+The same functions run against deliberately broken oracle builds (see
+test_oracle_mutants.py) to show that each plausible mistake fails one of them.
+
+Sources, by page title and section:
+  pixal3d_mrp_mlx, history of tests/, commit landing the pixel-aligned head
+    (grid_sample mapping, border clamp of the source index, -Z camera);
+  trellis.cpp PR #38 "Initial support for Pixal3D": commit adding pixal3d.cpp
+    (closed-form camera solve), commit exposing extend_pixel (worked example),
+    commit adding projection diagnostics (cube corners legitimately leave the
+    frame), commit introducing FlowCond (null proj zeroed).
+"""
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rel(a, b, scale):
+    return np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)) / scale)
+
+
+# ----------------------------------------------------------------- camera ---
+def pin_camera_distance_worked_example(o):
+    """The printed distances at 49.13 deg / 512 px / e = 0, 64, 128."""
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "camera_distance.txt"))
+            if l.strip() and not l.startswith("#")]
+    assert len(rows) == 3
+    for fov, size, ext, printed in rows:
+        d = o.distance_from_fov(float(fov), int(size), int(ext))
+        assert abs(d - float(printed)) <= 5e-4 + 1e-12, (fov, size, ext, d, printed)
+        assert "%.3f" % d == printed, (d, printed)
+
+
+def pin_corner_registration(o):
+    """At the closed-form distance the cube's z = 0 corners land on the frame
+    border (|g| -> 1), which holds only for focal = 1/tan(fov/2) with the
+    full-angle FOV, depth = d - z and unit-cube extent +-1/2. Cell centres
+    approach the corner as 1/2 - 1/(2R); the exact g is 1 - 1/R."""
+    R = 1001
+    mid = (R - 1) // 2
+    cells = np.array([[0, R - 1, R - 1, mid], [0, 0, 0, mid],
+                      [0, R - 1, 0, mid], [0, 0, R - 1, mid]], np.int32)
+    for fov in (30.0, 40.0, 49.13, 60.0):
+        f, d = o.camera(fov, o.distance_from_fov(fov, 512, 0))
+        p = o.project(cells, 4, R, [f], [d], 64, 64)
+        want = 1.0 - 1.0 / R
+        sx = np.array([1, -1, 1, -1])
+        sy = np.array([-1, 1, 1, -1])
+        assert _rel(p["grid"][:, 0], sx * want, 1.0) < 2e-6, (fov, p["grid"])
+        assert _rel(p["grid"][:, 1], sy * want, 1.0) < 2e-6, (fov, p["grid"])
+        assert p["mask"].tolist() == [1, 1, 1, 1]
+
+
+def pin_near_far_corners(o):
+    """Camera at +d looking down -Z: the near face (z = +1/2) is magnified past
+    the border and the far face (z = -1/2) shrinks inside it, so near corners
+    fall outside the frame (as the pages say they legitimately do) and far
+    corners inside. Exact closed form in binary64 for the cell centres."""
+    R = 64
+    h = 0.5 - 0.5 / R
+    for fov in (30.0, 40.0, 50.0):
+        f, d = o.camera(fov, o.distance_from_fov(fov, 512, 0))
+        cells = np.array([[0, R - 1, R - 1, R - 1], [0, 0, 0, R - 1],
+                          [0, R - 1, R - 1, 0], [0, 0, 0, 0]], np.int32)
+        p = o.project(cells, 4, R, [f], [d], 128, 128)
+        near = float(f) * h / (float(d) - h)
+        far = float(f) * h / (float(d) + h)
+        assert near > 1.0 > far
+        want_x = np.array([near, -near, far, -far])
+        want_y = -want_x
+        assert _rel(p["grid"][:, 0], want_x, 1.0) < 2e-6, (fov, p["grid"], want_x)
+        assert _rel(p["grid"][:, 1], want_y, 1.0) < 2e-6
+        assert _rel(p["depth"], [d - h, d - h, d + h, d + h], 1.0) < 1e-6
+        assert p["mask"].tolist() == [0, 0, 1, 1]
+
+
+def pin_on_axis_centre(o):
+    """Points on the optical axis (x = y = 0, odd R) land exactly on the image
+    centre: g = (0, 0), source index (W-1)/2, i.e. for even W the corners
+    W/2-1 and W/2 with fraction 1/2; for odd W the centre texel, fraction 0."""
+    R = 5
+    c = (R - 1) // 2
+    cells = np.array([[0, c, c, z] for z in range(R)], np.int32)
+    for H, W in ((1, 1), (2, 2), (3, 3), (8, 8), (3, 8), (8, 3)):
+        p = o.project(cells, R, R, [2.0], [1.7], H, W)
+        assert np.all(p["grid"] == 0.0), p["grid"]
+        for axis, size in ((0, W), (1, H)):
+            want_i0 = (size - 1) // 2
+            want_t = 0.5 if size % 2 == 0 else 0.0
+            assert np.all(p["pixel"][:, axis] == want_i0), (H, W, p["pixel"])
+            assert np.all(p["frac"][:, axis] == want_t), (H, W, p["frac"])
+        assert np.all(p["mask"] == 1)
+
+
+def pin_view_handedness(o):
+    """Looking down -Z from +Z: world +x appears on the right half of the
+    image (a camera looking down +Z would mirror it), world +y on the top
+    rows; mirrored cells give mirrored normalised coordinates."""
+    R = 16
+    rng = np.random.default_rng(7)
+    cells = np.concatenate([np.zeros((200, 1), np.int32),
+                            rng.integers(0, R, size=(200, 3)).astype(np.int32)], axis=1)
+    mirror = cells.copy()
+    mirror[:, 1] = R - 1 - cells[:, 1]
+    f, d = o.camera(40.0, 2.0)
+    p = o.project(cells, 200, R, [f], [d], 32, 32)
+    q = o.project(mirror, 200, R, [f], [d], 32, 32)
+    x = (cells[:, 1] + 0.5) / R - 0.5
+    y = (cells[:, 2] + 0.5) / R - 0.5
+    assert np.all(np.sign(p["grid"][:, 0]) == np.sign(x))
+    assert np.all(np.sign(p["grid"][:, 1]) == -np.sign(y))
+    ix = p["pixel"][:, 0] + p["frac"][:, 0]
+    iy = p["pixel"][:, 1] + p["frac"][:, 1]
+    assert np.all((ix > 15.5) == (x > 0)) and np.all((iy < 15.5) == (y > 0))
+    assert _rel(p["grid"][:, 0], -q["grid"][:, 0], 1.0) < 1e-6
+    assert _rel(p["grid"][:, 1], q["grid"][:, 1], 1.0) == 0.0
+
+
+def pin_mask_bounds(o):
+    """Mask = depth > 0 and both normalised coordinates within [-1, 1]
+    (inclusive). With focal 2, distance 3/4 and R = 2, the cell (1, 1, 1) sits
+    at (1/4, 1/4, 1/4): depth 1/2 and g = (1, -1) exactly."""
+    p = o.project(np.array([[0, 1, 1, 1], [0, 0, 0, 1]], np.int32), 2, 2,
+                  [2.0], [0.75], 4, 4)
+    assert p["grid"].tolist() == [[1.0, -1.0], [-1.0, 1.0]]
+    assert p["mask"].tolist() == [1, 1]
+    # distance 0.3: the near half of the cube is behind the camera.
+    R = 8
+    cells = np.array([[0, 3, 4, z] for z in range(R)], np.int32)
+    p = o.project(cells, R, R, [1.0], [0.3], 16, 16)
+    pz = (np.arange(R) + 0.5) / R - 0.5
+    assert np.all((p["depth"] > 0) == (0.3 - pz > 0))
+    assert np.all(p["mask"][0.3 - pz <= 0] == 0)
+    assert np.any(p["mask"][0.3 - pz > 0] == 1)
+
+
+def pin_dense_order_and_batch(o):
+    """Dense enumeration n = ((b R + x) R + y) R + z equals explicit coords
+    in that order; each batch item uses its own camera; a batch column
+    outside [0, batch) is masked out."""
+    R, B = 4, 2
+    n = B * R ** 3
+    t = np.arange(n)
+    coords = np.stack([t // R ** 3, (t // R ** 2) % R, (t // R) % R, t % R], 1).astype(np.int32)
+    fo, di = [1.5, 2.5], [1.2, 2.0]
+    a = o.project(None, n, R, fo, di, 8, 8)
+    b = o.project(coords, n, R, fo, di, 8, 8)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    solo = o.project(coords[R ** 3:] * np.array([0, 1, 1, 1], np.int32), R ** 3, R,
+                     [fo[1]], [di[1]], 8, 8)
+    assert np.array_equal(solo["grid"], a["grid"][R ** 3:])
+    bad = coords[:3].copy()
+    bad[:, 0] = [-1, 2, 7]
+    p = o.project(bad, 3, R, fo, di, 8, 8)
+    assert p["mask"].tolist() == [0, 0, 0]
+
+
+# ----------------------------------------------------------- index mapping ---
+def pin_half_texel(o):
+    """align_corners=False: g = -1 + (2k+1)/W is the centre of texel k, so the
+    source index is exactly k (fraction 0) and the sample is F[k]."""
+    for W in (1, 2, 4, 8, 512):
+        for k in range(W):
+            g = np.float32(-1.0 + (2 * k + 1) / W)
+            i0, i1, t = o.source_index(g, W)
+            assert (i0, i1, t) == (k, min(k + 1, W - 1), 0.0), (W, k, i0, i1, t)
+    for W in (3, 5, 7, 13):
+        feat = np.arange(W, dtype=np.float32).reshape(1, 1, W, 1)
+        g = np.array([[-1.0 + (2 * k + 1) / W, 0.0] for k in range(W)], np.float32)
+        s = o.sample(feat, g)[:, 0]
+        assert _rel(s, np.arange(W), 1.0) < 1e-5, (W, s)
+
+
+def pin_not_align_corners(o):
+    """On the map F[x] = x, g = -0.875 (W = 8) samples 0.0 and g = 0.5 samples
+    5.5; align_corners=True would give 0.4375 and 5.25."""
+    feat = np.arange(8, dtype=np.float32).reshape(1, 1, 8, 1)
+    s = o.sample(feat, np.array([[-0.875, 0.0], [0.5, 0.0]], np.float32))[:, 0]
+    assert s.tolist() == [0.0, 5.5], s
+
+
+def pin_border_clamp_index(o):
+    """padding_mode='border' clamps the SOURCE INDEX before the corners are
+    taken: any g at or beyond the border gives the edge texel with fraction 0
+    (clamping the corners afterwards would give fraction 1/2 at g = +-1 and
+    other weights further out); NaN clamps to texel 0."""
+    for W in (1, 2, 3, 8, 64):
+        for g in (1.0, 1.05, 3.0, 5.0, 1e30, math.inf):
+            assert o.source_index(g, W) == (W - 1, W - 1, 0.0), (W, g, o.source_index(g, W))
+        for g in (-1.0, -1.05, -3.0, -5.0, -1e30, -math.inf, math.nan):
+            assert o.source_index(g, W) == (0, min(1, W - 1), 0.0), (W, g)
+    # inside the outer half texel: clamped to the edge texel, weight 0 on the
+    # (clamped) neighbour
+    assert o.source_index(np.float32(-1.0 + 0.5 / 8), 8) == (0, 1, 0.0)
+    i0, i1, t = o.source_index(np.float32(1.0 - 0.5 / 8), 8)
+    assert (i0, i1, t) == (7, 7, 0.0)
+
+
+# ---------------------------------------------------------------- sampling ---
+def _grid(rng, n, lo=-1.3, hi=1.3):
+    return rng.uniform(lo, hi, size=(n, 2)).astype(np.float32)
+
+
+def _ix(g, size):
+    ix = ((g.astype(np.float64) + 1.0) * size - 1.0) / 2.0
+    return np.clip(ix, 0.0, size - 1.0)
+
+
+def pin_constant_map(o):
+    rng = np.random.default_rng(11)
+    for dt in (np.float32, np.uint16):
+        for (B, H, W, C) in ((1, 5, 7, 3), (2, 8, 8, 4)):
+            k = np.float32(rng.uniform(-4, 4))
+            if dt == np.uint16:
+                feat = np.full((B, H, W, C), o.f32_to_bf16(np.array([k]))[0], np.uint16)
+                k = o.bf16_to_f32(feat.ravel()[:1])[0]
+            else:
+                feat = np.full((B, H, W, C), k, np.float32)
+            g = _grid(rng, 300)
+            bi = rng.integers(0, B, size=300).astype(np.int32)
+            s = o.sample(feat, g, bi)
+            assert _rel(s, k, abs(float(k))) < 4 * 2.0 ** -24, (dt, k)
+
+
+def pin_linear_ramp_map(o):
+    """F = a_c x + b_c (resp. y): bilinear interpolation reproduces the ramp at
+    the clamped source index exactly (up to binary32 weights)."""
+    rng = np.random.default_rng(12)
+    for (H, W) in ((1, 1), (2, 3), (7, 5), (16, 16)):
+        C = 3
+        a = rng.uniform(-2, 2, C)
+        b = rng.uniform(-2, 2, C)
+        xs = np.arange(W, dtype=np.float64)
+        ys = np.arange(H, dtype=np.float64)
+        fx = (a[None, None, :] * xs[None, :, None] + b).astype(np.float32)
+        fx = np.broadcast_to(fx, (H, W, C))[None].copy()
+        fy = (a[None, None, :] * ys[:, None, None] + b).astype(np.float32)
+        fy = np.broadcast_to(fy, (H, W, C))[None].copy()
+        g = _grid(rng, 400, -1.5, 1.5)
+        sx = o.sample(fx, g)
+        sy = o.sample(fy, g)
+        wx = a[None, :] * _ix(g[:, 0], W)[:, None] + b[None, :]
+        wy = a[None, :] * _ix(g[:, 1], H)[:, None] + b[None, :]
+        scale = np.abs(a).max() * max(H, W) + np.abs(b).max()
+        assert _rel(sx, wx, scale) < 1e-6, (H, W)
+        assert _rel(sy, wy, scale) < 1e-6, (H, W)
+
+
+def _tent(u):
+    return np.maximum(0.0, 1.0 - np.abs(u))
+
+
+def pin_brute_force_tent(o):
+    """Bilinear sampling = sum over EVERY texel of tent(ix - j) tent(iy - i)
+    F[i, j], with (ix, iy) the border-clamped source index."""
+    rng = np.random.default_rng(13)
+    for (B, H, W, C) in ((1, 2, 2, 2), (2, 3, 5, 3), (1, 8, 8, 4), (2, 1, 6, 2)):
+        feat = rng.standard_normal((B, H, W, C)).astype(np.float32)
+        g = _grid(rng, 200, -1.6, 1.6)
+        bi = rng.integers(0, B, size=200).astype(np.int32)
+        s = o.sample(feat, g, bi)
+        ix = _ix(g[:, 0], W)
+        iy = _ix(g[:, 1], H)
+        wx = _tent(ix[:, None] - np.arange(W)[None, :])      # [n, W]
+        wy = _tent(iy[:, None] - np.arange(H)[None, :])      # [n, H]
+        want = np.einsum("nh,nw,nhwc->nc", wy, wx, feat[bi].astype(np.float64))
+        # the oracle's source index is binary32 (an ulp of W-1 moves a weight
+        # by ~W 2^-24), the tent sums use the binary64 index
+        assert _rel(s, want, np.abs(feat).max()) < 1e-5, (B, H, W, C)
+
+
+def pin_torch_grid_sample(o):
+    """torch.nn.functional.grid_sample(bilinear, align_corners=False,
+    padding_mode='border') on CPU, the routine the pages diffed against."""
+    import torch
+    rng = np.random.default_rng(14)
+    for (B, H, W, C, n) in ((1, 8, 8, 4, 300), (2, 13, 9, 3, 300), (1, 1, 7, 2, 50),
+                            (2, 32, 32, 16, 500)):
+        feat = rng.standard_normal((B, H, W, C)).astype(np.float32)
+        g = _grid(rng, n, -1.4, 1.4)
+        bi = rng.integers(0, B, size=n).astype(np.int32)
+        s = o.sample(feat, g, bi)
+        inp = torch.from_numpy(feat).permute(0, 3, 1, 2).contiguous()
+        want = np.empty((n, C))
+        for b in range(B):
+            sel = np.nonzero(bi == b)[0]
+            gr = torch.from_numpy(g[sel]).reshape(1, 1, -1, 2)
+            r = torch.nn.functional.grid_sample(inp[b:b + 1], gr, mode="bilinear",
+                                                padding_mode="border", align_corners=False)
+            want[sel] = r[0, :, 0, :].T.double().numpy()
+        scale = np.abs(feat).max()
+        assert _rel(s, want, scale) < 1e-6, (B, H, W, C)
+
+
+# ------------------------------------------------------------------ linear ---
+def pin_numpy_matmul(o):
+    rng = np.random.default_rng(15)
+    for (n, C, D, bf16, with_bias) in ((7, 16, 32, False, True), (33, 64, 48, True, True),
+                                       (5, 8, 16, True, False), (1, 4, 4, False, False)):
+        S = rng.standard_normal((n, C))
+        Wf = (rng.standard_normal((D, C)) * 0.02).astype(np.float32)
+        bf = (rng.standard_normal(D) * 0.02).astype(np.float32)
+        if bf16:
+            Wq, bq = o.f32_to_bf16(Wf), o.f32_to_bf16(bf)
+            Wd, bd = o.bf16_to_f32(Wq).astype(np.float64), o.bf16_to_f32(bq).astype(np.float64)
+        else:
+            Wq, bq, Wd, bd = Wf, bf, Wf.astype(np.float64), bf.astype(np.float64)
+        Y = o.linear(S, Wq, bq if with_bias else None)
+        want = S @ Wd.T + (bd if with_bias else 0.0)
+        scale = np.abs(S) @ np.abs(Wd).T + (np.abs(bd) if with_bias else 0.0)
+        assert np.max(np.abs(Y - want) / scale) < 1e-12
+
+
+# -------------------------------------------------------------------- bf16 ---
+def pin_bf16_rounding(o):
+    """binary32 -> bf16 against torch's round-to-nearest-even conversion, on
+    ties, subnormals, overflow to infinity, infinities and NaN; binary64 ->
+    bf16 against the nearest-even bf16 found by brute force."""
+    import torch
+    edge = np.array([0.0, -0.0, 1.0, -1.0, 1.00390625, 1.01171875, 1.0 + 2 ** -8,
+                     1.0 + 3 * 2 ** -8, 3.3895314e38, 3.3961776e38, 3.4e38, 1e-40, -1e-40,
+                     1.18e-38, 2 ** -133, np.inf, -np.inf], np.float32)
+    rng = np.random.default_rng(16)
+    x = np.concatenate([edge, (rng.standard_normal(4000) * 10.0 ** rng.integers(-30, 30, 4000)
+                               ).astype(np.float32)])
+    got = o.f32_to_bf16(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    nan = o.f32_to_bf16(np.array([np.nan], np.float32))[0]
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x007F) != 0
+    # binary64: candidates are the bf16 values bracketing x
+    xd = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-20, 20, 3000),
+                         1.0 + np.array([2 ** -8, 3 * 2 ** -8, 2 ** -8 + 2 ** -40,
+                                         2 ** -8 - 2 ** -40, 2 ** -9 * 3])])
+    got = o.f64_to_bf16(xd)
+    for v, gbits in zip(xd, got):
+        t = np.float32(v)
+        base = int(np.array([t], np.float32).view(np.uint32)[0] >> 16)
+        cands = [(base + k) & 0xFFFF for k in (-1, 0, 1, 2)]
+        vals = [float(o.bf16_to_f32(np.array([c], np.uint16))[0]) for c in cands]
+        errs = [abs(val - v) for val in vals]
+        best = min(errs)
+        ties = [c for c, e in zip(cands, errs) if e == best]
+        pick = ties[0] if len(ties) == 1 else [c for c in ties if c % 2 == 0][0]
+        assert gbits == pick, (v, gbits, pick)
+
+
+# -------------------------------------------------------------- whole path ---
+def pin_whole_path_composition(o):
+    """Whole path on a tiny dense 2^3 grid and a few sparse cells equals the
+    library composition: the oracle's projection, torch grid_sample (the
+    pages' reference routine) on CPU, bf16 rounding by torch, numpy matmul;
+    null rows equal the bias exactly."""
+    import torch
+    rng = np.random.default_rng(17)
+    for dt in ("f32", "bf16"):
+        R, B, H, W, C, D = 2, 1, 6, 6, 16, 32
+        n = B * R ** 3
+        featf = rng.standard_normal((B, H, W, C)).astype(np.float32)
+        Wf = (rng.standard_normal((D, C)) * 0.1).astype(np.float32)
+        bf = (rng.standard_normal(D) * 0.1).astype(np.float32)
+        if dt == "bf16":
+            feat, Wq, bq = o.f32_to_bf16(featf), o.f32_to_bf16(Wf), o.f32_to_bf16(bf)
+            featv = o.bf16_to_f32(feat)
+            Wd, bd = o.bf16_to_f32(Wq).astype(np.float64), o.bf16_to_f32(bq).astype(np.float64)
+        else:
+            feat, Wq, bq, featv = featf, Wf, bf, featf
+            Wd, bd = Wf.astype(np.float64), bf.astype(np.float64)
+        f, d = o.camera(40.0, 1.4)
+        n_null = 3
+        Y, mask = o.proj_cond_rows(None, n, R, [f], [d], feat, Wq, bq, n_null,
+                                   np.arange(n + n_null))
+        p = o.project(None, n, R, [f], [d], H, W)
+        inp = torch.from_numpy(featv).permute(0, 3, 1, 2).contiguous()
+        gr = torch.from_numpy(p["grid"]).reshape(1, 1, n, 2)
+        S = torch.nn.functional.grid_sample(inp, gr, mode="bilinear", padding_mode="border",
+                                            align_corners=False)[0, :, 0, :].T
+        if dt == "bf16":
+            S = S.to(torch.bfloat16)
+        S = S.double().numpy()
+        want = S @ Wd.T + bd
+        tol = 1e-5 if dt == "f32" else 2e-2
+        scale = np.abs(S) @ np.abs(Wd).T + np.abs(bd)
+        assert np.max(np.abs(Y[:n] - want) / scale) < tol, dt
+        assert np.array_equal(mask[:n], p["mask"])
+        assert np.array_equal(Y[n:], np.broadcast_to(bd, (n_null, D)))
+        assert np.all(mask[n:] == 0)
+        Y0, _ = o.proj_cond_rows(None, n, R, [f], [d], feat, Wq, None, n_null, [n, n + 2])
+        assert np.all(Y0 == 0.0)
+
+
+ALL_PINS = {name[len("pin_"):]: fn for name, fn in sorted(globals().items())
+            if name.startswith("pin_") and callable(fn)}

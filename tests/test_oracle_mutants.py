@@ -1,0 +1,94 @@
+"""Each plausible mistake in the oracle must fail at least one pin.
+
+A mutant is the oracle source with one textual edit (a sign slip, a dropped
+term, a swapped operand, the other grid_sample convention ...), compiled on
+the CPU into a temporary library. The pins run against it in a child process
+(a mutant that reads out of bounds may crash; that also counts as caught).
+CPU only; nothing here touches a GPU.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "p3d_oracle.c")
+
+# (id, text in the oracle source, replacement)
+MUTANTS = [
+    ("camera_looks_down_plus_z", "float depth = dist[b] - pz;", "float depth = dist[b] + pz;"),
+    ("image_y_not_flipped", "float gy = -((f * py) / depth);", "float gy = ((f * py) / depth);"),
+    ("x_y_swapped", "float gx = (f * px) / depth;", "float gx = (f * py) / depth;"),
+    ("align_corners_true", "float ix = ((g + 1.0f) * (float)size - 1.0f) / 2.0f;",
+     "float ix = (g + 1.0f) / 2.0f * (float)(size - 1);"),
+    ("half_texel_dropped", "float ix = ((g + 1.0f) * (float)size - 1.0f) / 2.0f;",
+     "float ix = ((g + 1.0f) * (float)size) / 2.0f;"),
+    ("clamp_corners_not_index",
+     "    ix = fminf(fmaxf(ix, 0.0f), (float)(size - 1));\n    float fl = floorf(ix);\n    *i0 = (int32_t)fl;\n    *t = ix - fl;\n    *i1 = (*i0 + 1 < size) ? *i0 + 1 : size - 1;",
+     "    float fl = floorf(ix);\n    *t = ix - fl;\n    int32_t a = (int32_t)fmaxf(fminf(fl, (float)(size - 1)), 0.0f);\n    int32_t c = (int32_t)fmaxf(fminf(fl + 1.0f, (float)(size - 1)), 0.0f);\n    if (!(*t >= 0.0f && *t <= 1.0f)) *t = 0.0f;\n    *i0 = a;\n    *i1 = c;"),
+    ("second_texel_dropped", "*i1 = (*i0 + 1 < size) ? *i0 + 1 : size - 1;", "*i1 = *i0;"),
+    ("weights_swapped", "float w01 = tx * (1.0f - ty);", "float w01 = (1.0f - tx) * ty;"),
+    ("corner_rows_swapped", "int64_t r10 = (base + y1) * W + x0, r11 = (base + y1) * W + x1;",
+     "int64_t r10 = (base + y1) * W + x1, r11 = (base + y1) * W + x0;"),
+    ("cell_node_not_centre", "return ((float)c + 0.5f) / (float)R - 0.5f;",
+     "return (float)c / (float)R - 0.5f;"),
+    ("fov_as_half_angle_focal", "*focal = (float)(1.0 / tan(fov_deg * pi / 360.0));",
+     "*focal = (float)(1.0 / tan(fov_deg * pi / 180.0));"),
+    ("distance_full_extent", "return 0.5 / tan(half_angle) * half_size / (half_size + (double)extend_px);",
+     "return 1.0 / tan(half_angle) * half_size / (half_size + (double)extend_px);"),
+    ("distance_extend_ignored", "return 0.5 / tan(half_angle) * half_size / (half_size + (double)extend_px);",
+     "return 0.5 / tan(half_angle);"),
+    ("mask_exclusive_border", "gx >= -1.0f && gx <= 1.0f &&", "gx > -1.0f && gx < 1.0f &&"),
+    ("mask_ignores_depth", "uint8_t m = (uint8_t)(valid && depth > 0.0f &&", "uint8_t m = (uint8_t)(valid &&"),
+    ("linear_weight_transposed", "acc += param_at(weight, is_bf16, (int64_t)d * C + c) * S[i * (int64_t)C + c];",
+     "acc += param_at(weight, is_bf16, (int64_t)(c % D) * C + (d % C)) * S[i * (int64_t)C + c];"),
+    ("linear_bias_dropped", "            if (bias) acc += param_at(bias, is_bf16, d);\n            Y[i",
+     "            Y[i"),
+    ("null_rows_zero", "y[d] = bias ? param_at(bias, is_bf16, d) : 0.0;", "y[d] = 0.0;"),
+    ("bf16_truncates", "if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))",
+     "if (0)"),
+    ("bf16_ties_away", "if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))",
+     "if (dropped >= 0x8000u)"),
+    ("dense_order_zyx", "cell[3] = (int32_t)(n % r);", "cell[3] = (int32_t)((n / (r * r)) % r); cell[1] = (int32_t)(n % r); if (0)"),
+]
+
+RUNNER = r"""
+import json, sys, traceback
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + "/tests")
+import oracle, oracle_pins
+o = oracle.Oracle(sys.argv[2])
+failed = []
+for name, fn in sorted(oracle_pins.ALL_PINS.items()):
+    try:
+        fn(o)
+    except Exception:
+        failed.append(name)
+print(json.dumps(failed))
+"""
+
+
+def _build(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor for %s not found exactly once" % name
+    path = tmp_path / ("mut_%s.c" % name)
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / ("libmut_%s.so" % name)
+    sys.path.insert(0, ROOT)
+    from oracle import build as obuild
+    obuild.build(src=str(path), out=str(lib), extra=["-Wno-unused-variable",
+                                                     "-Wno-unused-but-set-variable",
+                                                     "-Wno-unused-parameter"])
+    return str(lib)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    lib = _build(tmp_path, name, old, new)
+    r = subprocess.run([sys.executable, "-c", RUNNER, ROOT, lib], capture_output=True,
+                       text=True, timeout=300)
+    if r.returncode != 0:
+        return  # crashed: caught
+    failed = json.loads(r.stdout.strip().splitlines()[-1])
+    assert failed, "mutant %s passed every pin" % name

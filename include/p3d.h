@@ -1,0 +1,214 @@
+/*
+ * p3d.h -- C ABI of libp3d: pixel-aligned projection conditioning on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * For every token (a cell of a dense 3-D grid or a sparse voxel) the library
+ * projects the cell centre through a fixed frontal pinhole camera, samples a
+ * channels-last image feature map there with grid_sample semantics, emits an
+ * in-image mask, and applies the per-token linear layer proj_linear; the
+ * classifier-free-guidance null branch is filled on the device.
+ *
+ * Sources (web pages, cited by title and section):
+ *   pixal3d_mrp_mlx, history of tests/, commit landing the pixel-aligned head
+ *     -- project_points, bilinear_sample, ProjGrid and distance_from_fov; the
+ *     grid_sample conventions (align_corners=False half-texel mapping, border
+ *     padding that clamps the source index before the corners are taken) and
+ *     a camera that looks down -Z.
+ *   trellis.cpp PR #38 "Initial support for Pixal3D":
+ *     commit adding pixal3d.cpp -- tokens are grid cells projected by a fixed
+ *       frontal camera whose only free parameter is the FOV; closed-form
+ *       distance;
+ *     commit exposing extend_pixel -- worked example of that distance;
+ *     commit introducing FlowCond -- proj_linear maps the per-token
+ *       view-aligned feature into model space; the null proj of the CFG
+ *       negative branch is zeroed on the device instead of materialised;
+ *     commit wiring the stages -- proj_in_channels is read off the weight and
+ *       a mismatch fails with a message;
+ *     commit checking widths in lin() -- errors name the tensor and both
+ *       shapes;
+ *     commit adding per-request camera fields -- every image has its own FOV.
+ *
+ * Conventions shared by every call
+ *   - Tensor arguments are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or retains them past the call.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without synchronising. Results are ready when the
+ *     stream reaches that point.
+ *   - Every call returns a p3d_status. On any status other than P3D_OK
+ *     nothing was enqueued (P3D_ERR_HIP: the launch itself failed), and
+ *     p3d_last_error() -- a per-thread string, valid until that thread's next
+ *     call -- names the offending argument with the expected and actual
+ *     values or shapes.
+ *   - Camera arrays are HOST arrays, read during the call only.
+ *   - Floating-point decisions that produce integers (pixel indices, masks)
+ *     are taken in binary32 with one rounding per operation in the order
+ *     documented below (no contraction), so they are reproducible bit for
+ *     bit by any IEEE binary32 implementation of the same steps.
+ */
+#ifndef P3D_H
+#define P3D_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum p3d_status {
+    P3D_OK = 0,
+    P3D_ERR_INVALID_ARG = 1,  /* value outside its documented range */
+    P3D_ERR_SHAPE = 2,        /* sizes that must agree do not */
+    P3D_ERR_DTYPE = 3,        /* element type (combination) not supported */
+    P3D_ERR_UNSUPPORTED = 4,  /* valid, but outside what the kernels handle */
+    P3D_ERR_HIP = 5           /* the HIP runtime rejected a launch */
+} p3d_status;
+
+typedef enum p3d_dtype {
+    P3D_F32 = 0,              /* IEEE binary32 */
+    P3D_BF16 = 1              /* bfloat16 (upper half of a binary32) */
+} p3d_dtype;
+
+/* A per-image pinhole camera on the +Z axis looking down -Z at the origin.
+ * focal = 1 / tan(fov / 2) in normalised image units (full-angle FOV);
+ * distance = camera-to-origin distance in world units (the unit cube spans
+ * [-1/2, 1/2]^3). Both finite and > 0. */
+typedef struct p3d_camera {
+    float focal;
+    float distance;
+} p3d_camera;
+
+/* Largest batch (number of images / cameras) one call accepts. Cameras
+ * travel to the device inside the kernel arguments. */
+#define P3D_MAX_BATCH 256
+
+/* ------------------------------------------------------------------------
+ * Host helpers (no device work, no stream).
+ * --------------------------------------------------------------------- */
+
+/* Library version string, e.g. "p3d 1.0.0 gfx950". Static storage. */
+const char* p3d_version(void);
+
+/* Name of a status code. Static storage. */
+const char* p3d_status_string(p3d_status s);
+
+/* Message of this thread's last failed call ("" if none). */
+const char* p3d_last_error(void);
+
+/* Closed-form camera distance (pixal3d.cpp camera solve; extend_pixel worked
+ * example: 49.13 deg on a 512 px frame gives 1.094 / 0.875 / 0.729 for
+ * extend_px = 0 / 64 / 128). The distance puts the corner of the unit cube's
+ * z = 0 square on the frame border, pushed extend_px pixels beyond it:
+ *     d = 0.5 / tan(fov/2) * (S/2) / (S/2 + extend_px),   S = image_size.
+ * Computed in binary64 with the C library tan. fov_deg must lie in (0, 180),
+ * image_size >= 1 and S/2 + extend_px > 0; otherwise returns NaN and sets
+ * the last error. */
+double p3d_distance_from_fov(double fov_deg, int32_t image_size, int32_t extend_px);
+
+/* Camera for a full-angle FOV (degrees, in (0, 180)) and a distance (> 0,
+ * finite): focal = (float)(1 / tan(fov/2)) computed in binary64 and rounded
+ * once; distance rounded once to binary32. */
+p3d_status p3d_make_camera(double fov_deg, double distance, p3d_camera* out);
+
+/* ------------------------------------------------------------------------
+ * p3d_project_points -- project_points / ProjGrid (pixel-aligned head
+ * commit; pixal3d.cpp commit).
+ *
+ * Token n has the integer cell (b, x, y, z): coords[4n .. 4n+3], or, when
+ * coords is NULL, the dense enumeration n = ((b*R + x)*R + y)*R + z (then n
+ * must equal batch * R^3, or be 0). For each token, in binary32:
+ *   p_a   = ((float)c_a + 0.5f) / (float)R - 0.5f      (a = x, y, z)
+ *   depth = distance_b - p_z
+ *   gx    = (focal_b * p_x) / depth
+ *   gy    = -((focal_b * p_y) / depth)                 (image rows go down)
+ *   mask  = b in [0, batch) && depth > 0 && -1 <= gx <= 1 && -1 <= gy <= 1
+ *   ix    = min(max(((gx + 1) * W - 1) / 2, 0), W - 1)  (NaN -> 0)
+ *   x0    = floor(ix), tx = ix - x0; likewise iy, y0, ty with H.
+ * A batch column outside [0, batch) is clamped into range to pick the camera
+ * and gets mask 0. Cells outside [0, R) are projected by the same formulas.
+ *
+ *   coords  [n, 4] int32 device, or NULL (dense grid)
+ *   n       tokens (>= 0; 0 enqueues nothing)
+ *   resolution  R >= 1
+ *   cams    host array [batch]; 1 <= batch <= P3D_MAX_BATCH
+ *   height, width  H, W >= 1 of the feature map the pixels index
+ *   outputs (device, any may be NULL = not written):
+ *     grid  [n, 2] float (gx, gy)     pixel [n, 2] int32 (x0, y0)
+ *     frac  [n, 2] float (tx, ty)     depth [n] float    mask [n] uint8 0/1
+ * --------------------------------------------------------------------- */
+p3d_status p3d_project_points(const int32_t* coords, int64_t n, int32_t resolution,
+                              const p3d_camera* cams, int32_t batch,
+                              int32_t height, int32_t width,
+                              float* grid, int32_t* pixel, float* frac,
+                              float* depth, uint8_t* mask, void* stream);
+
+/* ------------------------------------------------------------------------
+ * p3d_bilinear_sample -- bilinear_sample == grid_sample(mode='bilinear',
+ * align_corners=False, padding_mode='border') (pixel-aligned head commit).
+ *
+ * feat is channels-last [batch, H, W, C] (row (b, y, x) holds C contiguous
+ * channels). For point n with normalised (gx, gy) = grid[2n], grid[2n+1] and
+ * item b = batch_index[n] (0 when batch_index is NULL; clamped into range):
+ * the source indices, corners and fractions follow p3d_project_points, the
+ * far corners are x1 = min(x0 + 1, W - 1), y1 = min(y0 + 1, H - 1), and
+ *   out[n, c] = (1-tx)(1-ty) F[y0,x0,c] + tx(1-ty) F[y0,x1,c]
+ *             + (1-tx)ty F[y1,x0,c] + tx ty F[y1,x1,c]
+ * with binary32 weights and binary32 arithmetic. Points outside the image
+ * keep their border-clamped value (only the mask of p3d_project_points
+ * flags them).
+ *
+ *   feat, feat_dtype   device map; F32 or BF16
+ *   batch, height, width, channels   map shape; C % 8 == 0 (BF16) or
+ *                      C % 4 == 0 (F32); batch*H*W < 2^31
+ *   grid [n, 2] float, batch_index [n] int32 or NULL   (device)
+ *   out [n, C] device, out_dtype: F32 (any map) or BF16 (BF16 map only;
+ *                      round to nearest even)
+ *   Alignment: feat and out 16-byte aligned.
+ * --------------------------------------------------------------------- */
+p3d_status p3d_bilinear_sample(const void* feat, p3d_dtype feat_dtype,
+                               int32_t batch, int32_t height, int32_t width,
+                               int32_t channels,
+                               const float* grid, const int32_t* batch_index, int64_t n,
+                               void* out, p3d_dtype out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * p3d_proj_cond -- the whole path, fused (pixal3d.cpp commit: grid
+ * projection and ProjCond; FlowCond commit: proj_linear and the null proj
+ * zeroed on the device).
+ *
+ * out has n + n_null rows of out_dim values, in `dtype`:
+ *   rows [0, n):            Y[n,:] = W * S[n,:] + bias, where S is the
+ *                           p3d_bilinear_sample of the p3d_project_points
+ *                           point of token n; for BF16 the sample is rounded
+ *                           to bf16 (nearest even) before the product, which
+ *                           accumulates in binary32 (matrix cores).
+ *   rows [n, n + n_null):   the CFG null branch: the proj input is zero, so
+ *                           the row is proj_linear(0) = bias (+0 with no
+ *                           bias). Neither the map nor the weight is read.
+ * Sampled features exist only on chip; they are never written to memory.
+ *
+ *   coords, n, resolution, cams, batch   as p3d_project_points
+ *   feat, dtype, height, width, channels  map as p3d_bilinear_sample; map,
+ *                           weight, bias and out all have `dtype`
+ *   weight [out_dim, weight_in] row-major (a torch Linear weight), device;
+ *                           weight_in must equal channels (the weight's input
+ *                           width is checked against the map's channels; a
+ *                           mismatch is P3D_ERR_SHAPE naming both shapes)
+ *   bias [out_dim] device, or NULL
+ *   out_dim                 D >= 1; D % 8 == 0 (BF16) or D % 4 == 0 (F32)
+ *   n_null                  >= 0 null rows appended after the n token rows
+ *   out [(n + n_null), D] device; mask [n] uint8 device or NULL
+ *   Alignment: feat, weight and out 16-byte aligned.
+ * --------------------------------------------------------------------- */
+p3d_status p3d_proj_cond(const int32_t* coords, int64_t n, int32_t resolution,
+                         const p3d_camera* cams, int32_t batch,
+                         const void* feat, p3d_dtype dtype,
+                         int32_t height, int32_t width, int32_t channels,
+                         const void* weight, int32_t out_dim, int32_t weight_in,
+                         const void* bias, int64_t n_null,
+                         void* out, uint8_t* mask, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* P3D_H */

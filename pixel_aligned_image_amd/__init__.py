@@ -1,0 +1,210 @@
+"""pixel_aligned_image_amd -- Python binding of libp3d (MI355X / gfx950).
+
+Thin ctypes marshalling over the C ABI in ``include/p3d.h``: every function
+here has the name of its C entry point, checks that the torch tensors it is
+given are on the GPU, contiguous and of the declared dtype, and passes their
+device pointers plus torch's current HIP stream. All computation happens in
+the HIP kernels of libp3d; there is no fallback. If ``libp3d.so`` is missing
+the import fails loudly (build it with ``__graft_entry__.build()`` or
+``python -m pixel_aligned_image_amd.build``).
+
+torch is imported before libp3d is loaded so that the library binds to the
+same HIP runtime as torch (both carry the soname libamdhip64.so.7).
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_version",
+           "p3d_status_string", "p3d_last_error", "p3d_distance_from_fov", "p3d_make_camera",
+           "p3d_project_points", "p3d_bilinear_sample", "p3d_proj_cond", "make_cameras",
+           "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libp3d.so")
+
+P3D_OK, P3D_ERR_INVALID_ARG, P3D_ERR_SHAPE, P3D_ERR_DTYPE, P3D_ERR_UNSUPPORTED, P3D_ERR_HIP = range(6)
+P3D_F32, P3D_BF16 = 0, 1
+P3D_MAX_BATCH = 256
+
+
+class p3d_camera(ctypes.Structure):
+    _fields_ = [("focal", ctypes.c_float), ("distance", ctypes.c_float)]
+
+
+class P3DError(RuntimeError):
+    """A libp3d call returned a status other than P3D_OK."""
+
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (_status_name(status), message))
+        self.status = status
+        self.message = message
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libp3d.so is not built at %s; run __graft_entry__.build() "
+                          "(or python -m pixel_aligned_image_amd.build)" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    cam_p = ctypes.POINTER(p3d_camera)
+    L.p3d_version.restype = ctypes.c_char_p
+    L.p3d_version.argtypes = []
+    L.p3d_status_string.restype = ctypes.c_char_p
+    L.p3d_status_string.argtypes = [ctypes.c_int]
+    L.p3d_last_error.restype = ctypes.c_char_p
+    L.p3d_last_error.argtypes = []
+    L.p3d_distance_from_fov.restype = ctypes.c_double
+    L.p3d_distance_from_fov.argtypes = [ctypes.c_double, i32, i32]
+    L.p3d_make_camera.restype = ctypes.c_int
+    L.p3d_make_camera.argtypes = [ctypes.c_double, ctypes.c_double, cam_p]
+    L.p3d_project_points.restype = ctypes.c_int
+    L.p3d_project_points.argtypes = [vp, i64, i32, cam_p, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    L.p3d_bilinear_sample.restype = ctypes.c_int
+    L.p3d_bilinear_sample.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, vp, vp, i64, vp,
+                                      ctypes.c_int, vp]
+    L.p3d_proj_cond.restype = ctypes.c_int
+    L.p3d_proj_cond.argtypes = [vp, i64, i32, cam_p, i32, vp, ctypes.c_int, i32, i32, i32,
+                                vp, i32, i32, vp, i64, vp, vp, vp]
+    return L
+
+
+lib = _load()
+
+
+def _status_name(s):
+    return lib.p3d_status_string(int(s)).decode()
+
+
+def _check(status):
+    if status != P3D_OK:
+        raise P3DError(status, lib.p3d_last_error().decode())
+
+
+def p3d_version():
+    return lib.p3d_version().decode()
+
+
+def p3d_status_string(status):
+    return _status_name(status)
+
+
+def p3d_last_error():
+    return lib.p3d_last_error().decode()
+
+
+def p3d_distance_from_fov(fov_deg, image_size, extend_px=0):
+    d = lib.p3d_distance_from_fov(float(fov_deg), int(image_size), int(extend_px))
+    if d != d:
+        raise P3DError(P3D_ERR_INVALID_ARG, lib.p3d_last_error().decode())
+    return d
+
+
+def p3d_make_camera(fov_deg, distance):
+    """(focal, distance) of the camera, as binary32 Python floats."""
+    c = p3d_camera()
+    _check(lib.p3d_make_camera(float(fov_deg), float(distance), ctypes.byref(c)))
+    return c.focal, c.distance
+
+
+def make_cameras(cams):
+    """ctypes array of p3d_camera from a sequence of (focal, distance)."""
+    arr = (p3d_camera * len(cams))()
+    for i, (f, d) in enumerate(cams):
+        arr[i].focal = f
+        arr[i].distance = d
+    return arr
+
+
+# ----------------------------------------------------------------- helpers ---
+_DT = {torch.float32: P3D_F32, torch.bfloat16: P3D_BF16}
+
+
+def _dev(t, name, dtype=None, shape=None):
+    """Device pointer of an optional tensor after checking it."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _cams(cams):
+    if isinstance(cams, ctypes.Array):
+        return cams, len(cams)
+    arr = make_cameras(list(cams))
+    return arr, len(arr)
+
+
+# -------------------------------------------------------------- entry points ---
+def p3d_project_points(coords, n, resolution, cams, height, width, grid=None, pixel=None,
+                       frac=None, depth=None, mask=None, stream=None):
+    """Enqueue p3d_project_points. coords: int32 [n, 4] device tensor or None
+    (dense grid); cams: sequence of (focal, distance) per batch item; outputs
+    are preallocated device tensors or None."""
+    camarr, batch = _cams(cams)
+    n = int(n)
+    _check(lib.p3d_project_points(
+        _dev(coords, "coords", torch.int32, (n, 4)), n, int(resolution), camarr, batch,
+        int(height), int(width),
+        _dev(grid, "grid", torch.float32, (n, 2)), _dev(pixel, "pixel", torch.int32, (n, 2)),
+        _dev(frac, "frac", torch.float32, (n, 2)), _dev(depth, "depth", torch.float32, (n,)),
+        _dev(mask, "mask", torch.uint8, (n,)), _stream(stream)))
+
+
+def p3d_bilinear_sample(feat, grid, out, batch_index=None, stream=None):
+    """Enqueue p3d_bilinear_sample. feat: [B, H, W, C] float32/bfloat16;
+    grid: float32 [n, 2]; out: [n, C] float32 (any map) or bfloat16 (bf16
+    map); batch_index: int32 [n] or None."""
+    if feat.dim() != 4:
+        raise ValueError("feat must be [B, H, W, C], got %s" % (tuple(feat.shape),))
+    B, H, W, C = feat.shape
+    n = grid.shape[0]
+    fdt = _DT.get(feat.dtype)
+    odt = _DT.get(out.dtype)
+    if fdt is None or odt is None:
+        raise TypeError("feat/out must be float32 or bfloat16")
+    _check(lib.p3d_bilinear_sample(
+        _dev(feat, "feat"), fdt, B, H, W, C, _dev(grid, "grid", torch.float32, (n, 2)),
+        _dev(batch_index, "batch_index", torch.int32, (n,)), n,
+        _dev(out, "out", None, (n, C)), odt, _stream(stream)))
+
+
+def p3d_proj_cond(coords, n, resolution, cams, feat, weight, out, bias=None, n_null=0,
+                  mask=None, stream=None):
+    """Enqueue p3d_proj_cond. feat: [B, H, W, C]; weight: [D, C_w] (torch
+    Linear layout; C_w is checked against C by the library); bias: [D] or
+    None; out: [n + n_null, D]; all of one dtype (float32 or bfloat16);
+    mask: uint8 [n] or None."""
+    camarr, batch = _cams(cams)
+    if feat.dim() != 4:
+        raise ValueError("feat must be [B, H, W, C], got %s" % (tuple(feat.shape),))
+    if weight.dim() != 2:
+        raise ValueError("weight must be [out_dim, in_dim], got %s" % (tuple(weight.shape),))
+    B, H, W, C = feat.shape
+    if B != batch:
+        raise ValueError("feat has %d batch items but %d cameras were given" % (B, batch))
+    D, Cw = weight.shape
+    dt = _DT.get(feat.dtype)
+    if dt is None:
+        raise TypeError("feat must be float32 or bfloat16, got %s" % feat.dtype)
+    n, n_null = int(n), int(n_null)
+    _check(lib.p3d_proj_cond(
+        _dev(coords, "coords", torch.int32, (n, 4)), n, int(resolution), camarr, batch,
+        _dev(feat, "feat"), dt, H, W, C, _dev(weight, "weight", feat.dtype), D, Cw,
+        _dev(bias, "bias", feat.dtype, (D,)), n_null,
+        _dev(out, "out", feat.dtype, (n + n_null, D)), _dev(mask, "mask", torch.uint8, (n,)),
+        _stream(stream)))

@@ -1,0 +1,251 @@
+// api.hip -- the extern "C" entry points of libp3d: validation of every
+// argument before anything is enqueued, the host-side camera helpers, and
+// dispatch to the kernels. Error messages follow the stage-wiring and lin()
+// width-check commits of trellis.cpp PR #38: name the argument and give both
+// the expected and the actual value or shape.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "p3d_internal.h"
+
+using namespace p3d;
+
+namespace {
+
+thread_local std::string g_err;
+
+constexpr int64_t kMaxTokens = int64_t(1) << 30;   // keeps tile counts in int32
+
+p3d_status fail(p3d_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+p3d_status ok() {
+    g_err.clear();
+    return P3D_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+const char* dtype_name(p3d_dtype d) {
+    return d == P3D_F32 ? "F32" : d == P3D_BF16 ? "BF16" : "unknown";
+}
+
+p3d_status hip_fail(const char* what, hipError_t e) {
+    return fail(P3D_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+// Shared checks of the token / camera arguments.
+p3d_status check_tokens(const char* fn, const int32_t* coords, int64_t n, int32_t R,
+                        const p3d_camera* cams, int32_t batch, int32_t H, int32_t W,
+                        CamTable* tab) {
+    if (n < 0) return fail(P3D_ERR_INVALID_ARG, "%s: n must be >= 0, got %lld", fn, (long long)n);
+    if (n > kMaxTokens)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: n must be <= %lld, got %lld", fn,
+                    (long long)kMaxTokens, (long long)n);
+    if (R < 1) return fail(P3D_ERR_INVALID_ARG, "%s: resolution must be >= 1, got %d", fn, R);
+    if (batch < 1 || batch > P3D_MAX_BATCH)
+        return fail(P3D_ERR_INVALID_ARG, "%s: batch must be in [1, %d], got %d", fn,
+                    P3D_MAX_BATCH, batch);
+    if (H < 1 || W < 1)
+        return fail(P3D_ERR_INVALID_ARG, "%s: feature map height/width must be >= 1, got %dx%d",
+                    fn, H, W);
+    if ((int64_t)batch * H * W > INT32_MAX)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: batch*height*width must be < 2^31 (row indices are int32), got %lld",
+                    fn, (long long)((int64_t)batch * H * W));
+    if (!coords) {
+        const int64_t r3 = (int64_t)R * R * R;
+        if (n > 0 && (R > 1290 || r3 * batch != n))   // 1290^3 * 256 still fits int64
+            return fail(P3D_ERR_SHAPE,
+                        "%s: dense grid (coords == NULL) needs n == batch*R^3 = %d*%d^3 = %lld, "
+                        "got n = %lld", fn, batch, R, (long long)(r3 * batch), (long long)n);
+    } else if (!aligned(coords, 16)) {
+        return fail(P3D_ERR_UNSUPPORTED, "%s: coords must be 16-byte aligned ([n,4] int32 rows)",
+                    fn);
+    }
+    if (!cams) return fail(P3D_ERR_INVALID_ARG, "%s: cams is NULL (host array [batch])", fn);
+    for (int32_t b = 0; b < batch; ++b) {
+        const float f = cams[b].focal, d = cams[b].distance;
+        if (!(isfinite(f) && f > 0.0f))
+            return fail(P3D_ERR_INVALID_ARG, "%s: cams[%d].focal must be finite and > 0, got %g",
+                        fn, b, (double)f);
+        if (!(isfinite(d) && d > 0.0f))
+            return fail(P3D_ERR_INVALID_ARG,
+                        "%s: cams[%d].distance must be finite and > 0, got %g", fn, b, (double)d);
+        tab->cam[b] = cams[b];
+    }
+    for (int32_t b = batch; b < P3D_MAX_BATCH; ++b) tab->cam[b] = cams[batch - 1];
+    return P3D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* p3d_version(void) { return "p3d 1.0.0 gfx950"; }
+
+const char* p3d_status_string(p3d_status s) {
+    switch (s) {
+        case P3D_OK: return "P3D_OK";
+        case P3D_ERR_INVALID_ARG: return "P3D_ERR_INVALID_ARG";
+        case P3D_ERR_SHAPE: return "P3D_ERR_SHAPE";
+        case P3D_ERR_DTYPE: return "P3D_ERR_DTYPE";
+        case P3D_ERR_UNSUPPORTED: return "P3D_ERR_UNSUPPORTED";
+        case P3D_ERR_HIP: return "P3D_ERR_HIP";
+    }
+    return "P3D_ERR_UNKNOWN";
+}
+
+const char* p3d_last_error(void) { return g_err.c_str(); }
+
+double p3d_distance_from_fov(double fov_deg, int32_t image_size, int32_t extend_px) {
+    if (!(fov_deg > 0.0 && fov_deg < 180.0)) {
+        fail(P3D_ERR_INVALID_ARG, "p3d_distance_from_fov: fov_deg must be in (0, 180), got %g",
+             fov_deg);
+        return NAN;
+    }
+    if (image_size < 1) {
+        fail(P3D_ERR_INVALID_ARG, "p3d_distance_from_fov: image_size must be >= 1, got %d",
+             image_size);
+        return NAN;
+    }
+    const double half = 0.5 * (double)image_size;
+    if (!(half + (double)extend_px > 0.0)) {
+        fail(P3D_ERR_INVALID_ARG,
+             "p3d_distance_from_fov: image_size/2 + extend_px must be > 0, got %g + %d", half,
+             extend_px);
+        return NAN;
+    }
+    g_err.clear();
+    const double tan_half = tan(fov_deg * M_PI / 360.0);
+    return 0.5 / tan_half * half / (half + (double)extend_px);
+}
+
+p3d_status p3d_make_camera(double fov_deg, double distance, p3d_camera* out) {
+    if (!out) return fail(P3D_ERR_INVALID_ARG, "p3d_make_camera: out is NULL");
+    if (!(fov_deg > 0.0 && fov_deg < 180.0))
+        return fail(P3D_ERR_INVALID_ARG, "p3d_make_camera: fov_deg must be in (0, 180), got %g",
+                    fov_deg);
+    if (!(isfinite(distance) && distance > 0.0))
+        return fail(P3D_ERR_INVALID_ARG,
+                    "p3d_make_camera: distance must be finite and > 0, got %g", distance);
+    out->focal = (float)(1.0 / tan(fov_deg * M_PI / 360.0));
+    out->distance = (float)distance;
+    return ok();
+}
+
+p3d_status p3d_project_points(const int32_t* coords, int64_t n, int32_t resolution,
+                              const p3d_camera* cams, int32_t batch, int32_t height,
+                              int32_t width, float* grid, int32_t* pixel, float* frac,
+                              float* depth, uint8_t* mask, void* stream) {
+    const char* fn = "p3d_project_points";
+    CamTable tab;
+    p3d_status st = check_tokens(fn, coords, n, resolution, cams, batch, height, width, &tab);
+    if (st != P3D_OK) return st;
+    if (!aligned(grid, 8) || !aligned(pixel, 8) || !aligned(frac, 8))
+        return fail(P3D_ERR_UNSUPPORTED, "%s: grid, pixel and frac must be 8-byte aligned", fn);
+    if (n == 0) return ok();
+    ProjectArgs a{coords, n, resolution, batch, height, width, grid, pixel, frac, depth, mask};
+    hipError_t e = launch_project(a, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+p3d_status p3d_bilinear_sample(const void* feat, p3d_dtype feat_dtype, int32_t batch,
+                               int32_t height, int32_t width, int32_t channels,
+                               const float* grid, const int32_t* batch_index, int64_t n,
+                               void* out, p3d_dtype out_dtype, void* stream) {
+    const char* fn = "p3d_bilinear_sample";
+    if (n < 0) return fail(P3D_ERR_INVALID_ARG, "%s: n must be >= 0, got %lld", fn, (long long)n);
+    if (n > kMaxTokens)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: n must be <= %lld, got %lld", fn,
+                    (long long)kMaxTokens, (long long)n);
+    if (feat_dtype != P3D_F32 && feat_dtype != P3D_BF16)
+        return fail(P3D_ERR_DTYPE, "%s: feat_dtype must be F32 or BF16, got %d", fn,
+                    (int)feat_dtype);
+    if (out_dtype != P3D_F32 && out_dtype != P3D_BF16)
+        return fail(P3D_ERR_DTYPE, "%s: out_dtype must be F32 or BF16, got %d", fn,
+                    (int)out_dtype);
+    if (feat_dtype == P3D_F32 && out_dtype == P3D_BF16)
+        return fail(P3D_ERR_DTYPE, "%s: a BF16 output needs a BF16 map (feat F32, out BF16)", fn);
+    if (batch < 1 || height < 1 || width < 1 || channels < 1)
+        return fail(P3D_ERR_INVALID_ARG,
+                    "%s: map shape must be positive, got [batch=%d, H=%d, W=%d, C=%d]", fn,
+                    batch, height, width, channels);
+    if ((int64_t)batch * height * width > INT32_MAX)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: batch*height*width must be < 2^31, got %lld", fn,
+                    (long long)((int64_t)batch * height * width));
+    const int epv = feat_dtype == P3D_BF16 ? 8 : 4;
+    if (channels % epv)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: channels must be a multiple of %d for a %s map (16-byte rows), got %d",
+                    fn, epv, dtype_name(feat_dtype), channels);
+    if (!aligned(feat, 16) || !aligned(out, 16) || !aligned(grid, 8))
+        return fail(P3D_ERR_UNSUPPORTED, "%s: feat and out must be 16-byte aligned, grid 8-byte",
+                    fn);
+    if (n == 0) return ok();
+    if (!feat || !grid || !out)
+        return fail(P3D_ERR_INVALID_ARG, "%s: feat, grid and out must be non-NULL", fn);
+    SampleArgs a{feat, batch, height, width, channels, grid, batch_index, n, out};
+    hipError_t e = launch_sample(a, feat_dtype, out_dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+p3d_status p3d_proj_cond(const int32_t* coords, int64_t n, int32_t resolution,
+                         const p3d_camera* cams, int32_t batch, const void* feat,
+                         p3d_dtype dtype, int32_t height, int32_t width, int32_t channels,
+                         const void* weight, int32_t out_dim, int32_t weight_in,
+                         const void* bias, int64_t n_null, void* out, uint8_t* mask,
+                         void* stream) {
+    const char* fn = "p3d_proj_cond";
+    CamTable tab;
+    p3d_status st = check_tokens(fn, coords, n, resolution, cams, batch, height, width, &tab);
+    if (st != P3D_OK) return st;
+    if (dtype != P3D_F32 && dtype != P3D_BF16)
+        return fail(P3D_ERR_DTYPE, "%s: dtype must be F32 or BF16, got %d", fn, (int)dtype);
+    if (n_null < 0 || n_null > kMaxTokens)
+        return fail(P3D_ERR_INVALID_ARG, "%s: n_null must be in [0, %lld], got %lld", fn,
+                    (long long)kMaxTokens, (long long)n_null);
+    if (channels < 1 || out_dim < 1)
+        return fail(P3D_ERR_INVALID_ARG, "%s: channels and out_dim must be >= 1, got %d, %d", fn,
+                    channels, out_dim);
+    if (weight_in != channels)
+        return fail(P3D_ERR_SHAPE,
+                    "%s: proj_linear weight is [%d, %d] but the feature map [%d, %d, %d, %d] has "
+                    "%d channels: the weight's input width must equal the map's channels",
+                    fn, out_dim, weight_in, batch, height, width, channels, channels);
+    const int epv = dtype == P3D_BF16 ? 8 : 4;
+    if (channels % epv)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: channels must be a multiple of %d for %s (16-byte rows), got %d", fn,
+                    epv, dtype_name(dtype), channels);
+    if (out_dim % epv)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: out_dim must be a multiple of %d for %s (16-byte rows), got %d", fn, epv,
+                    dtype_name(dtype), out_dim);
+    if (!aligned(feat, 16) || !aligned(weight, 16) || !aligned(out, 16) || !aligned(bias, 16))
+        return fail(P3D_ERR_UNSUPPORTED, "%s: feat, weight, bias and out must be 16-byte aligned",
+                    fn);
+    if (n == 0 && n_null == 0) return ok();
+    if (!out) return fail(P3D_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (n > 0 && (!feat || !weight))
+        return fail(P3D_ERR_INVALID_ARG, "%s: feat and weight must be non-NULL", fn);
+    ProjCondArgs a{coords, n, resolution, batch, feat, height, width, channels,
+                   weight, bias, out_dim, n_null, out, mask};
+    hipError_t e = launch_proj_cond(a, dtype, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+}  // extern "C"

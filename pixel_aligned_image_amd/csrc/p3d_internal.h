@@ -1,0 +1,186 @@
+// p3d_internal.h -- device-side building blocks and launch interfaces of
+// libp3d (gfx950). Not installed; the public interface is include/p3d.h.
+//
+// Every translation unit is compiled with -ffp-contract=off: the projection
+// and index mapping below must round once per operation, in the written
+// order, so that pixel indices and masks are reproducible bit for bit. Where
+// a fused multiply-add is wanted (the bilinear blend, never an index
+// decision) it is written explicitly with fmaf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "p3d.h"
+
+namespace p3d {
+
+struct CamTable {
+    p3d_camera cam[P3D_MAX_BATCH];
+};
+
+// ---------------------------------------------------------------------------
+// Projection (pixel-aligned head commit: project_points; pixal3d.cpp commit:
+// fixed frontal camera on +Z looking down -Z, full-angle focal).
+// ---------------------------------------------------------------------------
+
+// Integer cell of token t: explicit coords (b, x, y, z), or the dense
+// enumeration t = ((b*R + x)*R + y)*R + z.
+__device__ __forceinline__ void token_cell(const int32_t* __restrict__ coords, int64_t t,
+                                           int32_t R, int32_t& b, int32_t& x, int32_t& y,
+                                           int32_t& z) {
+    if (coords) {
+        const int4 c = *reinterpret_cast<const int4*>(coords + 4 * t);
+        b = c.x; x = c.y; y = c.z; z = c.w;
+    } else {
+        const int64_t r = R;
+        z = (int32_t)(t % r);
+        const int64_t q = t / r;
+        y = (int32_t)(q % r);
+        const int64_t q2 = q / r;
+        x = (int32_t)(q2 % r);
+        b = (int32_t)(q2 / r);
+    }
+}
+
+// Cell centre in the unit cube [-1/2, 1/2]: (c + 1/2)/R - 1/2, binary32.
+__device__ __forceinline__ float cell_centre(int32_t c, int32_t R) {
+    return ((float)c + 0.5f) / (float)R - 0.5f;
+}
+
+struct Projected {
+    float gx, gy, depth;
+    int32_t b;      // batch item after clamping into [0, batch)
+    uint8_t mask;
+};
+
+__device__ __forceinline__ Projected project_cell(int32_t b, int32_t cx, int32_t cy, int32_t cz,
+                                                  int32_t R, const CamTable& cams,
+                                                  int32_t batch) {
+    Projected p;
+    const bool valid = (b >= 0) && (b < batch);
+    b = b < 0 ? 0 : (b >= batch ? batch - 1 : b);
+    const float px = cell_centre(cx, R);
+    const float py = cell_centre(cy, R);
+    const float pz = cell_centre(cz, R);
+    const float f = cams.cam[b].focal;
+    const float depth = cams.cam[b].distance - pz;
+    const float gx = (f * px) / depth;
+    const float gy = -((f * py) / depth);
+    p.gx = gx;
+    p.gy = gy;
+    p.depth = depth;
+    p.b = b;
+    p.mask = (uint8_t)(valid && depth > 0.0f && gx >= -1.0f && gx <= 1.0f &&
+                       gy >= -1.0f && gy <= 1.0f);
+    return p;
+}
+
+// grid_sample(align_corners=False, padding_mode='border') source index: the
+// normalised g maps to ((g+1)*size - 1)/2, which is clamped to [0, size-1]
+// (NaN -> 0) BEFORE the two neighbouring texels are chosen.
+struct SrcIdx {
+    int32_t i0, i1;
+    float t;
+};
+
+__device__ __forceinline__ SrcIdx source_index(float g, int32_t size) {
+    float ix = ((g + 1.0f) * (float)size - 1.0f) / 2.0f;
+    ix = fminf(fmaxf(ix, 0.0f), (float)(size - 1));
+    const float fl = floorf(ix);
+    SrcIdx s;
+    s.i0 = (int32_t)fl;
+    s.t = ix - fl;
+    s.i1 = (s.i0 + 1 < size) ? s.i0 + 1 : size - 1;
+    return s;
+}
+
+// Corner rows (in units of map rows of C channels) and bilinear weights of
+// one sampling point.
+struct Corners {
+    int32_t r00, r01, r10, r11;
+    float w00, w01, w10, w11;
+};
+
+__device__ __forceinline__ Corners corners_of(float gx, float gy, int32_t b, int32_t H,
+                                              int32_t W) {
+    const SrcIdx sx = source_index(gx, W);
+    const SrcIdx sy = source_index(gy, H);
+    Corners c;
+    const int32_t base = b * H;
+    c.r00 = (base + sy.i0) * W + sx.i0;
+    c.r01 = (base + sy.i0) * W + sx.i1;
+    c.r10 = (base + sy.i1) * W + sx.i0;
+    c.r11 = (base + sy.i1) * W + sx.i1;
+    c.w00 = (1.0f - sx.t) * (1.0f - sy.t);
+    c.w01 = sx.t * (1.0f - sy.t);
+    c.w10 = (1.0f - sx.t) * sy.t;
+    c.w11 = sx.t * sy.t;
+    return c;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 helpers. Widening is a shift; narrowing uses the gfx950 packed
+// convert (round to nearest even, NaN stays NaN).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte store that bypasses the caches' allocate-on-write (streamed output).
+__device__ __forceinline__ void store_nt16(void* p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(p));
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------------------
+// Launch interfaces (each returns the hipError_t of its launch).
+// ---------------------------------------------------------------------------
+struct ProjectArgs {
+    const int32_t* coords;
+    int64_t n;
+    int32_t R, batch, H, W;
+    float* grid;
+    int32_t* pixel;
+    float* frac;
+    float* depth;
+    uint8_t* mask;
+};
+
+struct SampleArgs {
+    const void* feat;
+    int32_t batch, H, W, C;
+    const float* grid;
+    const int32_t* bidx;
+    int64_t n;
+    void* out;
+};
+
+struct ProjCondArgs {
+    const int32_t* coords;
+    int64_t n;
+    int32_t R, batch;
+    const void* feat;
+    int32_t H, W, C;
+    const void* weight;
+    const void* bias;
+    int32_t D;
+    int64_t n_null;
+    void* out;
+    uint8_t* mask;
+};
+
+hipError_t launch_project(const ProjectArgs& a, const CamTable& cams, hipStream_t s);
+hipError_t launch_sample(const SampleArgs& a, p3d_dtype in, p3d_dtype out, hipStream_t s);
+hipError_t launch_proj_cond(const ProjCondArgs& a, p3d_dtype dt, const CamTable& cams,
+                            hipStream_t s);
+
+}  // namespace p3d

@@ -1,0 +1,343 @@
+// proj_cond.hip -- p3d_proj_cond: projection -> bilinear gather ->
+// proj_linear on the matrix cores, fused; plus the CFG null-branch fill.
+//
+// Sources: pixal3d_mrp_mlx tests/ history, pixel-aligned head commit
+// (project_points, bilinear_sample); trellis.cpp PR #38 "Initial support for
+// Pixal3D", FlowCond commit (proj_linear maps the per-token view-aligned
+// feature into model space; the null proj is zeroed on the device, so the
+// null rows are proj_linear(0) = bias).
+//
+// GEMM view: Y[M=n, N=D] = S[M, K=C] * W[N, K]^T + bias, where the A operand
+// S is never stored: each workgroup projects its BM tokens, then for every
+// K chunk gathers the four corner rows of each token (16-byte vectors,
+// eight lanes per 128-byte corner segment), blends them in binary32, rounds
+// to the operand type and writes the chunk into LDS, next to the matching
+// chunk of W. The matrix cores (v_mfma_f32_16x16x32_bf16, or
+// v_mfma_f32_16x16x4_f32 for binary32 maps) accumulate in binary32. The
+// next chunk's global loads are issued before the current chunk's MFMAs.
+// Tiles are mapped so that the D-tiles of one token tile run on the same
+// XCD and share its gathered corner rows in that XCD's L2.
+#include "p3d_internal.h"
+
+namespace p3d {
+
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves, 2 (M) x 2 (N)
+
+template <bool Bf16>
+struct Cfg;
+template <>
+struct Cfg<true> {
+    static constexpr int BM = 128, BN = 256, BK = 64, EPV = 8;
+};
+template <>
+struct Cfg<false> {
+    static constexpr int BM = 128, BN = 128, BK = 32, EPV = 4;
+};
+
+// Tile rows in LDS are BK elements = 128 bytes = 8 vectors of 16 bytes; the
+// vector index is XOR-swizzled with the row so that 16 lanes reading one
+// column of vectors from 16 consecutive rows spread over the banks.
+__device__ __forceinline__ int swz(int row, int v) { return row * 8 + (v ^ (row & 7)); }
+
+template <bool Bf16>
+__device__ __forceinline__ uint4 blend4(const uint4 (&q)[4], float w0, float w1, float w2,
+                                        float w3) {
+    uint4 o;
+    if constexpr (Bf16) {
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(&q[0]);
+        const uint32_t* b = reinterpret_cast<const uint32_t*>(&q[1]);
+        const uint32_t* c = reinterpret_cast<const uint32_t*>(&q[2]);
+        const uint32_t* d = reinterpret_cast<const uint32_t*>(&q[3]);
+        uint32_t* r = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = fmaf(w3, bf16lo(d[e]), fmaf(w2, bf16lo(c[e]),
+                                  fmaf(w1, bf16lo(b[e]), w0 * bf16lo(a[e]))));
+            const float hi = fmaf(w3, bf16hi(d[e]), fmaf(w2, bf16hi(c[e]),
+                                  fmaf(w1, bf16hi(b[e]), w0 * bf16hi(a[e]))));
+            r[e] = pack_bf16x2(lo, hi);
+        }
+    } else {
+        const float* a = reinterpret_cast<const float*>(&q[0]);
+        const float* b = reinterpret_cast<const float*>(&q[1]);
+        const float* c = reinterpret_cast<const float*>(&q[2]);
+        const float* d = reinterpret_cast<const float*>(&q[3]);
+        float* r = reinterpret_cast<float*>(&o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r[e] = fmaf(w3, d[e], fmaf(w2, c[e], fmaf(w1, b[e], w0 * a[e])));
+    }
+    return o;
+}
+
+template <bool Bf16>
+__global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, CamTable cams,
+                                                             int32_t m_tiles, int32_t n_tiles,
+                                                             int32_t per_xcd) {
+    using C = Cfg<Bf16>;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, EPV = C::EPV;
+    constexpr int WM = BM / 2, WN = BN / 2;          // wave tile
+    constexpr int MI = WM / 16, NJ = WN / 16;        // 16x16 blocks per wave
+    constexpr int A_ITEMS = BM * 8 / kThreads;       // gathered vectors per thread
+    constexpr int B_ITEMS = BN * 8 / kThreads;       // weight vectors per thread
+    typedef typename std::conditional<Bf16, uint16_t, float>::type elem_t;
+
+    __shared__ int32_t s_row[BM][4];
+    __shared__ float s_w[BM][4];
+    __shared__ uint4 s_a[BM * 8];
+    __shared__ uint4 s_b[BN * 8];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    const int32_t g = blockIdx.x;
+    const int32_t tile = (g & 7) * per_xcd + (g >> 3);
+    if (tile >= m_tiles * n_tiles) return;
+    const int32_t mt = tile / n_tiles, nt = tile - mt * n_tiles;
+    const int64_t m0 = (int64_t)mt * BM;
+    const int32_t n0 = nt * BN;
+
+    // ---- project the tile's tokens: corner rows + weights into LDS
+    if (tid < BM) {
+        const int64_t t = m0 + tid;
+        if (t < a.n) {
+            int32_t b, x, y, z;
+            token_cell(a.coords, t, a.R, b, x, y, z);
+            const Projected p = project_cell(b, x, y, z, a.R, cams, a.batch);
+            const Corners c = corners_of(p.gx, p.gy, p.b, a.H, a.W);
+            s_row[tid][0] = c.r00; s_row[tid][1] = c.r01;
+            s_row[tid][2] = c.r10; s_row[tid][3] = c.r11;
+            s_w[tid][0] = c.w00; s_w[tid][1] = c.w01;
+            s_w[tid][2] = c.w10; s_w[tid][3] = c.w11;
+            if (a.mask && nt == 0) a.mask[t] = p.mask;
+        } else {
+            s_row[tid][0] = s_row[tid][1] = s_row[tid][2] = s_row[tid][3] = 0;
+            s_w[tid][0] = s_w[tid][1] = s_w[tid][2] = s_w[tid][3] = 0.0f;
+        }
+    }
+    __syncthreads();
+
+    const uint4* __restrict__ feat = reinterpret_cast<const uint4*>(a.feat);
+    const uint4* __restrict__ wgt = reinterpret_cast<const uint4*>(a.weight);
+    const int vpr = a.C / EPV;                       // vectors per map / weight row
+    const int nk = (a.C + BK - 1) / BK;
+
+    uint4 qa[A_ITEMS][4];
+    uint4 qb[B_ITEMS];
+
+    auto issue_loads = [&](int kc) {
+#pragma unroll
+        for (int u = 0; u < A_ITEMS; ++u) {
+            const int i = tid + u * kThreads;
+            const int m = i >> 3, v = i & 7;
+            const int kv = kc * 8 + v;
+            if (kv < vpr) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    qa[u][k] = feat[(int64_t)s_row[m][k] * vpr + kv];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) qa[u][k] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < B_ITEMS; ++u) {
+            const int i = tid + u * kThreads;
+            const int j = i >> 3, v = i & 7;
+            const int kv = kc * 8 + v;
+            qb[u] = (kv < vpr && n0 + j < a.D) ? wgt[(int64_t)(n0 + j) * vpr + kv]
+                                               : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    f32x4_t acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    issue_loads(0);
+    for (int kc = 0; kc < nk; ++kc) {
+        uint4 av[A_ITEMS];
+#pragma unroll
+        for (int u = 0; u < A_ITEMS; ++u) {
+            const int m = (tid + u * kThreads) >> 3;
+            av[u] = blend4<Bf16>(qa[u], s_w[m][0], s_w[m][1], s_w[m][2], s_w[m][3]);
+        }
+        __syncthreads();   // previous chunk's MFMA reads are done
+#pragma unroll
+        for (int u = 0; u < A_ITEMS; ++u) {
+            const int i = tid + u * kThreads;
+            s_a[swz(i >> 3, i & 7)] = av[u];
+        }
+#pragma unroll
+        for (int u = 0; u < B_ITEMS; ++u) {
+            const int i = tid + u * kThreads;
+            s_b[swz(i >> 3, i & 7)] = qb[u];
+        }
+        __syncthreads();
+        if (kc + 1 < nk) issue_loads(kc + 1);
+
+        if constexpr (Bf16) {
+#pragma unroll
+            for (int kk = 0; kk < BK / 32; ++kk) {
+                const int v = kk * 4 + (lane >> 4);
+                bf16x8_t af[MI], bfr[NJ];
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    const int row = wm * WM + i * 16 + (lane & 15);
+                    af[i] = __builtin_bit_cast(bf16x8_t, s_a[swz(row, v)]);
+                }
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int row = wn * WN + j * 16 + (lane & 15);
+                    bfr[j] = __builtin_bit_cast(bf16x8_t, s_b[swz(row, v)]);
+                }
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
+                                                                            acc[i][j], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int kq = 0; kq < BK / 16; ++kq) {
+                const int v = kq * 4 + (lane >> 4);
+                float4 af[MI], bfr[NJ];
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    const int row = wm * WM + i * 16 + (lane & 15);
+                    af[i] = __builtin_bit_cast(float4, s_a[swz(row, v)]);
+                }
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int row = wn * WN + j * 16 + (lane & 15);
+                    bfr[j] = __builtin_bit_cast(float4, s_b[swz(row, v)]);
+                }
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].x, bfr[j].x,
+                                                                        acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].y, bfr[j].y,
+                                                                        acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].z, bfr[j].z,
+                                                                        acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].w, bfr[j].w,
+                                                                        acc[i][j], 0, 0, 0);
+                    }
+            }
+        }
+    }
+
+    // ---- epilogue: + bias, round, stage 16 rows at a time through LDS for
+    // coalesced 16-byte row stores. A 16x16 block's lane l holds rows
+    // 4*(l/16) + r (r = 0..3) of column l % 16.
+    float bias_v[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int col = n0 + wn * WN + j * 16 + (lane & 15);
+        float bv = 0.0f;
+        if (a.bias && col < a.D) {
+            if constexpr (Bf16)
+                bv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.bias)[col] << 16);
+            else
+                bv = reinterpret_cast<const float*>(a.bias)[col];
+        }
+        bias_v[j] = bv;
+    }
+    constexpr int STAGE_VEC = 16 * WN * (int)sizeof(elem_t) / 16;  // vectors per wave stage
+    elem_t* stage = reinterpret_cast<elem_t*>(s_a) + wave * (16 * WN);
+    constexpr int ROW_VEC = WN * (int)sizeof(elem_t) / 16;          // vectors per staged row
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * (lane >> 4) + r;
+                const int col = j * 16 + (lane & 15);
+                const float y = acc[i][j][r] + bias_v[j];
+                if constexpr (Bf16)
+                    stage[row * WN + col] = __builtin_bit_cast(uint16_t, (__bf16)y);
+                else
+                    stage[row * WN + col] = y;
+            }
+        __syncthreads();
+        const uint4* st4 = reinterpret_cast<const uint4*>(stage);
+#pragma unroll
+        for (int q = lane; q < STAGE_VEC; q += 64) {
+            const int row = q / ROW_VEC, cv = q - row * ROW_VEC;
+            const int64_t t = m0 + wm * WM + i * 16 + row;
+            const int col = n0 + wn * WN + cv * EPV;
+            if (t < a.n && col < a.D) {
+                uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<elem_t*>(a.out) +
+                                                      t * a.D + col);
+                *dst = st4[q];
+            }
+        }
+    }
+}
+
+// Null rows [n, n + n_null): the bias (or +0) broadcast, 16-byte stores.
+template <bool Bf16>
+__global__ __launch_bounds__(256) void null_fill_kernel(const void* bias, int32_t D, int64_t n,
+                                                        int64_t n_null, void* out) {
+    constexpr int EPV = Bf16 ? 8 : 4;
+    const int vpr = D / EPV;
+    const int64_t total = n_null * vpr;
+    uint4* o = reinterpret_cast<uint4*>(out) + n * vpr;
+    const uint4* b = reinterpret_cast<const uint4*>(bias);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
+        const int v = (int)(q % vpr);
+        const uint4 val = b ? b[v] : make_uint4(0, 0, 0, 0);
+        store_nt16(o + q, val);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_proj_cond(const ProjCondArgs& a, p3d_dtype dt, const CamTable& cams,
+                            hipStream_t s) {
+    const bool bf16 = dt == P3D_BF16;
+    if (a.n > 0) {
+        const int BM = bf16 ? Cfg<true>::BM : Cfg<false>::BM;
+        const int BN = bf16 ? Cfg<true>::BN : Cfg<false>::BN;
+        int32_t m_tiles = (int32_t)((a.n + BM - 1) / BM);
+        int32_t n_tiles = (a.D + BN - 1) / BN;
+        int32_t per_xcd = (int32_t)(((int64_t)m_tiles * n_tiles + 7) / 8);
+        ProjCondArgs args = a;
+        CamTable tab = cams;
+        void* params[] = {&args, &tab, &m_tiles, &n_tiles, &per_xcd};
+        const void* fn = bf16 ? reinterpret_cast<const void*>(&proj_cond_kernel<true>)
+                              : reinterpret_cast<const void*>(&proj_cond_kernel<false>);
+        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)per_xcd * 8), dim3(kThreads), params,
+                                       0, s);
+        if (e != hipSuccess) return e;
+    }
+    if (a.n_null > 0) {
+        const void* bias = a.bias;
+        int32_t D = a.D;
+        int64_t n = a.n, nn = a.n_null;
+        void* out = a.out;
+        void* params[] = {&bias, &D, &n, &nn, &out};
+        const int64_t vec = a.n_null * (a.D / (bf16 ? 8 : 4));
+        int64_t blocks = (vec + 255) / 256;
+        if (blocks > 8192) blocks = 8192;
+        const void* fn = bf16 ? reinterpret_cast<const void*>(&null_fill_kernel<true>)
+                              : reinterpret_cast<const void*>(&null_fill_kernel<false>);
+        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), params, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace p3d

@@ -1,0 +1,140 @@
+// sample.hip -- p3d_bilinear_sample: grid_sample(bilinear,
+// align_corners=False, padding_mode='border') on a channels-last map
+// (pixel-aligned head commit, pixal3d_mrp_mlx: bilinear_sample).
+//
+// HBM-bound gather. A workgroup owns a run of TOK consecutive points; their
+// four corner rows are read as 16-byte vectors spread across the lanes
+// (eight consecutive lanes cover 128 contiguous bytes of one corner row, so
+// every wave request is made of whole 128-byte segments), blended in
+// binary32 and written with non-temporal 16-byte stores. Consecutive point
+// runs share most corner rows; tiles are mapped so that each XCD walks a
+// contiguous range of runs and those shared rows hit its own L2.
+#include "p3d_internal.h"
+
+namespace p3d {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTok = 16;        // points per workgroup
+constexpr int kUnroll = 4;      // 16-byte items in flight per thread per step
+
+struct Vec8 {
+    float v[8];
+};
+
+// One 16-byte input vector -> values (8 for bf16, 4 for f32).
+__device__ __forceinline__ void widen(const uint4& q, float* v, bool bf16) {
+    if (bf16) {
+        v[0] = bf16lo(q.x); v[1] = bf16hi(q.x);
+        v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
+        v[4] = bf16lo(q.z); v[5] = bf16hi(q.z);
+        v[6] = bf16lo(q.w); v[7] = bf16hi(q.w);
+    } else {
+        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+    }
+}
+
+template <bool InBf16, bool OutBf16>
+__global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, int64_t tiles,
+                                                          int64_t per_xcd) {
+    // XCD-aware order: workgroup g runs on XCD g % 8; give each XCD a
+    // contiguous range of tiles.
+    const int64_t g = blockIdx.x;
+    const int64_t tile = (g & 7) * per_xcd + (g >> 3);
+    if (tile >= tiles) return;
+
+    __shared__ int32_t s_row[kTok][4];
+    __shared__ float s_w[kTok][4];
+
+    const int64_t t0 = tile * kTok;
+    const int ntok = (int)((a.n - t0) < kTok ? (a.n - t0) : kTok);
+    if (threadIdx.x < ntok) {
+        const int64_t t = t0 + threadIdx.x;
+        const float2 gp = reinterpret_cast<const float2*>(a.grid)[t];
+        int32_t b = a.bidx ? a.bidx[t] : 0;
+        b = b < 0 ? 0 : (b >= a.batch ? a.batch - 1 : b);
+        const Corners c = corners_of(gp.x, gp.y, b, a.H, a.W);
+        s_row[threadIdx.x][0] = c.r00; s_row[threadIdx.x][1] = c.r01;
+        s_row[threadIdx.x][2] = c.r10; s_row[threadIdx.x][3] = c.r11;
+        s_w[threadIdx.x][0] = c.w00; s_w[threadIdx.x][1] = c.w01;
+        s_w[threadIdx.x][2] = c.w10; s_w[threadIdx.x][3] = c.w11;
+    }
+    __syncthreads();
+
+    constexpr int kEpv = InBf16 ? 8 : 4;          // elements per 16-byte vector
+    const int vpr = a.C / kEpv;                    // vectors per map row
+    const int items = ntok * vpr;
+    const uint4* __restrict__ feat = reinterpret_cast<const uint4*>(a.feat);
+
+    for (int base = threadIdx.x; base < items; base += kThreads * kUnroll) {
+        uint4 q[kUnroll][4];
+        int tok[kUnroll], vec[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = base + u * kThreads;
+            tok[u] = i < items ? i / vpr : 0;
+            vec[u] = i < items ? i - tok[u] * vpr : 0;
+            if (i < items) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    q[u][k] = feat[(int64_t)s_row[tok[u]][k] * vpr + vec[u]];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = base + u * kThreads;
+            if (i >= items) break;
+            const float w0 = s_w[tok[u]][0], w1 = s_w[tok[u]][1];
+            const float w2 = s_w[tok[u]][2], w3 = s_w[tok[u]][3];
+            float f0[8], f1[8], f2[8], f3[8], r[8];
+            widen(q[u][0], f0, InBf16);
+            widen(q[u][1], f1, InBf16);
+            widen(q[u][2], f2, InBf16);
+            widen(q[u][3], f3, InBf16);
+#pragma unroll
+            for (int e = 0; e < kEpv; ++e)
+                r[e] = fmaf(w3, f3[e], fmaf(w2, f2[e], fmaf(w1, f1[e], w0 * f0[e])));
+            const int64_t t = t0 + tok[u];
+            if (OutBf16) {
+                uint4 o;
+                o.x = pack_bf16x2(r[0], r[1]);
+                o.y = pack_bf16x2(r[2], r[3]);
+                o.z = pack_bf16x2(r[4], r[5]);
+                o.w = pack_bf16x2(r[6], r[7]);
+                uint4* dst = reinterpret_cast<uint4*>(a.out) + t * vpr + vec[u];
+                store_nt16(dst, o);
+            } else {
+                float4* dst = reinterpret_cast<float4*>(a.out) +
+                              (t * a.C + (int64_t)vec[u] * kEpv) / 4;
+                store_nt16(dst, make_uint4(__float_as_uint(r[0]), __float_as_uint(r[1]),
+                                           __float_as_uint(r[2]), __float_as_uint(r[3])));
+                if (kEpv == 8)
+                    store_nt16(dst + 1, make_uint4(__float_as_uint(r[4]), __float_as_uint(r[5]),
+                                                   __float_as_uint(r[6]), __float_as_uint(r[7])));
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sample(const SampleArgs& a, p3d_dtype in, p3d_dtype out, hipStream_t s) {
+    const int64_t tiles = (a.n + kTok - 1) / kTok;
+    const int64_t per_xcd = (tiles + 7) / 8;
+    const int64_t blocks = per_xcd * 8;
+    SampleArgs args = a;
+    int64_t t = tiles, p = per_xcd;
+    void* params[] = {&args, &t, &p};
+    const void* fn;
+    if (in == P3D_BF16 && out == P3D_BF16)
+        fn = reinterpret_cast<const void*>(&sample_kernel<true, true>);
+    else if (in == P3D_BF16)
+        fn = reinterpret_cast<const void*>(&sample_kernel<true, false>);
+    else
+        fn = reinterpret_cast<const void*>(&sample_kernel<false, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), params, 0, s);
+}
+
+}  // namespace p3d

@@ -1,0 +1,168 @@
+"""The C-ABI library loads and exports every entry point include/p3d.h
+declares; host-only helpers and argument validation behave as documented.
+CPU only: no call here reaches a kernel launch (each one fails validation
+first, or enqueues nothing), and the module skips itself on a machine with a
+GPU, where the parity tests cover the same calls for real."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "p3d.h")
+
+
+def _gpu_present():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+pytestmark = pytest.mark.skipif(_gpu_present(), reason="host-only checks (GPU box runs parity)")
+
+
+@pytest.fixture(scope="module")
+def p3d():
+    import pixel_aligned_image_amd
+    return pixel_aligned_image_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(p3d_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(p3d):
+    names = declared_functions()
+    assert len(names) == 8, names
+    lib = ctypes.CDLL(p3d.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(p3d):
+    assert "gfx950" in p3d.p3d_version()
+    for s, name in enumerate(["P3D_OK", "P3D_ERR_INVALID_ARG", "P3D_ERR_SHAPE", "P3D_ERR_DTYPE",
+                              "P3D_ERR_UNSUPPORTED", "P3D_ERR_HIP"]):
+        assert p3d.p3d_status_string(s) == name
+
+
+def test_distance_worked_example(p3d):
+    for e, printed in ((0, "1.094"), (64, "0.875"), (128, "0.729")):
+        assert "%.3f" % p3d.p3d_distance_from_fov(49.13, 512, e) == printed
+
+
+def test_camera_matches_oracle_bits(p3d):
+    import numpy as np
+    import oracle
+    o = oracle.get()
+    for fov in np.linspace(1.0, 179.0, 357):
+        for d in (0.3, 1.0, 1.6, 2.0):
+            f1, d1 = p3d.p3d_make_camera(fov, d)
+            f2, d2 = o.camera(fov, d)
+            assert np.float32(f1) == f2 and np.float32(d1) == d2
+        assert p3d.p3d_distance_from_fov(fov, 512, 0) == o.distance_from_fov(fov, 512, 0)
+
+
+@pytest.mark.parametrize("fov,size,ext", [(0.0, 512, 0), (180.0, 512, 0), (-5.0, 512, 0),
+                                          (float("nan"), 512, 0), (40.0, 0, 0), (40.0, 512, -256)])
+def test_distance_rejects(p3d, fov, size, ext):
+    with pytest.raises(p3d.P3DError) as e:
+        p3d.p3d_distance_from_fov(fov, size, ext)
+    assert e.value.status == p3d.P3D_ERR_INVALID_ARG
+
+
+def test_make_camera_rejects(p3d):
+    for fov, d in ((0.0, 1.0), (40.0, 0.0), (40.0, float("inf")), (40.0, -1.0)):
+        with pytest.raises(p3d.P3DError):
+            p3d.p3d_make_camera(fov, d)
+
+
+# ---------------------------------------------------- validation (raw C ABI)
+NULL = None
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def _cams(p3d, vals):
+    return p3d.make_cameras(vals)
+
+
+def _pc(p3d, **kw):
+    a = dict(coords=FAKE, n=16, R=8, cams=_cams(p3d, [(2.0, 2.0)]), batch=1, feat=FAKE,
+             dtype=p3d.P3D_BF16, H=4, W=4, C=64, weight=FAKE, D=64, Cw=64, bias=NULL,
+             n_null=0, out=FAKE, mask=NULL, stream=NULL)
+    a.update(kw)
+    st = p3d.lib.p3d_proj_cond(a["coords"], a["n"], a["R"], a["cams"], a["batch"], a["feat"],
+                               a["dtype"], a["H"], a["W"], a["C"], a["weight"], a["D"], a["Cw"],
+                               a["bias"], a["n_null"], a["out"], a["mask"], a["stream"])
+    return st, p3d.p3d_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(n=-1), 1, "n must be >= 0"),
+    (dict(R=0), 1, "resolution"),
+    (dict(batch=0), 1, "batch"),
+    (dict(batch=300), 1, "batch"),
+    (dict(H=0), 1, "height/width"),
+    (dict(coords=NULL, n=100), 2, "batch*R^3"),
+    (dict(coords=FAKE + 4), 4, "16-byte aligned"),
+    (dict(dtype=7), 3, "dtype"),
+    (dict(Cw=48), 2, "[64, 48]"),
+    (dict(C=60, Cw=60), 4, "multiple of 8"),
+    (dict(D=60), 4, "out_dim must be a multiple of 8"),
+    (dict(dtype=0, C=62, Cw=62), 4, "multiple of 4"),
+    (dict(n_null=-3), 1, "n_null"),
+    (dict(out=FAKE + 8), 4, "16-byte aligned"),
+    (dict(H=65536, W=65536), 4, "2^31"),
+    (dict(n=(1 << 30) + 1), 4, "n must be <="),
+], ids=lambda v: str(v)[:40])
+def test_proj_cond_validation(p3d, kw, status, needle):
+    st, msg = _pc(p3d, **kw)
+    assert st == status, (st, msg)
+    assert needle in msg, msg
+
+
+def test_proj_cond_camera_validation(p3d):
+    for cam in ((0.0, 2.0), (2.0, 0.0), (float("nan"), 2.0), (2.0, float("inf"))):
+        st, msg = _pc(p3d, cams=_cams(p3d, [cam]))
+        assert st == p3d.P3D_ERR_INVALID_ARG and "cams[0]" in msg
+    st, msg = _pc(p3d, cams=_cams(p3d, [(2.0, 2.0), (2.0, -1.0)]), batch=2)
+    assert st == p3d.P3D_ERR_INVALID_ARG and "cams[1].distance" in msg
+
+
+def test_zero_work_is_ok_without_touching_memory(p3d):
+    st, msg = _pc(p3d, n=0, n_null=0, coords=NULL)
+    assert st == 0, msg
+    st = p3d.lib.p3d_project_points(NULL, 0, 8, _cams(p3d, [(2.0, 2.0)]), 1, 4, 4, NULL, NULL,
+                                    NULL, NULL, NULL, NULL)
+    assert st == 0
+    st = p3d.lib.p3d_bilinear_sample(FAKE, p3d.P3D_BF16, 1, 4, 4, 64, FAKE, NULL, 0, FAKE,
+                                     p3d.P3D_BF16, NULL)
+    assert st == 0
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(fdt=0, odt=1), 3, "BF16 output needs a BF16 map"),
+    (dict(fdt=5), 3, "feat_dtype"),
+    (dict(C=20), 4, "multiple of 8"),
+    (dict(n=-2), 1, "n must be"),
+    (dict(feat=FAKE + 2), 4, "aligned"),
+    (dict(B=0), 1, "map shape"),
+])
+def test_bilinear_sample_validation(p3d, args, status, needle):
+    a = dict(feat=FAKE, fdt=1, B=1, H=4, W=4, C=64, grid=FAKE, bidx=NULL, n=10, out=FAKE, odt=1)
+    a.update(args)
+    st = p3d.lib.p3d_bilinear_sample(a["feat"], a["fdt"], a["B"], a["H"], a["W"], a["C"],
+                                     a["grid"], a["bidx"], a["n"], a["out"], a["odt"], NULL)
+    assert st == status
+    assert needle in p3d.p3d_last_error()
+
+
+def test_project_points_validation(p3d):
+    st = p3d.lib.p3d_project_points(FAKE, 10, 8, NULL, 1, 4, 4, NULL, NULL, NULL, NULL, NULL,
+                                    NULL)
+    assert st == 1 and "cams is NULL" in p3d.p3d_last_error()
+    st = p3d.lib.p3d_project_points(FAKE, 10, 8, _cams(p3d, [(2.0, 2.0)]), 1, 4, 4, FAKE + 4,
+                                    NULL, NULL, NULL, NULL, NULL)
+    assert st == 4 and "8-byte aligned" in p3d.p3d_last_error()

@@ -1,0 +1,308 @@
+"""Benchmark: projected tokens/s of the fused pixel-aligned conditioning path
+on one MI355X, with the roofline of its dominant kernel and the CPU oracle
+timed beside it.
+
+One step = one p3d_proj_cond call over the whole batch: projection of every
+token, bilinear gather, proj_linear on the matrix cores, mask, and the CFG
+null branch. The default workload is the largest one (a 1024^3 sparse shell
+of 100k tokens with a 100k-row null branch, bf16 map 1x512x512x2048,
+proj_linear 2048->1536); inputs are synthetic, seeded and resident in HBM
+before the timed region starts.
+
+Prints ONE JSON line. Fields beyond the common ones:
+  roofline       dominant kernel (the fused gather+MFMA kernel): algorithmic
+                 flops per launch / its mean duration (HIP events on the launch
+                 stream, measured in this run) against the bf16 dense MFMA peak;
+                 traffic = HBM bytes per launch from the committed rocprofv3
+                 FETCH_SIZE/WRITE_SIZE runs, scaled by a copy kernel of known
+                 size, or null if the kernel source changed since.
+  cpu_baseline   the CPU oracle on a bounded prefix of the same tokens.
+  gather         the standalone bilinear gather on the same points: algorithmic
+                 bytes / duration against peak HBM bandwidth.
+  null_fill      the null-branch fill alone: bytes written / duration.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+F32_PEAK_TFLOPS = 157.3        # MI355X fp32 MFMA, TFLOP/s
+DEFAULT_WORKLOAD = "shell1024_cfg_bf16_c2048_d1536"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest():
+    """sha256 over the HIP sources of libp3d: counters taken on one build are
+    reused only while this matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "pixel_aligned_image_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the fused kernel from profiles/, if the sources
+    still match the digest recorded there."""
+    path = os.path.join(PROFILE_DIR, "proj_cond_%s_hbm_traffic.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_digest = re.search(r"source_digest:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_digest and m_bytes) or m_digest.group(1) != kernel_source_digest():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def unique_corner_rows(pixel, bidx, H, W):
+    """Distinct map rows among the four corners of every point (what the
+    gather must fetch at least once)."""
+    import numpy as np
+    x0 = pixel[:, 0].astype(np.int64)
+    y0 = pixel[:, 1].astype(np.int64)
+    x1 = np.minimum(x0 + 1, W - 1)
+    y1 = np.minimum(y0 + 1, H - 1)
+    b = bidx.astype(np.int64)
+    rows = np.concatenate([(b * H + y) * W + x for y in (y0, y1) for x in (x0, x1)])
+    return int(np.unique(rows).size)
+
+
+def time_events(fn, reps, stream):
+    """Mean duration (ms) of fn() over reps launches, HIP events on stream."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline(inp, cams_o, target_s=12.0):
+    """The oracle, untuned, over a prefix of the same tokens until about
+    target_s seconds of CPU work; tokens/s."""
+    import numpy as np
+    import oracle
+    o = oracle.get()
+    want = min(16, len(os.sched_getaffinity(0)))
+    threads = o.set_threads(want)
+    w = inp["w"]
+    fo, do = cams_o
+    done, t_total, chunk = 0, 0.0, 512
+    while t_total < target_s and done < inp["n"]:
+        rows = np.arange(done, min(inp["n"], done + chunk))
+        t0 = time.perf_counter()
+        o.proj_cond_rows(inp["coords"], inp["n"], w.resolution, fo, do, inp["feat"],
+                         inp["weight"], inp["bias"], inp["n_null"], rows)
+        t_total += time.perf_counter() - t0
+        done += rows.size
+        if t_total > 0:
+            chunk = int(max(256, min(8192, rows.size * (target_s - t_total) / max(t_total, 1e-3))))
+    return {"value": done / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d tokens of the same workload (the full path per token: "
+                      "projection, gather, bf16 rounding, proj_linear in binary64), %.1f s, "
+                      "CPU %s" % (done, inp["n"], t_total, cpu_model())}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB per launch (counter scale)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures a single GPU: the path shards by tokens with no per-call "
+              "collective, and only the one-GPU share is measured. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import p3d_synth as synth
+    import pixel_aligned_image_amd as p3d
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(args.warmup + args.steps):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                          "launches": args.warmup + args.steps}))
+        return
+
+    w = synth.workload(args.workload)
+    bf16 = w.dtype == "bf16"
+    t_gen = time.perf_counter()
+    coords = synth.coords(w)
+    feat_np = synth.feature_map(w)
+    weight_np = synth.weight(w)
+    bias_np = synth.bias(w)
+    fovs = synth.fovs(w)
+    n, n_null = w.n_tokens, w.n_null
+    t_gen = time.perf_counter() - t_gen
+
+    def dev(a, as_bf16=False):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if as_bf16:
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.cuda()
+
+    coords_d = dev(coords)
+    feat = dev(feat_np, bf16)
+    weight = dev(weight_np, bf16)
+    bias = dev(bias_np, bf16)
+    dists = [w.distance] * w.batch
+    cams = []
+    for a, d in zip(fovs, dists):
+        cams.append(p3d.p3d_make_camera(a, d if d is not None else
+                                        p3d.p3d_distance_from_fov(a, w.width, 0)))
+    camarr = p3d.make_cameras(cams)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    out = torch.empty((n + n_null, w.out_dim), dtype=dt, device="cuda")
+    mask = torch.empty((n,), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        p3d.p3d_proj_cond(coords_d, n, w.resolution, camarr, feat, weight, out, bias=bias,
+                          n_null=n_null, mask=mask)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- dominant kernel alone (same launch configuration, no null rows)
+    out_tokens, out_null = out[:n], out[n:]
+
+    def fused_only():
+        p3d.p3d_proj_cond(coords_d, n, w.resolution, camarr, feat, weight, out_tokens,
+                          bias=bias, n_null=0, mask=mask)
+
+    def null_only():
+        p3d.p3d_proj_cond(None, 0, w.resolution, camarr, feat, weight, out_null, bias=bias,
+                          n_null=n_null)
+
+    reps = max(args.steps, 5)
+    fused_ms = time_events(fused_only, reps, stream)
+    null_ms = time_events(null_only, reps, stream) if n_null else 0.0
+
+    # ---- the standalone gather on the same points
+    grid = torch.empty((n, 2), device="cuda")
+    pixel = torch.empty((n, 2), dtype=torch.int32, device="cuda")
+    p3d.p3d_project_points(coords_d, n, w.resolution, camarr, w.height, w.width, grid=grid,
+                           pixel=pixel)
+    bidx_np = coords[:, 0].copy() if coords is not None else np.repeat(
+        np.arange(w.batch, dtype=np.int32), w.resolution ** 3)
+    bidx = dev(bidx_np)
+    s_out = torch.empty((n, w.channels), dtype=dt, device="cuda")
+
+    def gather_only():
+        p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx)
+
+    gather_only()
+    gather_ms = time_events(gather_only, reps, stream)
+    torch.cuda.synchronize()
+    U = unique_corner_rows(pixel.cpu().numpy(), bidx_np, w.height, w.width)
+    s = 2 if bf16 else 4
+    C, D = w.channels, w.out_dim
+    flops = 2.0 * n * C * D
+    fused_bytes = 16 * n + U * C * s + D * C * s + (D * s if bias is not None else 0) \
+        + n * D * s + n
+    gather_bytes = 8 * n + 4 * n + U * C * s + n * C * s
+    null_bytes = n_null * D * s
+    peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
+    achieved = flops / (fused_ms * 1e-3) / 1e12
+    traffic = recorded_traffic(w.name)
+
+    line = {
+        "metric": "projected tokens/sec (project+sample+proj_linear); HBM GB/s & MFMA % of peak",
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": n, "null_rows": n_null,
+                   "resolution": w.resolution, "batch": w.batch,
+                   "map": "%dx%dx%dx%d %s NHWC" % (w.batch, w.height, w.width, C, w.dtype),
+                   "proj_linear": "%d->%d%s" % (C, D, " +bias" if bias is not None else ""),
+                   "unique_corner_rows": U},
+        "rows_per_sec_incl_null": (n + n_null) / (ms_per_step * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "proj_cond_kernel", "mean_ms": fused_ms,
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": fused_bytes},
+        "gather": {"bound": "hbm", "achieved": gather_bytes / (gather_ms * 1e-3) / 1e9,
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": gather_bytes / (gather_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "kernel": "sample_kernel", "mean_ms": gather_ms,
+                   "algorithmic_bytes_per_launch": gather_bytes},
+        "null_fill": {"bound": "hbm", "mean_ms": null_ms,
+                      "achieved": null_bytes / (null_ms * 1e-3) / 1e9 if null_ms else None,
+                      "unit": "GB/s", "bytes_per_launch": null_bytes},
+        "input_generation_s": t_gen,
+        "source_digest": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        o = oracle.get()
+        fo, do = o.cameras(fovs, [d if d is not None else o.distance_from_fov(a, w.width, 0)
+                                  for a, d in zip(fovs, dists)])
+        inp = dict(w=w, coords=coords, n=n, n_null=n_null, feat=feat_np, weight=weight_np,
+                   bias=bias_np)
+        line["cpu_baseline"] = cpu_baseline(inp, (fo, do))
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

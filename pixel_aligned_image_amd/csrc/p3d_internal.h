@@ -182,5 +182,7 @@ hipError_t launch_project(const ProjectArgs& a, const CamTable& cams, hipStream_
 hipError_t launch_sample(const SampleArgs& a, p3d_dtype in, p3d_dtype out, hipStream_t s);
 hipError_t launch_proj_cond(const ProjCondArgs& a, p3d_dtype dt, const CamTable& cams,
                             hipStream_t s);
+// bf16 fused kernel; writes the null rows too when a.n > 0
+hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hipStream_t s);
 
 }  // namespace p3d

@@ -28,10 +28,6 @@ constexpr int kThreads = 256;   // 4 waves, 2 (M) x 2 (N)
 template <bool Bf16>
 struct Cfg;
 template <>
-struct Cfg<true> {
-    static constexpr int BM = 128, BN = 256, BK = 64, EPV = 8;
-};
-template <>
 struct Cfg<false> {
     static constexpr int BM = 128, BN = 128, BK = 32, EPV = 4;
 };
@@ -308,19 +304,17 @@ __global__ __launch_bounds__(256) void null_fill_kernel(const void* bias, int32_
 hipError_t launch_proj_cond(const ProjCondArgs& a, p3d_dtype dt, const CamTable& cams,
                             hipStream_t s) {
     const bool bf16 = dt == P3D_BF16;
+    if (bf16 && a.n > 0) return launch_proj_cond_bf16(a, cams, s);   // null rows included
     if (a.n > 0) {
-        const int BM = bf16 ? Cfg<true>::BM : Cfg<false>::BM;
-        const int BN = bf16 ? Cfg<true>::BN : Cfg<false>::BN;
+        const int BM = Cfg<false>::BM, BN = Cfg<false>::BN;
         int32_t m_tiles = (int32_t)((a.n + BM - 1) / BM);
         int32_t n_tiles = (a.D + BN - 1) / BN;
         int32_t per_xcd = (int32_t)(((int64_t)m_tiles * n_tiles + 7) / 8);
         ProjCondArgs args = a;
         CamTable tab = cams;
         void* params[] = {&args, &tab, &m_tiles, &n_tiles, &per_xcd};
-        const void* fn = bf16 ? reinterpret_cast<const void*>(&proj_cond_kernel<true>)
-                              : reinterpret_cast<const void*>(&proj_cond_kernel<false>);
-        hipError_t e = hipLaunchKernel(fn, dim3((unsigned)per_xcd * 8), dim3(kThreads), params,
-                                       0, s);
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&proj_cond_kernel<false>),
+                                       dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
         if (e != hipSuccess) return e;
     }
     if (a.n_null > 0) {

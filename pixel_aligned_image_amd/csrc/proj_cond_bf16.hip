@@ -1,0 +1,345 @@
+// proj_cond_bf16.hip -- the fused projection -> gather -> proj_linear kernel
+// for bf16 maps and weights (fp32 accumulation on the matrix cores), plus the
+// CFG null-branch rows in the same launch.
+//
+// Sources: pixal3d_mrp_mlx tests/ history, pixel-aligned head commit
+// (project_points, bilinear_sample with grid_sample's align_corners=False,
+// border padding); trellis.cpp PR #38 "Initial support for Pixal3D",
+// FlowCond commit (proj_linear; the null proj is zeroed on the device, so its
+// rows are proj_linear(0) = bias).
+//
+// GEMM view: Y[M=n, N=D] = S[M, K=C] W[N, K]^T + b, S never stored.
+//
+// Workgroup: 128 tokens x 512 output features, 4 waves (one per SIMD, 512
+// registers each), one workgroup per CU (the whole 160 KB of LDS). Wave w
+// owns features [128w, 128w + 128) for all 128 tokens: 8 x 8 blocks of
+// v_mfma_f32_16x16x32_bf16 (256 accumulator registers) with W as the row
+// operand and S as the column operand, so each lane ends up with four
+// consecutive features of one token.
+//
+// Per 64-channel K chunk:
+//   W tile (512 rows x 128 bytes) arrives through global_load_lds_dwordx4,
+//   each wave loading the rows of its own features, eight full 128-byte rows
+//   per wave instruction (a wave instruction covering 16 rows x 64 bytes,
+//   which is what loading MFMA fragments straight from a row-major W would
+//   do, moves about a third of the bytes per clock). The LDS slot of each
+//   16-byte vector is swizzled through the source address, since the
+//   destination of a direct load is fixed by the lane number. Two W stages.
+//   S tile (128 tokens x 64 channels): each thread gathers four 16-byte
+//   vectors of the four corner rows into registers a chunk ahead, blends
+//   them in binary32, rounds to bf16 and writes them to one of two LDS
+//   stages.
+// Why 128 x 512: every N tile repeats the gather (four corner reads and a
+// blend per token and channel), every M tile re-reads W; with 64K fp32
+// accumulators per CU, 128 x 512 minimises the sum.
+// Tile order: workgroup g runs on XCD g % 8; each XCD walks a contiguous
+// range of (token tile, N tile) pairs, N fastest, so the N tiles of a token
+// tile and its neighbours share corner rows in that XCD's L2.
+// Null rows: each workgroup also writes the 128 x 512 blocks of the null
+// branch (the bias broadcast) with its own token-tile index, after its
+// output tile; those stores overlap the matrix work of the other CUs.
+#include "p3d_internal.h"
+
+namespace p3d {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int NWAVES = 4;           // one wave per SIMD: 512 registers each
+constexpr int kThreads = 64 * NWAVES;
+constexpr int BM = 128, BN = 512, BK = 64;
+constexpr int WN = BN / NWAVES;     // features per wave
+constexpr int TI = BM / 16;         // token blocks per wave
+constexpr int FJ = WN / 16;         // feature blocks per wave
+constexpr int G_ITEMS = BM * (BK / 8) / kThreads;   // gathered vectors per thread per chunk
+constexpr int W_INSTR = WN * (BK / 8) / 64;         // direct W loads per lane per chunk
+constexpr int NULL_VEC = BM * BN / 8;               // 16-byte vectors of a null block
+
+// LDS slot of 16-byte vector v (0..7) of tile row `row` (128-byte rows).
+// Sixteen lanes reading vector v of sixteen consecutive rows then hit
+// sixteen distinct 16-byte slots of a 256-byte bank window (64 banks).
+__device__ __forceinline__ int slot(int row, int v) { return row * 8 + (v ^ ((row >> 1) & 7)); }
+
+__device__ __forceinline__ uint4 blend_bf16(const uint4 (&q)[4], const float (&w)[4]) {
+    const uint32_t* a = reinterpret_cast<const uint32_t*>(&q[0]);
+    const uint32_t* b = reinterpret_cast<const uint32_t*>(&q[1]);
+    const uint32_t* c = reinterpret_cast<const uint32_t*>(&q[2]);
+    const uint32_t* d = reinterpret_cast<const uint32_t*>(&q[3]);
+    uint4 o;
+    uint32_t* r = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float lo = fmaf(w[3], bf16lo(d[e]), fmaf(w[2], bf16lo(c[e]),
+                              fmaf(w[1], bf16lo(b[e]), w[0] * bf16lo(a[e]))));
+        const float hi = fmaf(w[3], bf16hi(d[e]), fmaf(w[2], bf16hi(c[e]),
+                              fmaf(w[1], bf16hi(b[e]), w[0] * bf16hi(a[e]))));
+        r[e] = pack_bf16x2(lo, hi);
+    }
+    return o;
+}
+
+// Per-thread state of the K pipeline.
+struct Pipe {
+    const uint4* feat;
+    const uint4* wgt;
+    int vpr, D, W, n0, tid, lane, wave;
+    int gv;                          // vector of each gathered 128-byte segment
+    int wrow0, wv_even, wv_odd;      // direct W loads
+    int4 gt[G_ITEMS];                // (top-left row, steps, tx, ty) per item
+    uint4 gq[G_ITEMS][4];            // corner vectors in flight
+    f32x4_t acc[FJ][TI];
+
+    // Queue the four corner vectors of every item for chunk kc. A K tail
+    // (C not a multiple of 64, or the padding chunk) clamps the address and
+    // zeroes the value.
+    __device__ __forceinline__ void gather_issue(int kc) {
+        const int kv = min(kc * 8 + gv, vpr - 1);
+#pragma unroll
+        for (int u = 0; u < G_ITEMS; ++u) {
+            // the 32-bit row index stays live, not four hoisted 64-bit
+            // addresses (those would not fit in the registers)
+            int32_t r00 = gt[u].x, steps = gt[u].y;
+            asm volatile("" : "+v"(r00), "+v"(steps));
+            const int32_t dx = steps & 1, dyw = (steps & 2) ? W : 0;
+            const int32_t rows[4] = {r00, r00 + dx, r00 + dyw, r00 + dyw + dx};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) gq[u][k] = feat[(int64_t)rows[k] * vpr + kv];
+        }
+        if ((kc + 1) * 8 > vpr) {                     // uniform: partial or padding chunk
+            const bool dead = kc * 8 + gv >= vpr;
+#pragma unroll
+            for (int u = 0; u < G_ITEMS; ++u)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (dead) gq[u][k] = make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    // Blend the queued vectors (bilinear weights computed as in the
+    // standalone sampler) and store the bf16 S chunk into sa.
+    __device__ __forceinline__ void gather_commit(uint4* __restrict__ sa) {
+#pragma unroll
+        for (int u = 0; u < G_ITEMS; ++u) {
+            const float tx = __int_as_float(gt[u].z), ty = __int_as_float(gt[u].w);
+            float w[4] = {(1.0f - tx) * (1.0f - ty), tx * (1.0f - ty), (1.0f - tx) * ty, tx * ty};
+            if (gt[u].y & 4) w[0] = 0.0f;             // padding token: all weights 0
+            sa[slot((tid + u * kThreads) >> 3, gv)] = blend_bf16(gq[u], w);
+        }
+    }
+
+    // This wave's W rows of chunk kc into sw: row wave*WN + q*8 + lane/8,
+    // LDS slot lane%8, which holds logical vector (lane%8) ^ ((row/2) % 8);
+    // that swizzle only depends on the parity of q.
+    __device__ __forceinline__ void w_issue(uint4* __restrict__ sw, int kc) {
+#pragma unroll
+        for (int q = 0; q < W_INSTR; ++q) {
+            int col = min(n0 + wrow0 + q * 8, D - 1);   // rows past D: discarded later
+            asm volatile("" : "+v"(col));
+            const int kv = min(kc * 8 + ((q & 1) ? wv_odd : wv_even), vpr - 1);  // K tail: S is 0
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const void*>(wgt + (int64_t)col * vpr + kv),
+                (lds_void*)(sw + (wave * WN + q * 8) * 8), 16, 0, 0);
+        }
+    }
+
+    // The chunk's 2 x 8 x 8 MFMAs; the next token block's S fragment is read
+    // while the current one multiplies.
+    __device__ __forceinline__ void mfma_chunk(const uint4* __restrict__ sa,
+                                               const uint4* __restrict__ sw) {
+        const int n = lane & 15, g4 = lane >> 4;
+#pragma unroll
+        for (int s = 0; s < BK / 32; ++s) {
+            const int v = s * 4 + g4;
+            bf16x8_t wf[FJ];
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                wf[j] = __builtin_bit_cast(bf16x8_t, sw[slot(wave * WN + j * 16 + n, v)]);
+            bf16x8_t sf = __builtin_bit_cast(bf16x8_t, sa[slot(n, v)]);
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const bf16x8_t sf_next = __builtin_bit_cast(
+                    bf16x8_t, sa[slot(((i + 1) % TI) * 16 + n, v)]);
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], sf, acc[j][i],
+                                                                        0, 0, 0);
+                sf = sf_next;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+};
+
+// One K chunk kc. First blend chunk kc+1 (its corner rows were queued a chunk
+// ago) into sa_n -- the wait for those loads also covers this wave's W tile
+// of chunk kc, queued right after them -- then queue W of chunk kc+1 into
+// sw_n and the corner rows of chunk kc+2, and only then run chunk kc on the
+// matrix cores while all of that is in flight. Each wave reads only the W
+// rows it loaded itself, so W needs no barrier; the barrier publishes sa_n
+// and frees sa. The LDS stages are restrict parameters so that the compiler
+// can tell the direct W loads apart from the other LDS accesses.
+__device__ __forceinline__ void pipe_step(Pipe& p, int kc, int nk2,
+                                          const uint4* __restrict__ sa,
+                                          const uint4* __restrict__ sw,
+                                          uint4* __restrict__ sa_n,
+                                          uint4* __restrict__ sw_n) {
+    if (kc + 1 < nk2) {
+        p.gather_commit(sa_n);
+        p.w_issue(sw_n, kc + 1);
+        if (kc + 2 < nk2) p.gather_issue(kc + 2);
+    } else {
+        // s_waitcnt vmcnt(0) (expcnt, lgkmcnt at their maxima): this wave's W
+        // tile of the last chunk has landed
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    p.mfma_chunk(sa, sw);
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a, CamTable cams,
+                                                                  int32_t m_tiles,
+                                                                  int32_t n_tiles,
+                                                                  int32_t per_xcd,
+                                                                  int32_t null_tiles) {
+    __shared__ uint4 sW0[BN * 8], sW1[BN * 8];     // 2 x 64 KB
+    __shared__ uint4 sA0[BM * 8], sA1[BM * 8];     // 2 x 16 KB
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    const int32_t g = blockIdx.x;
+    const int32_t tile = (g & 7) * per_xcd + (g >> 3);
+    if (tile >= m_tiles * n_tiles) return;
+    const int32_t mt = tile / n_tiles, nt = tile - mt * n_tiles;
+    const int64_t m0 = (int64_t)mt * BM;
+    const int32_t n0 = nt * BN;
+
+    // ---- project the tile's tokens; per token park (top-left row, the
+    // row steps to the right / lower corner, the two fractions) in sA1
+    int4* s_tok = reinterpret_cast<int4*>(sA1);                // [BM]
+    if (tid < BM) {
+        const int64_t t = m0 + tid;
+        int4 e = make_int4(0, 4, 0, 0);                         // padding token: weights 0
+        if (t < a.n) {
+            int32_t b, x, y, z;
+            token_cell(a.coords, t, a.R, b, x, y, z);
+            const Projected p = project_cell(b, x, y, z, a.R, cams, a.batch);
+            const SrcIdx sx = source_index(p.gx, a.W);
+            const SrcIdx sy = source_index(p.gy, a.H);
+            e.x = (p.b * a.H + sy.i0) * a.W + sx.i0;
+            e.y = (sx.i1 - sx.i0) | ((sy.i1 - sy.i0) << 1);     // 0/1 steps in x and y
+            e.z = __float_as_int(sx.t);
+            e.w = __float_as_int(sy.t);
+            if (a.mask && nt == 0) a.mask[t] = p.mask;
+        }
+        s_tok[tid] = e;
+    }
+    __syncthreads();
+
+    Pipe p;
+    p.feat = reinterpret_cast<const uint4*>(a.feat);
+    p.wgt = reinterpret_cast<const uint4*>(a.weight);
+    p.vpr = a.C >> 3;                                  // 16-byte vectors per row
+    p.D = a.D;
+    p.W = a.W;
+    p.n0 = n0;
+    p.tid = tid;
+    p.lane = lane;
+    p.wave = wave;
+    p.gv = tid & 7;
+    p.wrow0 = wave * WN + (lane >> 3);
+    p.wv_even = (lane & 7) ^ ((lane >> 4) & 7);
+    p.wv_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
+#pragma unroll
+    for (int u = 0; u < G_ITEMS; ++u) p.gt[u] = s_tok[(tid + u * kThreads) >> 3];
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int i = 0; i < TI; ++i) p.acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();                                   // sA1 is free again
+
+    // ---- K loop, two chunks per iteration so every LDS stage is named
+    // statically; an odd chunk count is padded with one all-zero chunk
+    // (gather and W loads are clamped and the gathered values zeroed).
+    const int nk = (a.C + BK - 1) / BK;
+    const int nk2 = (nk + 1) & ~1;
+    p.gather_issue(0);
+    p.gather_commit(sA0);
+    p.w_issue(sW0, 0);
+    p.gather_issue(1);
+    __syncthreads();
+    for (int kc = 0; kc < nk2; kc += 2) {
+        pipe_step(p, kc, nk2, sA0, sW0, sA1, sW1);
+        pipe_step(p, kc + 1, nk2, sA1, sW1, sA0, sW0);
+    }
+
+    // ---- epilogue: + bias, round to bf16, stage each wave's 128 x 128 tile
+    // in the free W stages (token-major, 256-byte rows), 16-byte row stores.
+    // Lane l of block (j, i) holds features 4*(l/16) + r of token l % 16.
+    uint4* out4 = reinterpret_cast<uint4*>(a.out);
+    const int dv = a.D >> 3;                           // 16-byte vectors per output row
+    const int fbase = n0 + wave * WN;
+    constexpr int WAVES_PER_STAGE = NWAVES / 2;
+    uint4* stage4 = (wave < WAVES_PER_STAGE ? sW0 : sW1) +
+                    (wave % WAVES_PER_STAGE) * (BM * WN / 8);
+    uint2* stage2 = reinterpret_cast<uint2*>(stage4);
+    const uint16_t* bias16 = reinterpret_cast<const uint16_t*>(a.bias);
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+        float bv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int f = fbase + j * 16 + 4 * (lane >> 4) + r;
+            bv[r] = (bias16 && f < a.D) ? __uint_as_float((uint32_t)bias16[f] << 16) : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            const int t = i * 16 + (lane & 15);
+            const int f = j * 16 + 4 * (lane >> 4);
+            uint2 pk;
+            pk.x = pack_bf16x2(p.acc[j][i][0] + bv[0], p.acc[j][i][1] + bv[1]);
+            pk.y = pack_bf16x2(p.acc[j][i][2] + bv[2], p.acc[j][i][3] + bv[3]);
+            stage2[(t * WN + f) >> 2] = pk;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = lane; q < BM * WN / 8; q += 64) {
+        const int t = q / (WN / 8), cv = q % (WN / 8);
+        const int64_t tok = m0 + t;
+        const int colv = (fbase >> 3) + cv;
+        if (tok < a.n && colv < dv) out4[tok * dv + colv] = stage4[q];
+    }
+
+    // ---- null blocks of this workgroup: q = mt, mt + m_tiles, ...
+    const uint4* bias4 = reinterpret_cast<const uint4*>(a.bias);
+    for (int32_t q = mt; q < null_tiles; q += m_tiles) {
+        for (int idx = tid; idx < NULL_VEC; idx += kThreads) {
+            const int r = idx >> 6, cv = idx & 63;     // 64 vectors per 512-wide row
+            const int64_t row = a.n + (int64_t)q * BM + r;
+            const int colv = (n0 >> 3) + cv;
+            if (row < a.n + a.n_null && colv < dv) {
+                const uint4 val = bias4 ? bias4[colv] : make_uint4(0, 0, 0, 0);
+                store_nt16(out4 + row * dv + colv, val);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hipStream_t s) {
+    int32_t m_tiles = (int32_t)((a.n + BM - 1) / BM);
+    int32_t n_tiles = (a.D + BN - 1) / BN;
+    int32_t per_xcd = (int32_t)(((int64_t)m_tiles * n_tiles + 7) / 8);
+    int32_t null_tiles = (int32_t)((a.n_null + BM - 1) / BM);
+    ProjCondArgs args = a;
+    CamTable tab = cams;
+    void* params[] = {&args, &tab, &m_tiles, &n_tiles, &per_xcd, &null_tiles};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_cond_bf16_kernel),
+                           dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
+}
+
+}  // namespace p3d

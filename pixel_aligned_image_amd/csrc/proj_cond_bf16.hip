@@ -10,34 +10,39 @@
 //
 // GEMM view: Y[M=n, N=D] = S[M, K=C] W[N, K]^T + b, S never stored.
 //
-// Workgroup: 128 tokens x 512 output features, 4 waves (one per SIMD, 512
-// registers each), one workgroup per CU (the whole 160 KB of LDS). Wave w
-// owns features [128w, 128w + 128) for all 128 tokens: 8 x 8 blocks of
-// v_mfma_f32_16x16x32_bf16 (256 accumulator registers) with W as the row
-// operand and S as the column operand, so each lane ends up with four
-// consecutive features of one token.
+// Workgroup: 128 tokens x 512 output features, one workgroup per CU (all 160
+// KB of LDS), 12 waves in two roles, three waves per SIMD:
+//   8 consumer waves (two per SIMD) only run the matrix cores: consumer c
+//     owns features [64c, 64c + 64) for all 128 tokens, 4 x 8 blocks of
+//     v_mfma_f32_16x16x32_bf16 (128 accumulator registers), W as the row
+//     operand and S as the column operand (a lane ends up with four
+//     consecutive features of one token);
+//   4 producer waves (one per SIMD) do everything else: project the tokens,
+//     keep the corner-row gather a chunk ahead in registers, blend and
+//     round the samples into the LDS S tile, stream W through LDS with
+//     direct loads, and write the null rows at the end.
+// A wave issuing MFMAs is held at each one until the matrix core takes it,
+// so a wave's own VALU work does not overlap its MFMAs; a producer on the
+// same SIMD fills those issue slots instead.
 //
-// Per 64-channel K chunk:
-//   W tile (512 rows x 128 bytes) arrives through global_load_lds_dwordx4,
-//   each wave loading the rows of its own features, eight full 128-byte rows
-//   per wave instruction (a wave instruction covering 16 rows x 64 bytes,
-//   which is what loading MFMA fragments straight from a row-major W would
-//   do, moves about a third of the bytes per clock). The LDS slot of each
-//   16-byte vector is swizzled through the source address, since the
-//   destination of a direct load is fixed by the lane number. Two W stages.
-//   S tile (128 tokens x 64 channels): each thread gathers four 16-byte
-//   vectors of the four corner rows into registers a chunk ahead, blends
-//   them in binary32, rounds to bf16 and writes them to one of two LDS
-//   stages.
+// Per 64-channel K chunk k (barrier B_k before it):
+//   consumers: MFMA on S stage k%2 and W stage k%2;
+//   producers: queue W of chunk k+1 into W stage (k+1)%2 (freed at B_k),
+//     blend chunk k+1 (queued a chunk ago) into S stage (k+1)%2, queue the
+//     corner rows of chunk k+2, then wait for their own W loads;
+//   B_{k+1}.
+// W tile (512 rows x 128 bytes) arrives through global_load_lds_dwordx4,
+// eight full 128-byte rows per wave instruction (16 rows x 64 bytes, which
+// is what loading MFMA fragments straight from a row-major W would do, moves
+// about a third of the bytes per clock); the LDS slot of each 16-byte vector
+// is swizzled through the source address, since the destination of a direct
+// load is fixed by the lane number.
 // Why 128 x 512: every N tile repeats the gather (four corner reads and a
 // blend per token and channel), every M tile re-reads W; with 64K fp32
 // accumulators per CU, 128 x 512 minimises the sum.
 // Tile order: workgroup g runs on XCD g % 8; each XCD walks a contiguous
 // range of (token tile, N tile) pairs, N fastest, so the N tiles of a token
 // tile and its neighbours share corner rows in that XCD's L2.
-// Null rows: each workgroup also writes the 128 x 512 blocks of the null
-// branch (the bias broadcast) with its own token-tile index, after its
-// output tile; those stores overlap the matrix work of the other CUs.
 #include "p3d_internal.h"
 
 namespace p3d {
@@ -46,15 +51,34 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int NWAVES = 4;           // one wave per SIMD: 512 registers each
-constexpr int kThreads = 64 * NWAVES;
+constexpr int N_CONS = 8, N_PROD = 4;
+constexpr int kThreads = 64 * (N_CONS + N_PROD);
+constexpr int kProdThreads = 64 * N_PROD;
 constexpr int BM = 128, BN = 512, BK = 64;
-constexpr int WN = BN / NWAVES;     // features per wave
-constexpr int TI = BM / 16;         // token blocks per wave
-constexpr int FJ = WN / 16;         // feature blocks per wave
-constexpr int G_ITEMS = BM * (BK / 8) / kThreads;   // gathered vectors per thread per chunk
-constexpr int W_INSTR = WN * (BK / 8) / 64;         // direct W loads per lane per chunk
-constexpr int NULL_VEC = BM * BN / 8;               // 16-byte vectors of a null block
+constexpr int WN = BN / N_CONS;     // features per consumer wave
+constexpr int TI = BM / 16;         // token blocks per consumer wave
+constexpr int FJ = WN / 16;         // feature blocks per consumer wave
+constexpr int G_ITEMS = BM * (BK / 8) / kProdThreads;   // gathered vectors per producer thread
+constexpr int W_ROWS = BN / N_PROD;                     // W rows loaded per producer wave
+constexpr int W_INSTR = W_ROWS * (BK / 8) / 64;         // direct W loads per producer lane
+constexpr int NULL_VEC = BM * BN / 8;                   // 16-byte vectors of a null block
+
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maxima (gfx9 layout:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for LDS hand-offs only: this wave's LDS accesses have
+// completed, then s_barrier. Unlike __syncthreads() it does not wait for
+// outstanding global loads (that fence drains vmcnt), so the gather queued
+// for a later chunk stays in flight across it; whoever hands over data that
+// arrived by direct-to-LDS loads waits for those explicitly first.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // LDS slot of 16-byte vector v (0..7) of tile row `row` (128-byte rows).
 // Sixteen lanes reading vector v of sixteen consecutive rows then hit
@@ -79,21 +103,20 @@ __device__ __forceinline__ uint4 blend_bf16(const uint4 (&q)[4], const float (&w
     return o;
 }
 
-// Per-thread state of the K pipeline.
-struct Pipe {
+typedef uint4 Gq[G_ITEMS][4];
+
+// Producer state: one thread of the four producer waves.
+struct Producer {
     const uint4* feat;
     const uint4* wgt;
-    int vpr, D, W, n0, tid, lane, wave;
+    int vpr, D, W, n0, ptid, lane, pw;
     int gv;                          // vector of each gathered 128-byte segment
-    int wrow0, wv_even, wv_odd;      // direct W loads
     int4 gt[G_ITEMS];                // (top-left row, steps, tx, ty) per item
-    uint4 gq[G_ITEMS][4];            // corner vectors in flight
-    f32x4_t acc[FJ][TI];
 
-    // Queue the four corner vectors of every item for chunk kc. A K tail
-    // (C not a multiple of 64, or the padding chunk) clamps the address and
+    // Queue the four corner vectors of every item of chunk kc. A K tail (C
+    // not a multiple of 64, or the padding chunk) clamps the address and
     // zeroes the value.
-    __device__ __forceinline__ void gather_issue(int kc) {
+    __device__ __forceinline__ void gather_issue(Gq& gq, int kc) const {
         const int kv = min(kc * 8 + gv, vpr - 1);
 #pragma unroll
         for (int u = 0; u < G_ITEMS; ++u) {
@@ -118,83 +141,76 @@ struct Pipe {
 
     // Blend the queued vectors (bilinear weights computed as in the
     // standalone sampler) and store the bf16 S chunk into sa.
-    __device__ __forceinline__ void gather_commit(uint4* __restrict__ sa) {
+    __device__ __forceinline__ void commit(const Gq& gq, uint4* __restrict__ sa) const {
 #pragma unroll
         for (int u = 0; u < G_ITEMS; ++u) {
             const float tx = __int_as_float(gt[u].z), ty = __int_as_float(gt[u].w);
             float w[4] = {(1.0f - tx) * (1.0f - ty), tx * (1.0f - ty), (1.0f - tx) * ty, tx * ty};
             if (gt[u].y & 4) w[0] = 0.0f;             // padding token: all weights 0
-            sa[slot((tid + u * kThreads) >> 3, gv)] = blend_bf16(gq[u], w);
+            sa[slot((ptid + u * kProdThreads) >> 3, gv)] = blend_bf16(gq[u], w);
         }
     }
 
-    // This wave's W rows of chunk kc into sw: row wave*WN + q*8 + lane/8,
+    // This wave's W rows of chunk kc into sw: row pw*W_ROWS + q*8 + lane/8,
     // LDS slot lane%8, which holds logical vector (lane%8) ^ ((row/2) % 8);
     // that swizzle only depends on the parity of q.
-    __device__ __forceinline__ void w_issue(uint4* __restrict__ sw, int kc) {
+    __device__ __forceinline__ void w_issue(uint4* __restrict__ sw, int kc) const {
+        const int wv_even = (lane & 7) ^ ((lane >> 4) & 7);
+        const int wv_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
 #pragma unroll
         for (int q = 0; q < W_INSTR; ++q) {
-            int col = min(n0 + wrow0 + q * 8, D - 1);   // rows past D: discarded later
+            int col = min(n0 + pw * W_ROWS + q * 8 + (lane >> 3), D - 1);  // rows past D: unused
             asm volatile("" : "+v"(col));
             const int kv = min(kc * 8 + ((q & 1) ? wv_odd : wv_even), vpr - 1);  // K tail: S is 0
             __builtin_amdgcn_global_load_lds(
                 reinterpret_cast<const void*>(wgt + (int64_t)col * vpr + kv),
-                (lds_void*)(sw + (wave * WN + q * 8) * 8), 16, 0, 0);
-        }
-    }
-
-    // The chunk's 2 x 8 x 8 MFMAs; the next token block's S fragment is read
-    // while the current one multiplies.
-    __device__ __forceinline__ void mfma_chunk(const uint4* __restrict__ sa,
-                                               const uint4* __restrict__ sw) {
-        const int n = lane & 15, g4 = lane >> 4;
-#pragma unroll
-        for (int s = 0; s < BK / 32; ++s) {
-            const int v = s * 4 + g4;
-            bf16x8_t wf[FJ];
-#pragma unroll
-            for (int j = 0; j < FJ; ++j)
-                wf[j] = __builtin_bit_cast(bf16x8_t, sw[slot(wave * WN + j * 16 + n, v)]);
-            bf16x8_t sf = __builtin_bit_cast(bf16x8_t, sa[slot(n, v)]);
-#pragma unroll
-            for (int i = 0; i < TI; ++i) {
-                const bf16x8_t sf_next = __builtin_bit_cast(
-                    bf16x8_t, sa[slot(((i + 1) % TI) * 16 + n, v)]);
-#pragma unroll
-                for (int j = 0; j < FJ; ++j)
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], sf, acc[j][i],
-                                                                        0, 0, 0);
-                sf = sf_next;
-                __builtin_amdgcn_sched_barrier(0);
-            }
+                (lds_void*)(sw + (pw * W_ROWS + q * 8) * 8), 16, 0, 0);
         }
     }
 };
 
-// One K chunk kc. First blend chunk kc+1 (its corner rows were queued a chunk
-// ago) into sa_n -- the wait for those loads also covers this wave's W tile
-// of chunk kc, queued right after them -- then queue W of chunk kc+1 into
-// sw_n and the corner rows of chunk kc+2, and only then run chunk kc on the
-// matrix cores while all of that is in flight. Each wave reads only the W
-// rows it loaded itself, so W needs no barrier; the barrier publishes sa_n
-// and frees sa. The LDS stages are restrict parameters so that the compiler
-// can tell the direct W loads apart from the other LDS accesses.
-__device__ __forceinline__ void pipe_step(Pipe& p, int kc, int nk2,
-                                          const uint4* __restrict__ sa,
-                                          const uint4* __restrict__ sw,
-                                          uint4* __restrict__ sa_n,
-                                          uint4* __restrict__ sw_n) {
+// One producer iteration: W of chunk kc+1, S of chunk kc+1 (its corner rows
+// were queued one chunk ago), corner rows of chunk kc+2, then this wave's W
+// loads must have landed before the barrier. The LDS stages are restrict
+// parameters so that the compiler can tell the direct W loads apart from
+// the S stores.
+__device__ __forceinline__ void produce(const Producer& p, int kc, int nk2, Gq& gq,
+                                        uint4* __restrict__ sa_n, uint4* __restrict__ sw_n) {
     if (kc + 1 < nk2) {
-        p.gather_commit(sa_n);
         p.w_issue(sw_n, kc + 1);
-        if (kc + 2 < nk2) p.gather_issue(kc + 2);
-    } else {
-        // s_waitcnt vmcnt(0) (expcnt, lgkmcnt at their maxima): this wave's W
-        // tile of the last chunk has landed
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+        p.commit(gq, sa_n);
+        if (kc + 2 < nk2) {
+            p.gather_issue(gq, kc + 2);
+            wait_vmcnt<G_ITEMS * 4>();               // the queued gather may stay in flight
+        } else {
+            wait_vmcnt<0>();
+        }
     }
-    p.mfma_chunk(sa, sw);
-    __syncthreads();
+    lds_barrier();
+}
+
+// Consumer: the chunk's 2 x 8 x 4 MFMAs. The other consumer wave on the SIMD
+// covers the LDS latency of the fragment reads.
+__device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TI], int lane, int cw,
+                                        const uint4* __restrict__ sa,
+                                        const uint4* __restrict__ sw) {
+    const int n = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s) {
+        const int v = s * 4 + g4;
+        bf16x8_t wf[FJ];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            wf[j] = __builtin_bit_cast(bf16x8_t, sw[slot(cw * WN + j * 16 + n, v)]);
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            const bf16x8_t sf = __builtin_bit_cast(bf16x8_t, sa[slot(i * 16 + n, v)]);
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], sf, acc[j][i], 0, 0, 0);
+        }
+    }
+    lds_barrier();
 }
 
 __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a, CamTable cams,
@@ -208,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const bool producer = wave >= N_CONS;
 
     const int32_t g = blockIdx.x;
     const int32_t tile = (g & 7) * per_xcd + (g >> 3);
@@ -215,75 +232,99 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
     const int32_t mt = tile / n_tiles, nt = tile - mt * n_tiles;
     const int64_t m0 = (int64_t)mt * BM;
     const int32_t n0 = nt * BN;
+    const int nk = (a.C + BK - 1) / BK;
+    const int nk2 = (nk + 1) & ~1;                    // even chunk count: two stages per round
+    uint4* out4 = reinterpret_cast<uint4*>(a.out);
+    const int dv = a.D >> 3;                          // 16-byte vectors per output row
 
-    // ---- project the tile's tokens; per token park (top-left row, the
-    // row steps to the right / lower corner, the two fractions) in sA1
-    int4* s_tok = reinterpret_cast<int4*>(sA1);                // [BM]
-    if (tid < BM) {
-        const int64_t t = m0 + tid;
-        int4 e = make_int4(0, 4, 0, 0);                         // padding token: weights 0
-        if (t < a.n) {
-            int32_t b, x, y, z;
-            token_cell(a.coords, t, a.R, b, x, y, z);
-            const Projected p = project_cell(b, x, y, z, a.R, cams, a.batch);
-            const SrcIdx sx = source_index(p.gx, a.W);
-            const SrcIdx sy = source_index(p.gy, a.H);
-            e.x = (p.b * a.H + sy.i0) * a.W + sx.i0;
-            e.y = (sx.i1 - sx.i0) | ((sy.i1 - sy.i0) << 1);     // 0/1 steps in x and y
-            e.z = __float_as_int(sx.t);
-            e.w = __float_as_int(sy.t);
-            if (a.mask && nt == 0) a.mask[t] = p.mask;
+    if (producer) {
+        const int ptid = tid - N_CONS * 64;
+        // ---- project the tile's tokens; per token park (top-left row, the
+        // row steps to the right / lower corner, the two fractions) in sA1
+        int4* s_tok = reinterpret_cast<int4*>(sA1);            // [BM]
+        if (ptid < BM) {
+            const int64_t t = m0 + ptid;
+            int4 e = make_int4(0, 4, 0, 0);                     // padding token: weights 0
+            if (t < a.n) {
+                int32_t b, x, y, z;
+                token_cell(a.coords, t, a.R, b, x, y, z);
+                const Projected pr = project_cell(b, x, y, z, a.R, cams, a.batch);
+                const SrcIdx sx = source_index(pr.gx, a.W);
+                const SrcIdx sy = source_index(pr.gy, a.H);
+                e.x = (pr.b * a.H + sy.i0) * a.W + sx.i0;
+                e.y = (sx.i1 - sx.i0) | ((sy.i1 - sy.i0) << 1);  // 0/1 steps in x and y
+                e.z = __float_as_int(sx.t);
+                e.w = __float_as_int(sy.t);
+                if (a.mask && nt == 0) a.mask[t] = pr.mask;
+            }
+            s_tok[ptid] = e;
         }
-        s_tok[tid] = e;
-    }
-    __syncthreads();
+        __syncthreads();                                          // (1) tokens parked
 
-    Pipe p;
-    p.feat = reinterpret_cast<const uint4*>(a.feat);
-    p.wgt = reinterpret_cast<const uint4*>(a.weight);
-    p.vpr = a.C >> 3;                                  // 16-byte vectors per row
-    p.D = a.D;
-    p.W = a.W;
-    p.n0 = n0;
-    p.tid = tid;
-    p.lane = lane;
-    p.wave = wave;
-    p.gv = tid & 7;
-    p.wrow0 = wave * WN + (lane >> 3);
-    p.wv_even = (lane & 7) ^ ((lane >> 4) & 7);
-    p.wv_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
+        Producer p;
+        p.feat = reinterpret_cast<const uint4*>(a.feat);
+        p.wgt = reinterpret_cast<const uint4*>(a.weight);
+        p.vpr = a.C >> 3;
+        p.D = a.D;
+        p.W = a.W;
+        p.n0 = n0;
+        p.ptid = ptid;
+        p.lane = lane;
+        p.pw = wave - N_CONS;
+        p.gv = ptid & 7;
 #pragma unroll
-    for (int u = 0; u < G_ITEMS; ++u) p.gt[u] = s_tok[(tid + u * kThreads) >> 3];
+        for (int u = 0; u < G_ITEMS; ++u) p.gt[u] = s_tok[(ptid + u * kProdThreads) >> 3];
+        Gq gq;
+        p.gather_issue(gq, 0);
+        __syncthreads();                                          // (2) sA1 free again
+        p.w_issue(sW0, 0);
+        p.commit(gq, sA0);
+        p.gather_issue(gq, 1);
+        wait_vmcnt<G_ITEMS * 4>();
+        lds_barrier();                                            // B_0
+        for (int kc = 0; kc < nk2; kc += 2) {
+            produce(p, kc, nk2, gq, sA1, sW1);
+            produce(p, kc + 1, nk2, gq, sA0, sW0);
+        }
+        __syncthreads();                                          // consumers staged
+
+        // ---- null blocks of this workgroup: q = mt, mt + m_tiles, ...
+        const uint4* bias4 = reinterpret_cast<const uint4*>(a.bias);
+        for (int32_t q = mt; q < null_tiles; q += m_tiles) {
+            for (int idx = ptid; idx < NULL_VEC; idx += kProdThreads) {
+                const int r = idx >> 6, cv = idx & 63;         // 64 vectors per 512-wide row
+                const int64_t row = a.n + (int64_t)q * BM + r;
+                const int colv = (n0 >> 3) + cv;
+                if (row < a.n + a.n_null && colv < dv) {
+                    const uint4 val = bias4 ? bias4[colv] : make_uint4(0, 0, 0, 0);
+                    store_nt16(out4 + row * dv + colv, val);
+                }
+            }
+        }
+        return;
+    }
+
+    // ---------------------------------------------------------- consumers
+    const int cw = wave;
+    f32x4_t acc[FJ][TI];
 #pragma unroll
     for (int j = 0; j < FJ; ++j)
 #pragma unroll
-        for (int i = 0; i < TI; ++i) p.acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();                                   // sA1 is free again
-
-    // ---- K loop, two chunks per iteration so every LDS stage is named
-    // statically; an odd chunk count is padded with one all-zero chunk
-    // (gather and W loads are clamped and the gathered values zeroed).
-    const int nk = (a.C + BK - 1) / BK;
-    const int nk2 = (nk + 1) & ~1;
-    p.gather_issue(0);
-    p.gather_commit(sA0);
-    p.w_issue(sW0, 0);
-    p.gather_issue(1);
-    __syncthreads();
+        for (int i = 0; i < TI; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();                                              // (1)
+    __syncthreads();                                              // (2)
+    lds_barrier();                                                // B_0
     for (int kc = 0; kc < nk2; kc += 2) {
-        pipe_step(p, kc, nk2, sA0, sW0, sA1, sW1);
-        pipe_step(p, kc + 1, nk2, sA1, sW1, sA0, sW0);
+        consume(acc, lane, cw, sA0, sW0);
+        consume(acc, lane, cw, sA1, sW1);
     }
 
-    // ---- epilogue: + bias, round to bf16, stage each wave's 128 x 128 tile
-    // in the free W stages (token-major, 256-byte rows), 16-byte row stores.
-    // Lane l of block (j, i) holds features 4*(l/16) + r of token l % 16.
-    uint4* out4 = reinterpret_cast<uint4*>(a.out);
-    const int dv = a.D >> 3;                           // 16-byte vectors per output row
-    const int fbase = n0 + wave * WN;
-    constexpr int WAVES_PER_STAGE = NWAVES / 2;
-    uint4* stage4 = (wave < WAVES_PER_STAGE ? sW0 : sW1) +
-                    (wave % WAVES_PER_STAGE) * (BM * WN / 8);
+    // ---- epilogue: + bias, round to bf16, stage the 128 x 64 tile in the
+    // free W stages (token-major 128-byte rows, same slot swizzle), 16-byte
+    // row stores. Lane l of block (j, i) holds features 4*(l/16) + r of
+    // token l % 16.
+    const int fbase = n0 + cw * WN;
+    uint4* stage4 = (cw < N_CONS / 2 ? sW0 : sW1) + (cw % (N_CONS / 2)) * (BM * 8);
     uint2* stage2 = reinterpret_cast<uint2*>(stage4);
     const uint16_t* bias16 = reinterpret_cast<const uint16_t*>(a.bias);
 #pragma unroll
@@ -299,32 +340,19 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
             const int t = i * 16 + (lane & 15);
             const int f = j * 16 + 4 * (lane >> 4);
             uint2 pk;
-            pk.x = pack_bf16x2(p.acc[j][i][0] + bv[0], p.acc[j][i][1] + bv[1]);
-            pk.y = pack_bf16x2(p.acc[j][i][2] + bv[2], p.acc[j][i][3] + bv[3]);
-            stage2[(t * WN + f) >> 2] = pk;
+            pk.x = pack_bf16x2(acc[j][i][0] + bv[0], acc[j][i][1] + bv[1]);
+            pk.y = pack_bf16x2(acc[j][i][2] + bv[2], acc[j][i][3] + bv[3]);
+            stage2[slot(t, f >> 3) * 2 + ((f >> 2) & 1)] = pk;
         }
     }
-    __syncthreads();
+    __syncthreads();                                              // consumers staged
 #pragma unroll
-    for (int q = lane; q < BM * WN / 8; q += 64) {
-        const int t = q / (WN / 8), cv = q % (WN / 8);
+    for (int r = 0; r < BM * 8 / 64; ++r) {
+        const int q = r * 64 + lane;
+        const int t = q >> 3, cv = q & 7;
         const int64_t tok = m0 + t;
         const int colv = (fbase >> 3) + cv;
-        if (tok < a.n && colv < dv) out4[tok * dv + colv] = stage4[q];
-    }
-
-    // ---- null blocks of this workgroup: q = mt, mt + m_tiles, ...
-    const uint4* bias4 = reinterpret_cast<const uint4*>(a.bias);
-    for (int32_t q = mt; q < null_tiles; q += m_tiles) {
-        for (int idx = tid; idx < NULL_VEC; idx += kThreads) {
-            const int r = idx >> 6, cv = idx & 63;     // 64 vectors per 512-wide row
-            const int64_t row = a.n + (int64_t)q * BM + r;
-            const int colv = (n0 >> 3) + cv;
-            if (row < a.n + a.n_null && colv < dv) {
-                const uint4 val = bias4 ? bias4[colv] : make_uint4(0, 0, 0, 0);
-                store_nt16(out4 + row * dv + colv, val);
-            }
-        }
+        if (tok < a.n && colv < dv) out4[tok * dv + colv] = stage4[slot(t, cv)];
     }
 }
 

@@ -10,12 +10,13 @@ proj_linear 2048->1536); inputs are synthetic, seeded and resident in HBM
 before the timed region starts.
 
 Prints ONE JSON line. Fields beyond the common ones:
-  roofline       dominant kernel (the fused gather+MFMA kernel): algorithmic
-                 flops per launch / its mean duration (HIP events on the launch
-                 stream, measured in this run) against the bf16 dense MFMA peak;
-                 traffic = HBM bytes per launch from the committed rocprofv3
-                 FETCH_SIZE/WRITE_SIZE runs, scaled by a copy kernel of known
-                 size, or null if the kernel source changed since.
+  roofline       dominant kernel (the fused gather+MFMA kernel, which a bf16
+                 step launches once, null rows included): algorithmic flops
+                 per launch / its mean duration (HIP events on the launch
+                 stream around the timed steps) against the bf16 dense MFMA
+                 peak; traffic = HBM bytes per launch from the committed
+                 rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled by a copy kernel
+                 of known size, or null if the kernel source changed since.
   cpu_baseline   the CPU oracle on a bounded prefix of the same tokens.
   gather         the standalone bilinear gather on the same points: algorithmic
                  bytes / duration against peak HBM bandwidth.
@@ -51,10 +52,10 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload):
-    """HBM bytes per launch of the fused kernel from profiles/, if the sources
-    still match the digest recorded there."""
-    path = os.path.join(PROFILE_DIR, "proj_cond_%s_hbm_traffic.md" % workload)
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/, if the
+    sources still match the digest recorded there."""
+    path = os.path.join(PROFILE_DIR, "%s_%s_hbm_traffic.md" % (kernel, workload))
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -88,11 +89,15 @@ def unique_corner_rows(pixel, bidx, H, W):
     return int(np.unique(rows).size)
 
 
-def time_events(fn, reps, stream):
-    """Mean duration (ms) of fn() over reps launches, HIP events on stream."""
+def time_events(fn, reps, stream, lead=None):
+    """Mean duration (ms) of fn() over reps launches, HIP events on stream.
+    lead(), enqueued first and not timed, keeps the GPU busy while the host
+    queues launches that are shorter than their own host-side call."""
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    if lead is not None:
+        lead()
     e0.record(stream)
     for _ in range(reps):
         fn()
@@ -203,32 +208,7 @@ def main():
         p3d.p3d_proj_cond(coords_d, n, w.resolution, camarr, feat, weight, out, bias=bias,
                           n_null=n_null, mask=mask)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # ---- dominant kernel alone (same launch configuration, no null rows)
-    out_tokens, out_null = out[:n], out[n:]
-
-    def fused_only():
-        p3d.p3d_proj_cond(coords_d, n, w.resolution, camarr, feat, weight, out_tokens,
-                          bias=bias, n_null=0, mask=mask)
-
-    def null_only():
-        p3d.p3d_proj_cond(None, 0, w.resolution, camarr, feat, weight, out_null, bias=bias,
-                          n_null=n_null)
-
-    reps = max(args.steps, 5)
-    fused_ms = time_events(fused_only, reps, stream)
-    null_ms = time_events(null_only, reps, stream) if n_null else 0.0
-
-    # ---- the standalone gather on the same points
+    # ---- side measurements first; the standalone gather on the same points
     grid = torch.empty((n, 2), device="cuda")
     pixel = torch.empty((n, 2), dtype=torch.int32, device="cuda")
     p3d.p3d_project_points(coords_d, n, w.resolution, camarr, w.height, w.width, grid=grid,
@@ -241,20 +221,62 @@ def main():
     def gather_only():
         p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx)
 
-    gather_only()
+    reps = max(args.steps, 20)
+    for _ in range(reps):
+        gather_only()
     gather_ms = time_events(gather_only, reps, stream)
+
+    # the null-branch fill alone (its own kernel when there are no tokens)
+    out_null = out[n:]
+
+    def null_only():
+        p3d.p3d_proj_cond(None, 0, w.resolution, camarr, feat, weight, out_null, bias=bias,
+                          n_null=n_null)
+
+    def lead():
+        for _ in range(4):
+            step()
+
+    null_ms = time_events(null_only, reps, stream, lead) if n_null else 0.0
     torch.cuda.synchronize()
+
+    # ---- the timed steps. An idle GPU takes tens of milliseconds of work to
+    # reach its working clocks, so untimed steps run for a fixed 0.3 s before
+    # the W warmup steps.
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < 0.3:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # the step is one launch of the fused kernel (bf16), so the events around
+    # the timed steps give its mean launch duration
+    fused_ms = e0.elapsed_time(e1) / args.steps
+
     U = unique_corner_rows(pixel.cpu().numpy(), bidx_np, w.height, w.width)
     s = 2 if bf16 else 4
     C, D = w.channels, w.out_dim
     flops = 2.0 * n * C * D
     fused_bytes = 16 * n + U * C * s + D * C * s + (D * s if bias is not None else 0) \
-        + n * D * s + n
+        + n * D * s + n + n_null * D * s
     gather_bytes = 8 * n + 4 * n + U * C * s + n * C * s
     null_bytes = n_null * D * s
     peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
     achieved = flops / (fused_ms * 1e-3) / 1e12
-    traffic = recorded_traffic(w.name)
+    kname = "proj_cond_bf16_kernel" if bf16 else "proj_cond_kernel"
+    traffic = recorded_traffic(kname, w.name)
 
     line = {
         "metric": "projected tokens/sec (project+sample+proj_linear); HBM GB/s & MFMA % of peak",
@@ -277,13 +299,14 @@ def main():
         "rows_per_sec_incl_null": (n + n_null) / (ms_per_step * 1e-3),
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "proj_cond_kernel", "mean_ms": fused_ms,
+                     "kernel": kname, "mean_ms": fused_ms,
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": fused_bytes},
         "gather": {"bound": "hbm", "achieved": gather_bytes / (gather_ms * 1e-3) / 1e9,
                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
                    "frac": gather_bytes / (gather_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                    "kernel": "sample_kernel", "mean_ms": gather_ms,
+                   "traffic": recorded_traffic("sample_kernel", w.name),
                    "algorithmic_bytes_per_launch": gather_bytes},
         "null_fill": {"bound": "hbm", "mean_ms": null_ms,
                       "achieved": null_bytes / (null_ms * 1e-3) / 1e9 if null_ms else None,

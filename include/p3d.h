@@ -194,10 +194,10 @@ p3d_status p3d_bilinear_sample(const void* feat, p3d_dtype feat_dtype,
  *                           width is checked against the map's channels; a
  *                           mismatch is P3D_ERR_SHAPE naming both shapes)
  *   bias [out_dim] device, or NULL
- *   out_dim                 D >= 1; D % 8 == 0 (BF16) or D % 4 == 0 (F32)
+ *   out_dim                 1 <= D <= 2^20; D % 8 == 0 (BF16) or D % 4 == 0 (F32)
  *   n_null                  >= 0 null rows appended after the n token rows
  *   out [(n + n_null), D] device; mask [n] uint8 device or NULL
- *   Alignment: feat, weight and out 16-byte aligned.
+ *   Alignment: feat, weight, bias and out 16-byte aligned.
  * --------------------------------------------------------------------- */
 p3d_status p3d_proj_cond(const int32_t* coords, int64_t n, int32_t resolution,
                          const p3d_camera* cams, int32_t batch,

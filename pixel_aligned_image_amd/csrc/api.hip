@@ -18,6 +18,7 @@ namespace {
 thread_local std::string g_err;
 
 constexpr int64_t kMaxTokens = int64_t(1) << 30;   // keeps tile counts in int32
+constexpr int32_t kMaxOutDim = 1 << 20;            // keeps a tile's offsets in int32
 
 p3d_status fail(p3d_status s, const char* fmt, ...) {
     char buf[512];
@@ -220,6 +221,9 @@ p3d_status p3d_proj_cond(const int32_t* coords, int64_t n, int32_t resolution,
     if (channels < 1 || out_dim < 1)
         return fail(P3D_ERR_INVALID_ARG, "%s: channels and out_dim must be >= 1, got %d, %d", fn,
                     channels, out_dim);
+    if (out_dim > kMaxOutDim)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: out_dim must be <= %d, got %d", fn, kMaxOutDim,
+                    out_dim);
     if (weight_in != channels)
         return fail(P3D_ERR_SHAPE,
                     "%s: proj_linear weight is [%d, %d] but the feature map [%d, %d, %d, %d] has "

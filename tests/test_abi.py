@@ -116,6 +116,7 @@ def _pc(p3d, **kw):
     (dict(out=FAKE + 8), 4, "16-byte aligned"),
     (dict(H=65536, W=65536), 4, "2^31"),
     (dict(n=(1 << 30) + 1), 4, "n must be <="),
+    (dict(D=(1 << 20) + 8), 4, "out_dim must be <="),
 ], ids=lambda v: str(v)[:40])
 def test_proj_cond_validation(p3d, kw, status, needle):
     st, msg = _pc(p3d, **kw)

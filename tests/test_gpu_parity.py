@@ -264,6 +264,9 @@ SMALL = [
          n_null=17),
     dict(name="bf16_outside_frame", bf16=True, R=16, B=1, n=400, H=16, W=16, C=64, D=256,
          bias=True, n_null=0, fov=70.0, dist=0.8, spill=4),
+    # null rows far beyond the token rows, ragged, 25 vectors per row
+    dict(name="bf16_null_heavy", bf16=True, R=16, B=1, n=130, H=8, W=8, C=64, D=200,
+         bias=True, n_null=700),
 ]
 
 

@@ -56,6 +56,11 @@ def _declare(lib):
     lib.orc_project.restype = None
     lib.orc_project.argtypes = [_i32p, _i64, _i32, _f32p, _f32p, _i32, _i32, _i32,
                                 _f32p, _i32p, _f32p, _f32p, _u8p]
+    lib.orc_project_ex.restype = None
+    lib.orc_project_ex.argtypes = [_i32p, _i64, _i32, _i32, _f32p, _f32p, _i32, _i32, _i32,
+                                   _f32p, _i32p, _f32p, _f32p, _u8p]
+    lib.orc_requantize.restype = None
+    lib.orc_requantize.argtypes = [_i32p, _i64, _i32, _i32, _i32, _i32p]
     lib.orc_sample.restype = None
     lib.orc_sample.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _f32p, _i32p, _i64, _f64p]
     lib.orc_linear.restype = None
@@ -64,7 +69,16 @@ def _declare(lib):
     lib.orc_proj_cond_rows.argtypes = [_i32p, _i64, _i32, _f32p, _f32p, _vp, _i32, _i32,
                                        _i32, _i32, _i32, _vp, _vp, _i32, _i64,
                                        _i64p, _i64, _f64p, _u8p, _f64p]
+    lib.orc_proj_cond_rows_ex.restype = None
+    lib.orc_proj_cond_rows_ex.argtypes = [_i32p, _i64, _i32, _i32, _f32p, _f32p, _i32, _i32,
+                                          ctypes.POINTER(_vp), _i32p, _i32p, _i32p, _i32,
+                                          _vp, _vp, _i32, _i64, _i64p, _i64, _f64p, _u8p,
+                                          _f64p]
     return lib
+
+
+POINTS = {"cell_centres": 0, "grid_nodes": 1}
+REQUANT = {"round_nodes": 0, "floor_cells": 1}
 
 
 class Oracle:
@@ -131,9 +145,11 @@ class Oracle:
                                   ctypes.byref(i1), ctypes.byref(t))
         return i0.value, i1.value, np.float32(t.value)
 
-    def project(self, coords, n, resolution, focal, dist, height, width):
+    def project(self, coords, n, resolution, focal, dist, height, width,
+                points="cell_centres"):
         """dict grid[n,2] f32, pixel[n,2] i32, frac[n,2] f32, depth[n] f32,
-        mask[n] u8. coords None = dense grid (n = B*R^3)."""
+        mask[n] u8. coords None = dense grid (n = B*R^3). points:
+        "cell_centres" or "grid_nodes"."""
         focal = np.ascontiguousarray(focal, dtype=np.float32).reshape(-1)
         dist = np.ascontiguousarray(dist, dtype=np.float32).reshape(-1)
         assert focal.shape == dist.shape
@@ -143,11 +159,21 @@ class Oracle:
         out = dict(grid=np.empty((n, 2), np.float32), pixel=np.empty((n, 2), np.int32),
                    frac=np.empty((n, 2), np.float32), depth=np.empty(n, np.float32),
                    mask=np.empty(n, np.uint8))
-        self.lib.orc_project(_ptr(coords, _i32p), n, resolution, _ptr(focal, _f32p),
-                             _ptr(dist, _f32p), len(focal), height, width,
-                             _ptr(out["grid"], _f32p), _ptr(out["pixel"], _i32p),
-                             _ptr(out["frac"], _f32p), _ptr(out["depth"], _f32p),
-                             _ptr(out["mask"], _u8p))
+        self.lib.orc_project_ex(_ptr(coords, _i32p), n, resolution, POINTS[points],
+                                _ptr(focal, _f32p), _ptr(dist, _f32p), len(focal), height,
+                                width, _ptr(out["grid"], _f32p), _ptr(out["pixel"], _i32p),
+                                _ptr(out["frac"], _f32p), _ptr(out["depth"], _f32p),
+                                _ptr(out["mask"], _u8p))
+        return out
+
+    def requantize(self, coords, src_res, grid, mode="round_nodes"):
+        """(b, x, y, z) on a src_res grid -> (b, X, Y, Z) on `grid`:
+        "round_nodes" = round(u (grid-1)), "floor_cells" = floor(u grid),
+        u = (c + 1/2)/src_res; exact."""
+        coords = np.ascontiguousarray(coords, dtype=np.int32).reshape(-1, 4)
+        out = np.empty_like(coords)
+        self.lib.orc_requantize(_ptr(coords, _i32p), len(coords), int(src_res), int(grid),
+                                REQUANT[mode], _ptr(out, _i32p))
         return out
 
     # ---------------------------------------------------------- sampling ---
@@ -186,19 +212,27 @@ class Oracle:
 
     # -------------------------------------------------------- whole path ---
     def proj_cond_rows(self, coords, n, resolution, focal, dist, feat, weight, bias,
-                       n_null, rows):
+                       n_null, rows, points="cell_centres"):
         """Rows `rows` (indices into [0, n + n_null)) of the whole path:
-        float64 [len(rows), D] before rounding to the output type, and mask."""
-        feat = np.ascontiguousarray(feat)
+        float64 [len(rows), D] before rounding to the output type, and mask.
+        feat is one map or a list of maps (same batch, own H, W, C) whose
+        samples are concatenated; weight is [D, sum of C]."""
+        feats = [np.ascontiguousarray(f) for f in (feat if isinstance(feat, (list, tuple))
+                                                    else [feat])]
         weight = np.ascontiguousarray(weight)
-        is_bf16 = feat.dtype == np.uint16
-        assert weight.dtype == feat.dtype
-        B, H, W, C = feat.shape
+        is_bf16 = feats[0].dtype == np.uint16
+        assert all(f.dtype == feats[0].dtype for f in feats) and weight.dtype == feats[0].dtype
+        B = feats[0].shape[0]
+        assert all(f.shape[0] == B for f in feats)
+        Hs = np.array([f.shape[1] for f in feats], np.int32)
+        Ws = np.array([f.shape[2] for f in feats], np.int32)
+        Cs = np.array([f.shape[3] for f in feats], np.int32)
+        C = int(Cs.sum())
         D = weight.shape[0]
         assert weight.shape == (D, C)
         if bias is not None:
             bias = np.ascontiguousarray(bias)
-            assert bias.dtype == feat.dtype and bias.shape == (D,)
+            assert bias.dtype == feats[0].dtype and bias.shape == (D,)
         if coords is not None:
             coords = np.ascontiguousarray(coords, dtype=np.int32)
             assert coords.shape == (n, 4)
@@ -210,11 +244,13 @@ class Oracle:
         Y = np.empty((rows.size, D), np.float64)
         mask = np.empty(rows.size, np.uint8)
         S = np.empty((rows.size, C), np.float64)
-        self.lib.orc_proj_cond_rows(_ptr(coords, _i32p), n, resolution, _ptr(focal, _f32p),
-                                    _ptr(dist, _f32p), _vptr(feat), int(is_bf16), B, H, W,
-                                    C, _vptr(weight), _vptr(bias), D, n_null,
-                                    _ptr(rows, _i64p), rows.size, _ptr(Y, _f64p),
-                                    _ptr(mask, _u8p), _ptr(S, _f64p))
+        fp = (_vp * len(feats))(*[f.ctypes.data for f in feats])
+        self.lib.orc_proj_cond_rows_ex(_ptr(coords, _i32p), n, resolution, POINTS[points],
+                                       _ptr(focal, _f32p), _ptr(dist, _f32p), B, len(feats),
+                                       fp, _ptr(Hs, _i32p), _ptr(Ws, _i32p), _ptr(Cs, _i32p),
+                                       int(is_bf16), _vptr(weight), _vptr(bias), D, n_null,
+                                       _ptr(rows, _i64p), rows.size, _ptr(Y, _f64p),
+                                       _ptr(mask, _u8p), _ptr(S, _f64p))
         return Y, mask
 
 

@@ -18,6 +18,15 @@
  *               camera distance at 49.13 deg on a 512 px frame).
  *   [PR38-flow] same PR, commit introducing FlowCond / proj_linear (null proj
  *               zeroed on the device).
+ *   [PR38-quant] same PR, commit on the cascade requantization: the
+ *               projection grid is the endpoint-inclusive linspace(-1, 1,
+ *               grid), and Pixal3D maps a high-resolution coordinate to the
+ *               NEAREST node, round(u * (grid - 1)), where TRELLIS.2 takes
+ *               floor(u * grid).
+ *   [PR38-naf]  same PR, commit adding the NAF upsampler: the shape and
+ *               texture stages sample two maps (the DINOv3 map and its
+ *               NAF-upsampled version) and feed the concatenation, hence
+ *               proj_in_channels = 2048.
  *
  * Precision. Whatever decides an integer (pixel index, in-image mask) is
  * computed in binary32 with one IEEE rounding per operation, in the order
@@ -27,6 +36,13 @@
  *
  * Readings taken where the pages are silent:
  *   - token point = cell centre (c + 1/2)/R - 1/2 per axis, world extent +-1/2;
+ *     in grid-node mode the point is node c of linspace(-1, 1, R) scaled to
+ *     the same extent: c/(R - 1) - 1/2;
+ *   - requantization: u = (c + 1/2)/R_src (the source cell centre in [0, 1]);
+ *     "round" is to the nearest integer, ties to even, and is evaluated
+ *     exactly in integers (no ties occur at the pages' sizes);
+ *   - two maps: the sample is map 0's channels followed by map 1's, each map
+ *     sampled at the same normalised point on its own height and width;
  *   - camera at (0, 0, +d) looking down -Z: depth = d - z;
  *   - FOV is the full angle: focal = 1/tan(fov/2) in normalised image units;
  *   - image y grows downwards: gy = -(f*y)/depth;
@@ -148,6 +164,50 @@ static float cell_centre(int32_t c, int32_t R)
     return ((float)c + 0.5f) / (float)R - 0.5f;
 }
 
+/* [PR38-quant]: node c of the endpoint-inclusive grid linspace(-1, 1, R), in
+ * world units (half of the normalised value): c/(R-1) - 1/2. R >= 2. */
+static float grid_node(int32_t c, int32_t R)
+{
+    return (float)c / (float)(R - 1) - 0.5f;
+}
+
+/* The world coordinate of integer position c on a grid of R: the cell centre
+ * (points == 0) or the grid node (points == 1). */
+static float token_point(int32_t c, int32_t R, int32_t points)
+{
+    return points ? grid_node(c, R) : cell_centre(c, R);
+}
+
+/* ---------------------------------------------------- requantization ---
+ * [PR38-quant]: a coordinate c on the source grid of R_src cells has the
+ * normalised position u = (c + 1/2)/R_src. Mode 0 (Pixal3D) maps it to the
+ * nearest node of a grid of G nodes, round(u (G - 1)); mode 1 (TRELLIS.2)
+ * to the cell floor(u G). Both are ratios of integers:
+ *   u (G - 1) = (2c + 1)(G - 1) / (2 R_src),   u G = (2c + 1) G / (2 R_src),
+ * so they are evaluated exactly. Coordinates are clamped to [0, R_src - 1]
+ * first; the batch column is copied. */
+static int32_t requant_axis(int32_t c, int32_t src_res, int32_t grid, int32_t mode)
+{
+    if (c < 0) c = 0;
+    if (c > src_res - 1) c = src_res - 1;
+    int64_t den = 2 * (int64_t)src_res;
+    if (mode == 1) return (int32_t)(((2 * (int64_t)c + 1) * grid) / den);
+    int64_t num = (2 * (int64_t)c + 1) * (int64_t)(grid - 1);
+    int64_t q = num / den, rem = num - q * den;
+    if (2 * rem > den || (2 * rem == den && (q & 1))) q += 1;
+    return (int32_t)q;
+}
+
+void orc_requantize(const int32_t* src, int64_t n, int32_t src_res, int32_t grid,
+                    int32_t mode, int32_t* dst)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        dst[4 * i] = src[4 * i];
+        for (int k = 1; k < 4; ++k)
+            dst[4 * i + k] = requant_axis(src[4 * i + k], src_res, grid, mode);
+    }
+}
+
 /* grid_sample, align_corners=False, padding_mode='border' ([MLX-head]): a
  * normalised coordinate g maps to the source index ((g+1)*size - 1)/2, the
  * SOURCE INDEX is clamped to [0, size-1], and only then are the two
@@ -185,8 +245,8 @@ static void token_cell(const int32_t* coords, int64_t n, int32_t R, int32_t cell
 
 /* One token: normalised image coordinates, depth, mask, corner indices and
  * fractions. cams: focal[b], dist[b]. */
-static void project_one(const int32_t cell[4], int32_t R, const float* focal,
-                        const float* dist, int32_t batch, int32_t H, int32_t W,
+static void project_one(const int32_t cell[4], int32_t R, int32_t points,
+                        const float* focal, const float* dist, int32_t batch,
                         float* gx_out, float* gy_out, float* depth_out,
                         uint8_t* mask_out, int32_t* bsel)
 {
@@ -194,16 +254,15 @@ static void project_one(const int32_t cell[4], int32_t R, const float* focal,
     int valid = (b >= 0 && b < batch);
     if (b < 0) b = 0;
     if (b >= batch) b = batch - 1;
-    float px = cell_centre(cell[1], R);
-    float py = cell_centre(cell[2], R);
-    float pz = cell_centre(cell[3], R);
+    float px = token_point(cell[1], R, points);
+    float py = token_point(cell[2], R, points);
+    float pz = token_point(cell[3], R, points);
     float f = focal[b];
     float depth = dist[b] - pz;                 /* camera at +d, looks down -Z */
     float gx = (f * px) / depth;
     float gy = -((f * py) / depth);             /* image rows grow downwards */
     uint8_t m = (uint8_t)(valid && depth > 0.0f && gx >= -1.0f && gx <= 1.0f &&
                           gy >= -1.0f && gy <= 1.0f);
-    (void)H; (void)W;
     *gx_out = gx;
     *gy_out = gy;
     *depth_out = depth;
@@ -214,11 +273,11 @@ static void project_one(const int32_t cell[4], int32_t R, const float* focal,
 /* Project tokens [0, n). Any output pointer may be NULL.
  *   grid  [n,2] (gx, gy)      pixel [n,2] (x0, y0) after the border clamp
  *   frac  [n,2] (tx, ty)      depth [n]             mask [n] (0/1)       */
-void orc_project(const int32_t* coords, int64_t n, int32_t R,
-                 const float* focal, const float* dist, int32_t batch,
-                 int32_t H, int32_t W,
-                 float* grid, int32_t* pixel, float* frac, float* depth,
-                 uint8_t* mask)
+void orc_project_ex(const int32_t* coords, int64_t n, int32_t R, int32_t points,
+                    const float* focal, const float* dist, int32_t batch,
+                    int32_t H, int32_t W,
+                    float* grid, int32_t* pixel, float* frac, float* depth,
+                    uint8_t* mask)
 {
     for (int64_t i = 0; i < n; ++i) {
         int32_t cell[4];
@@ -226,7 +285,7 @@ void orc_project(const int32_t* coords, int64_t n, int32_t R,
         float gx, gy, d;
         uint8_t m;
         int32_t b;
-        project_one(cell, R, focal, dist, batch, H, W, &gx, &gy, &d, &m, &b);
+        project_one(cell, R, points, focal, dist, batch, &gx, &gy, &d, &m, &b);
         int32_t x0, x1, y0, y1;
         float tx, ty;
         source_index(gx, W, &x0, &x1, &tx);
@@ -237,6 +296,16 @@ void orc_project(const int32_t* coords, int64_t n, int32_t R,
         if (depth) depth[i] = d;
         if (mask) mask[i] = m;
     }
+}
+
+/* Cell-centre projection (the default point mode). */
+void orc_project(const int32_t* coords, int64_t n, int32_t R,
+                 const float* focal, const float* dist, int32_t batch,
+                 int32_t H, int32_t W,
+                 float* grid, int32_t* pixel, float* frac, float* depth,
+                 uint8_t* mask)
+{
+    orc_project_ex(coords, n, R, 0, focal, dist, batch, H, W, grid, pixel, frac, depth, mask);
 }
 
 /* ------------------------------------------------------ bilinear sample ---
@@ -318,20 +387,24 @@ void orc_linear(const double* S, int64_t n, int32_t C, const void* weight,
 /* ---------------------------------------------------------- whole path ---
  * Projection conditioning for a chosen subset of output rows.
  * rows[k] in [0, n + n_null): rows below n are tokens (project -> sample ->
- * [bf16 rounding of the sample when the map is bf16, as a bf16 grid_sample
+ * [bf16 rounding of the sample when the maps are bf16, as a bf16 grid_sample
  * feeding a bf16 Linear would do] -> proj_linear); rows at or above n are the
  * CFG null branch, whose proj input is zero ([PR38-flow]), i.e. the bias.
- * Y [nrows, D] binary64 (not yet rounded to the output type), mask [nrows]
- * (null rows: 0). Every step is the single-token function above. */
-void orc_proj_cond_rows(const int32_t* coords, int64_t n, int32_t R,
-                        const float* focal, const float* dist,
-                        const void* feat, int32_t is_bf16, int32_t batch,
-                        int32_t H, int32_t W, int32_t C, const void* weight,
-                        const void* bias, int32_t D, int64_t n_null,
-                        const int64_t* rows, int64_t nrows,
-                        double* Y, uint8_t* mask, double* S_scratch)
+ * The sample is the concatenation over the n_maps maps ([PR38-naf]): map m
+ * is feats[m], [batch, Hs[m], Ws[m], Cs[m]], and the weight is
+ * [D, sum of Cs]. Y [nrows, D] binary64 (not yet rounded to the output
+ * type), mask [nrows] (null rows: 0). S_scratch holds nrows * sum(Cs). */
+void orc_proj_cond_rows_ex(const int32_t* coords, int64_t n, int32_t R, int32_t points,
+                           const float* focal, const float* dist, int32_t batch,
+                           int32_t n_maps, const void* const* feats, const int32_t* Hs,
+                           const int32_t* Ws, const int32_t* Cs, int32_t is_bf16,
+                           const void* weight, const void* bias, int32_t D, int64_t n_null,
+                           const int64_t* rows, int64_t nrows,
+                           double* Y, uint8_t* mask, double* S_scratch)
 {
     (void)n_null;
+    int32_t C = 0;
+    for (int32_t m = 0; m < n_maps; ++m) C += Cs[m];
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t k = 0; k < nrows; ++k) {
         int64_t r = rows[k];
@@ -344,11 +417,15 @@ void orc_proj_cond_rows(const int32_t* coords, int64_t n, int32_t R,
         int32_t cell[4];
         token_cell(coords, r, R, cell);
         float gx, gy, dep;
-        uint8_t m;
+        uint8_t msk;
         int32_t b;
-        project_one(cell, R, focal, dist, batch, H, W, &gx, &gy, &dep, &m, &b);
+        project_one(cell, R, points, focal, dist, batch, &gx, &gy, &dep, &msk, &b);
         double* s = S_scratch + k * (int64_t)C;
-        sample_one(feat, is_bf16, b, H, W, C, gx, gy, s);
+        int32_t off = 0;
+        for (int32_t m = 0; m < n_maps; ++m) {
+            sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, s + off);
+            off += Cs[m];
+        }
         if (is_bf16)
             for (int32_t c = 0; c < C; ++c) s[c] = (double)orc_bf16_to_f32(orc_f64_to_bf16(s[c]));
         for (int32_t d = 0; d < D; ++d) {
@@ -358,6 +435,20 @@ void orc_proj_cond_rows(const int32_t* coords, int64_t n, int32_t R,
             if (bias) acc += param_at(bias, is_bf16, d);
             y[d] = acc;
         }
-        if (mask) mask[k] = m;
+        if (mask) mask[k] = msk;
     }
+}
+
+/* One map, cell centres. */
+void orc_proj_cond_rows(const int32_t* coords, int64_t n, int32_t R,
+                        const float* focal, const float* dist,
+                        const void* feat, int32_t is_bf16, int32_t batch,
+                        int32_t H, int32_t W, int32_t C, const void* weight,
+                        const void* bias, int32_t D, int64_t n_null,
+                        const int64_t* rows, int64_t nrows,
+                        double* Y, uint8_t* mask, double* S_scratch)
+{
+    const void* feats[1] = {feat};
+    orc_proj_cond_rows_ex(coords, n, R, 0, focal, dist, batch, 1, feats, &H, &W, &C, is_bf16,
+                          weight, bias, D, n_null, rows, nrows, Y, mask, S_scratch);
 }

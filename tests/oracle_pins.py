@@ -18,7 +18,11 @@ Sources, by page title and section:
   trellis.cpp PR #38 "Initial support for Pixal3D": commit adding pixal3d.cpp
     (closed-form camera solve), commit exposing extend_pixel (worked example),
     commit adding projection diagnostics (cube corners legitimately leave the
-    frame), commit introducing FlowCond (null proj zeroed).
+    frame), commit introducing FlowCond (null proj zeroed), commit on the
+    cascade requantization (endpoint-inclusive projection grid, nearest-node
+    rounding; a quarter of the coordinates per axis and 58 % of tokens move
+    under flooring at grid 64, in stripes of period 8), commit adding the NAF
+    upsampler (two maps concatenated into 2048 proj channels).
 """
 import math
 import os
@@ -401,6 +405,157 @@ def pin_whole_path_composition(o):
         assert np.all(mask[n:] == 0)
         Y0, _ = o.proj_cond_rows(None, n, R, [f], [d], feat, Wq, None, n_null, [n, n + 2])
         assert np.all(Y0 == 0.0)
+
+
+# ---------------------------------------------------- grid nodes, cascade ---
+def pin_requant_pages_fractions(o):
+    """Res-512 coordinates requantized to a grid of 64: flooring u*64 and
+    rounding u*63 disagree on exactly a quarter of the coordinates of each
+    axis, always by one full cell, in stripes of period 8 (res-512 units);
+    over the cube that is 1 - (3/4)^3 = 57.8 % of tokens off on at least one
+    axis (the pages' 58 %)."""
+    c = np.arange(512, dtype=np.int32)
+    toks = np.stack([np.zeros_like(c), c, c, c], 1)
+    r = o.requantize(toks, 512, 64, "round_nodes")[:, 1]
+    f = o.requantize(toks, 512, 64, "floor_cells")[:, 1]
+    d = r != f
+    assert d.sum() == 128, d.sum()
+    assert set(np.abs(r - f).tolist()) == {0, 1}
+    # stripes of period 8: within each aligned block of 8 coordinates (one
+    # grid-64 cell) the disagreements form one contiguous run, whose width
+    # shrinks from 4 at the faces to 0 at the centre (mirror symmetric)
+    for blk in d.reshape(-1, 8):
+        idx = np.nonzero(blk)[0]
+        assert idx.size == 0 or idx[-1] - idx[0] + 1 == idx.size, blk
+    assert np.array_equal(d, d[::-1])
+    assert d[:8].sum() == 4 and d[252:260].sum() == 0
+    assert r.min() == 0 and r.max() == 63 and f.min() == 0 and f.max() == 63
+    assert np.all(np.diff(r) >= 0) and np.all(np.diff(f) >= 0)
+    # every token of the 512^3 cube: the per-axis disagreement is independent
+    keep = 1.0 - d.mean()
+    assert abs((1.0 - keep ** 3) - 0.578125) < 1e-12
+    rng = np.random.default_rng(67)
+    t = np.concatenate([np.zeros((200000, 1), np.int32),
+                        rng.integers(0, 512, (200000, 3)).astype(np.int32)], 1)
+    moved = np.any(o.requantize(t, 512, 64, "round_nodes")[:, 1:] !=
+                   o.requantize(t, 512, 64, "floor_cells")[:, 1:], axis=1).mean()
+    assert abs(moved - 0.578125) < 0.005, moved
+
+
+def pin_requant_identity(o):
+    """A grid requantized to its own size is unchanged in both modes."""
+    for R in (1, 2, 3, 7, 64, 100, 512):
+        c = np.arange(R, dtype=np.int32)
+        toks = np.stack([np.full_like(c, 3), c, c[::-1], c], 1)
+        for mode in ("round_nodes", "floor_cells"):
+            if R == 1 and mode == "round_nodes":
+                continue
+            assert np.array_equal(o.requantize(toks, R, R, mode), toks), (R, mode)
+
+
+def pin_requant_brute_force(o):
+    """Against exact rationals: round half to even of (c+1/2)(G-1)/R and
+    floor of (c+1/2)G/R, for every coordinate of small grids."""
+    from fractions import Fraction
+    for R in range(1, 41):
+        c = np.arange(R, dtype=np.int32)
+        toks = np.stack([np.zeros_like(c), c, c, c], 1)
+        for G in range(2, 41):
+            r = o.requantize(toks, R, G, "round_nodes")[:, 1]
+            f = o.requantize(toks, R, G, "floor_cells")[:, 1]
+            for ci in range(R):
+                u = Fraction(2 * ci + 1, 2 * R)
+                assert r[ci] == round(u * (G - 1)), (R, G, ci)
+                assert f[ci] == math.floor(u * G), (R, G, ci)
+
+
+def pin_grid_node_endpoints(o):
+    """Node i of linspace(-1, 1, R) at half scale: the end nodes sit exactly on
+    the cube faces (+-1/2), the middle node of an odd grid on the axis, so
+    on-axis nodes land on the image centre exactly."""
+    for R in (2, 3, 5, 64, 65, 1025):
+        cells = np.array([[0, 0, R - 1, 0], [0, R - 1, 0, R - 1]], np.int32)
+        f, d = 2.0, 3.0
+        p = o.project(cells, 2, R, [f], [d], 8, 8, points="grid_nodes")
+        # z = -1/2 and +1/2 exactly: depth = d -+ 1/2
+        assert p["depth"].tolist() == [np.float32(d + 0.5), np.float32(d - 0.5)]
+        want = np.float32(f) * np.float32(0.5) / np.array([d + 0.5, d - 0.5], np.float32)
+        assert p["grid"][0, 0] == -want[0] and p["grid"][1, 0] == want[1]
+        if R % 2:
+            m = (R - 1) // 2
+            q = o.project(np.array([[0, m, m, 0]], np.int32), 1, R, [f], [d], 8, 8,
+                          points="grid_nodes")
+            assert np.all(q["grid"] == 0.0) and q["pixel"].tolist() == [[3, 3]]
+
+
+def pin_grid_node_registration(o):
+    """The camera solve registers the grid so that its z = 0 corner nodes
+    land on the frame border: |g| = 1 up to binary32 rounding of focal and
+    distance (cell centres only approach it, as 1 - 1/R)."""
+    R = 65
+    m = (R - 1) // 2
+    cells = np.array([[0, R - 1, R - 1, m], [0, 0, 0, m], [0, R - 1, 0, m]], np.int32)
+    for fov in (30.0, 40.0, 49.13):
+        f, d = o.camera(fov, o.distance_from_fov(fov, 512, 0))
+        p = o.project(cells, 3, R, [f], [d], 64, 64, points="grid_nodes")
+        assert np.max(np.abs(np.abs(p["grid"]) - 1.0)) < 4e-7, (fov, p["grid"])
+
+
+# ---------------------------------------------------------------- two maps ---
+def _affine_map(B, H, W, a, b, g):
+    """map[y][x][c] = a_c * xn + b_c * yn + g_c at pixel centres in normalised
+    coordinates (xn = (2x+1)/W - 1), binary32."""
+    xn = ((2 * np.arange(W) + 1) / W - 1).astype(np.float64)
+    yn = ((2 * np.arange(H) + 1) / H - 1).astype(np.float64)
+    m = a[None, None, :] * xn[None, :, None] + b[None, None, :] * yn[:, None, None] + g
+    return np.ascontiguousarray(np.broadcast_to(m, (B, H, W, len(a))).astype(np.float32))
+
+
+def pin_two_map_affine_maps(o):
+    """Bilinear interpolation reproduces an affine function of the normalised
+    coordinates on any grid, so two affine maps of different sizes sampled at
+    one point give each its own a*g + b*gy + c, concatenated map 0 first;
+    with an identity proj_linear that is the output."""
+    rng = np.random.default_rng(23)
+    C0, C1 = 8, 12
+    a0, b0, g0 = rng.standard_normal((3, C0))
+    a1, b1, g1 = rng.standard_normal((3, C1))
+    m0 = _affine_map(1, 16, 24, a0, b0, g0)
+    m1 = _affine_map(1, 40, 32, a1, b1, g1)
+    Wt = np.eye(C0 + C1, dtype=np.float32)
+    R = 16
+    coords = np.array([[0, x, y, z] for x, y, z in rng.integers(3, R - 3, (40, 3))], np.int32)
+    f, d = o.camera(30.0, 2.5)
+    for points in ("cell_centres", "grid_nodes"):
+        Y, _ = o.proj_cond_rows(coords, len(coords), R, [f], [d], [m0, m1], Wt, None, 0,
+                                np.arange(len(coords)), points=points)
+        p = o.project(coords, len(coords), R, [f], [d], 16, 16, points=points)
+        gx = p["grid"][:, :1].astype(np.float64)
+        gy = p["grid"][:, 1:].astype(np.float64)
+        assert np.all(np.abs(p["grid"]) < 0.9)       # away from every border clamp
+        want = np.concatenate([a0 * gx + b0 * gy + g0, a1 * gx + b1 * gy + g1], 1)
+        assert _rel(Y, want, np.abs(want).max()) < 2e-6, points
+
+
+def pin_two_map_linearity(o):
+    """proj_linear over the concatenated sample splits over the halves:
+    Y([m0, m1]; [W0 | W1], b) = Y(m0; W0, b) + Y(m1; W1, no bias)."""
+    rng = np.random.default_rng(29)
+    m0 = rng.standard_normal((2, 9, 7, 8)).astype(np.float32)
+    m1 = rng.standard_normal((2, 5, 11, 16)).astype(np.float32)
+    W0 = rng.standard_normal((20, 8)).astype(np.float32)
+    W1 = rng.standard_normal((20, 16)).astype(np.float32)
+    bias = rng.standard_normal(20).astype(np.float32)
+    coords = np.concatenate([rng.integers(0, 2, (50, 1)), rng.integers(0, 12, (50, 3))],
+                            1).astype(np.int32)
+    fo, do = o.cameras([35.0, 45.0], [None, 1.8])
+    rows = np.arange(50)
+    Y, mask = o.proj_cond_rows(coords, 50, 12, fo, do, [m0, m1], np.concatenate([W0, W1], 1),
+                               bias, 0, rows)
+    Ya, ma = o.proj_cond_rows(coords, 50, 12, fo, do, m0, W0, bias, 0, rows)
+    Yb, mb = o.proj_cond_rows(coords, 50, 12, fo, do, m1, W1, None, 0, rows)
+    assert np.array_equal(mask, ma) and np.array_equal(mask, mb)
+    assert _rel(Y, Ya + Yb, np.abs(Y).max()) < 1e-12
 
 
 ALL_PINS = {name[len("pin_"):]: fn for name, fn in sorted(globals().items())

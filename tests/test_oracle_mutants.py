@@ -52,6 +52,27 @@ MUTANTS = [
     ("bf16_ties_away", "if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))",
      "if (dropped >= 0x8000u)"),
     ("dense_order_zyx", "cell[3] = (int32_t)(n % r);", "cell[3] = (int32_t)((n / (r * r)) % r); cell[1] = (int32_t)(n % r); if (0)"),
+    ("node_spacing_over_R", "return (float)c / (float)(R - 1) - 0.5f;",
+     "return (float)c / (float)R - 0.5f;"),
+    ("node_full_linspace_extent", "return (float)c / (float)(R - 1) - 0.5f;",
+     "return 2.0f * (float)c / (float)(R - 1) - 1.0f;"),
+    ("node_mode_ignored", "return points ? grid_node(c, R) : cell_centre(c, R);",
+     "return cell_centre(c, R);"),
+    ("requant_round_floors", "if (2 * rem > den || (2 * rem == den && (q & 1))) q += 1;",
+     "if (0) q += 1;"),
+    ("requant_ties_up", "if (2 * rem > den || (2 * rem == den && (q & 1))) q += 1;",
+     "if (2 * rem >= den) q += 1;"),
+    ("requant_no_half_cell", "int64_t num = (2 * (int64_t)c + 1) * (int64_t)(grid - 1);",
+     "int64_t num = (2 * (int64_t)c) * (int64_t)(grid - 1);"),
+    ("requant_floor_over_grid_minus_1",
+     "if (mode == 1) return (int32_t)(((2 * (int64_t)c + 1) * grid) / den);",
+     "if (mode == 1) return (int32_t)(((2 * (int64_t)c + 1) * (grid - 1)) / den);"),
+    ("two_maps_share_first_size",
+     "sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, s + off);",
+     "sample_one(feats[m], is_bf16, b, Hs[0], Ws[0], Cs[m], gx, gy, s + off);"),
+    ("two_maps_order_reversed",
+     "sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, s + off);",
+     "sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, s + (C - off - Cs[m]));"),
 ]
 
 RUNNER = r"""
@@ -79,7 +100,8 @@ def _build(tmp_path, name, old, new):
     from oracle import build as obuild
     obuild.build(src=str(path), out=str(lib), extra=["-Wno-unused-variable",
                                                      "-Wno-unused-but-set-variable",
-                                                     "-Wno-unused-parameter"])
+                                                     "-Wno-unused-parameter",
+                                                     "-Wno-unused-function"])
     return str(lib)
 
 

@@ -26,7 +26,14 @@
  *       a mismatch fails with a message;
  *     commit checking widths in lin() -- errors name the tensor and both
  *       shapes;
- *     commit adding per-request camera fields -- every image has its own FOV.
+ *     commit adding per-request camera fields -- every image has its own FOV;
+ *     commit on the cascade requantization -- the projection grid is the
+ *       endpoint-inclusive linspace(-1, 1, grid), and a high-resolution token
+ *       maps to the nearest node, round(u * (grid - 1)), where TRELLIS.2
+ *       floors u * grid;
+ *     commit adding the NAF upsampler -- the shape and texture stages sample
+ *       the DINOv3 map and its NAF-upsampled version (another size) at the
+ *       same points and concatenate them, hence proj_in_channels = 2048.
  *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers owned by the caller. The library
@@ -206,6 +213,87 @@ p3d_status p3d_proj_cond(const int32_t* coords, int64_t n, int32_t resolution,
                          const void* weight, int32_t out_dim, int32_t weight_in,
                          const void* bias, int64_t n_null,
                          void* out, uint8_t* mask, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Point modes and cascade requantization (PR #38, cascade requantization
+ * commit; pixel-aligned head commit: ProjGrid).
+ *
+ * P3D_POINTS_CELL_CENTRES: integer position c on a grid of R is the cell
+ *   centre (c + 1/2)/R - 1/2 (binary32, in that order); the default of
+ *   p3d_project_points and p3d_proj_cond.
+ * P3D_POINTS_GRID_NODES: c is node c of the endpoint-inclusive projection
+ *   grid linspace(-1, 1, R) at half scale: c/(R - 1) - 1/2 (binary32, in
+ *   that order); R >= 2. The end nodes lie on the faces of the unit cube.
+ * --------------------------------------------------------------------- */
+typedef enum p3d_points {
+    P3D_POINTS_CELL_CENTRES = 0,
+    P3D_POINTS_GRID_NODES = 1
+} p3d_points;
+
+typedef enum p3d_requant {
+    P3D_REQUANT_ROUND_NODES = 0,  /* Pixal3D: nearest node, round(u (G - 1)) */
+    P3D_REQUANT_FLOOR_CELLS = 1   /* TRELLIS.2: cell floor(u G) */
+} p3d_requant;
+
+/* p3d_requantize_coords -- map sparse coords of a source grid of
+ * src_resolution cells onto a grid of `grid` positions (the cascade step
+ * from the upsampled res-512 coords to the high-resolution token grid).
+ *
+ * For each token (b, x, y, z) and each axis, u = (c + 1/2)/src_resolution
+ * (the source cell centre in [0, 1]); the output position is
+ *   P3D_REQUANT_ROUND_NODES: round(u (grid - 1)), nearest integer, ties to
+ *     even -- the node whose projection-grid point is nearest, which keeps
+ *     the pixel-aligned sample registered (use P3D_POINTS_GRID_NODES next);
+ *   P3D_REQUANT_FLOOR_CELLS: floor(u grid) -- the cell containing u.
+ * Both are evaluated exactly in integer arithmetic (no rounding error).
+ * Coordinates outside [0, src_resolution) are clamped into it first; the
+ * batch column is copied unchanged.
+ *
+ *   src [n,4] int32 device, 16-byte aligned; dst [n,4] int32 device,
+ *   16-byte aligned (may equal src); 1 <= src_resolution, 1 <= grid, both
+ *   <= 2^20; grid >= 2 for P3D_REQUANT_ROUND_NODES.
+ * --------------------------------------------------------------------- */
+p3d_status p3d_requantize_coords(const int32_t* src, int64_t n, int32_t src_resolution,
+                                 int32_t grid, p3d_requant mode, int32_t* dst, void* stream);
+
+/* p3d_project_points_ex -- p3d_project_points with a point mode. */
+p3d_status p3d_project_points_ex(const int32_t* coords, int64_t n, int32_t resolution,
+                                 p3d_points points, const p3d_camera* cams, int32_t batch,
+                                 int32_t height, int32_t width,
+                                 float* grid, int32_t* pixel, float* frac,
+                                 float* depth, uint8_t* mask, void* stream);
+
+/* One channels-last feature map [batch, height, width, channels] on the
+ * device (the batch count is the call's). */
+typedef struct p3d_map {
+    const void* feat;
+    int32_t height;
+    int32_t width;
+    int32_t channels;
+} p3d_map;
+
+/* p3d_proj_cond_ex -- p3d_proj_cond with a point mode and one or two maps.
+ *
+ * With two maps (the NAF commit's 2048 proj channels: the DINOv3 map and its
+ * upsampled version) every token is projected once; the normalised point is
+ * sampled on each map at that map's own height and width, and the sample is
+ * map 0's channels followed by map 1's:
+ *   S[n] = [ sample(maps[0], g_n) , sample(maps[1], g_n) ]     (C0 + C1)
+ *   Y[n] = W S[n] + bias,   W [out_dim, C0 + C1].
+ * Everything else is as p3d_proj_cond (null rows, mask, rounding).
+ *
+ *   maps    host array [n_maps] of p3d_map, 1 <= n_maps <= 2; every map has
+ *           `dtype`, the call's batch count, batch*height*width < 2^31 and
+ *           channels % 8 == 0 (BF16) or % 4 == 0 (F32); with two maps,
+ *           maps[0].channels % 64 == 0
+ *   weight_in must equal the summed channels (P3D_ERR_SHAPE otherwise)
+ * --------------------------------------------------------------------- */
+p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution,
+                            p3d_points points, const p3d_camera* cams, int32_t batch,
+                            p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                            const void* weight, int32_t out_dim, int32_t weight_in,
+                            const void* bias, int64_t n_null,
+                            void* out, uint8_t* mask, void* stream);
 
 #ifdef __cplusplus
 }

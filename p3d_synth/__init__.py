@@ -26,8 +26,8 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "workload", "shell_coords", "feature_map",
-           "weight", "bias", "fovs", "bf16_bits", "bits_to_f32"]
+__all__ = ["Workload", "WORKLOADS", "EXTRA_WORKLOADS", "workload", "shell_coords",
+           "feature_map", "feature_maps", "weight", "bias", "fovs", "bf16_bits", "bits_to_f32"]
 
 
 @dataclass(frozen=True)
@@ -49,6 +49,13 @@ class Workload:
     distance: Optional[float]     # None = closed-form distance for the FOV
     null_rows: bool               # CFG null branch of the same size as the tokens
     seeds: dict = field(default_factory=dict)
+    # second map (height, width, channels), concatenated after the first;
+    # `channels` is then map 0's and the weight is [out_dim, channels + C1]
+    map1: Optional[Tuple[int, int, int]] = None
+    points: str = "cell_centres"  # or "grid_nodes"
+    # cascade: coords are drawn on a grid of this resolution and must be
+    # requantized onto `resolution` nodes before projection
+    coords_resolution: Optional[int] = None
 
     @property
     def n_tokens(self):
@@ -59,6 +66,10 @@ class Workload:
     @property
     def n_null(self):
         return self.n_tokens if self.null_rows else 0
+
+    @property
+    def k_total(self):
+        return self.channels + (self.map1[2] if self.map1 else 0)
 
 
 WORKLOADS = [
@@ -79,11 +90,28 @@ WORKLOADS = [
              dict(coords=500, map=501, weight=502)),
 ]
 
+# Workloads of the adjacent parts:
+#  - the cascade: a res-512 shell's coords requantized onto the 64-node
+#    high-resolution projection grid (64 cells of 16 res-1024 voxels), then
+#    projected as grid nodes; one 2048-channel map as in the texture stage;
+#  - two maps: the texture stage's tokens sampled on the DINOv3 map of a
+#    1024-pixel image (64 x 64 patches, 1024 channels) and on its upsampled
+#    version (512 x 512, 1024 channels), concatenated into 2048 proj channels.
+EXTRA_WORKLOADS = [
+    Workload("cascade512_grid64_nodes_bf16_c2048_d1536", 64, 1, False, 100000, 512, 512, 2048,
+             1536, "bf16", ("normal", 0.0, 1.0), "none", ("fixed", 40.0, 0.0), None, False,
+             dict(coords=600, map=601, weight=602), points="grid_nodes",
+             coords_resolution=512),
+    Workload("shell1024_cfg_twomap_bf16_c1024x2_d1536", 1024, 1, False, 100000, 64, 64, 1024,
+             1536, "bf16", ("normal", 0.0, 1.0), "none", ("fixed", 40.0, 0.0), None, True,
+             dict(coords=500, map=701, map1=702, weight=703), map1=(512, 512, 1024)),
+]
+
 
 def workload(name_or_index):
     if isinstance(name_or_index, int):
         return WORKLOADS[name_or_index]
-    for w in WORKLOADS:
+    for w in WORKLOADS + EXTRA_WORKLOADS:
         if w.name == name_or_index:
             return w
     raise KeyError(name_or_index)
@@ -138,10 +166,12 @@ def shell_coords(resolution, batch, per_item, seed):
 
 
 def coords(w: Workload):
-    """Token coords for a workload (None for the dense grid)."""
+    """Token coords for a workload (None for the dense grid). For a cascade
+    workload these are on the coords_resolution grid (before requantization)."""
     if w.dense:
         return None
-    return shell_coords(w.resolution, w.batch, w.tokens_per_item, w.seeds["coords"])
+    return shell_coords(w.coords_resolution or w.resolution, w.batch, w.tokens_per_item,
+                        w.seeds["coords"])
 
 
 # ------------------------------------------------------------------ tensors
@@ -155,9 +185,15 @@ def _draw(rng, dist, shape):
     raise ValueError(kind)
 
 
-def feature_map(w: Workload, rows_per_chunk=64):
-    """Channels-last [B, H, W, C] map: float32, or uint16 bf16 bits."""
-    B, H, W, C = w.batch, w.height, w.width, w.channels
+def feature_map(w: Workload, rows_per_chunk=64, which=0):
+    """Channels-last [B, H, W, C] map (map `which` of the workload): float32,
+    or uint16 bf16 bits."""
+    if which == 0:
+        B, H, W, C = w.batch, w.height, w.width, w.channels
+        seed = w.seeds["map"]
+    else:
+        (H, W, C), B = w.map1, w.batch
+        seed = w.seeds["map1"]
     dt = np.uint16 if w.dtype == "bf16" else np.float32
     out = np.empty((B, H, W, C), dt)
 
@@ -165,7 +201,7 @@ def feature_map(w: Workload, rows_per_chunk=64):
         b, ci = job
         y0 = ci * rows_per_chunk
         y1 = min(H, y0 + rows_per_chunk)
-        rng = np.random.default_rng([w.seeds["map"], b, ci])
+        rng = np.random.default_rng([seed, b, ci])
         x = _draw(rng, w.map_dist, (y1 - y0, W, C))
         out[b, y0:y1] = bf16_bits(x) if w.dtype == "bf16" else x
 
@@ -175,10 +211,16 @@ def feature_map(w: Workload, rows_per_chunk=64):
     return out
 
 
+def feature_maps(w: Workload):
+    """The workload's maps as a list (one or two)."""
+    return [feature_map(w)] + ([feature_map(w, which=1)] if w.map1 else [])
+
+
 def weight(w: Workload):
-    """proj_linear weight [D, C] ~ N(0, 0.02): float32 or bf16 bits."""
+    """proj_linear weight [D, K] ~ N(0, 0.02) (K = summed map channels):
+    float32 or bf16 bits."""
     rng = np.random.default_rng([w.seeds["weight"]])
-    x = _draw(rng, ("normal", 0.0, 0.02), (w.out_dim, w.channels))
+    x = _draw(rng, ("normal", 0.0, 0.02), (w.out_dim, w.k_total))
     return bf16_bits(x) if w.dtype == "bf16" else x
 
 

@@ -18,18 +18,25 @@ import torch
 
 __all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_version",
            "p3d_status_string", "p3d_last_error", "p3d_distance_from_fov", "p3d_make_camera",
-           "p3d_project_points", "p3d_bilinear_sample", "p3d_proj_cond", "make_cameras",
-           "LIB_PATH"]
+           "p3d_project_points", "p3d_bilinear_sample", "p3d_proj_cond",
+           "p3d_requantize_coords", "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libp3d.so")
 
 P3D_OK, P3D_ERR_INVALID_ARG, P3D_ERR_SHAPE, P3D_ERR_DTYPE, P3D_ERR_UNSUPPORTED, P3D_ERR_HIP = range(6)
 P3D_F32, P3D_BF16 = 0, 1
 P3D_MAX_BATCH = 256
+POINTS = {"cell_centres": 0, "grid_nodes": 1}          # p3d_points
+REQUANT = {"round_nodes": 0, "floor_cells": 1}          # p3d_requant
 
 
 class p3d_camera(ctypes.Structure):
     _fields_ = [("focal", ctypes.c_float), ("distance", ctypes.c_float)]
+
+
+class p3d_map(ctypes.Structure):
+    _fields_ = [("feat", ctypes.c_void_p), ("height", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("channels", ctypes.c_int32)]
 
 
 class P3DError(RuntimeError):
@@ -66,6 +73,15 @@ def _load():
     L.p3d_proj_cond.restype = ctypes.c_int
     L.p3d_proj_cond.argtypes = [vp, i64, i32, cam_p, i32, vp, ctypes.c_int, i32, i32, i32,
                                 vp, i32, i32, vp, i64, vp, vp, vp]
+    L.p3d_project_points_ex.restype = ctypes.c_int
+    L.p3d_project_points_ex.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, i32, i32, vp,
+                                        vp, vp, vp, vp, vp]
+    L.p3d_requantize_coords.restype = ctypes.c_int
+    L.p3d_requantize_coords.argtypes = [vp, i64, i32, i32, ctypes.c_int, vp, vp]
+    L.p3d_proj_cond_ex.restype = ctypes.c_int
+    L.p3d_proj_cond_ex.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
+                                   ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp, vp,
+                                   vp]
     return L
 
 
@@ -151,18 +167,34 @@ def _cams(cams):
 
 # -------------------------------------------------------------- entry points ---
 def p3d_project_points(coords, n, resolution, cams, height, width, grid=None, pixel=None,
-                       frac=None, depth=None, mask=None, stream=None):
-    """Enqueue p3d_project_points. coords: int32 [n, 4] device tensor or None
-    (dense grid); cams: sequence of (focal, distance) per batch item; outputs
-    are preallocated device tensors or None."""
+                       frac=None, depth=None, mask=None, stream=None, points="cell_centres"):
+    """Enqueue p3d_project_points (points="cell_centres") or
+    p3d_project_points_ex. coords: int32 [n, 4] device tensor or None (dense
+    grid); cams: sequence of (focal, distance) per batch item; outputs are
+    preallocated device tensors or None; points: "cell_centres" or
+    "grid_nodes"."""
     camarr, batch = _cams(cams)
     n = int(n)
-    _check(lib.p3d_project_points(
-        _dev(coords, "coords", torch.int32, (n, 4)), n, int(resolution), camarr, batch,
-        int(height), int(width),
-        _dev(grid, "grid", torch.float32, (n, 2)), _dev(pixel, "pixel", torch.int32, (n, 2)),
-        _dev(frac, "frac", torch.float32, (n, 2)), _dev(depth, "depth", torch.float32, (n,)),
-        _dev(mask, "mask", torch.uint8, (n,)), _stream(stream)))
+    args = (_dev(grid, "grid", torch.float32, (n, 2)), _dev(pixel, "pixel", torch.int32, (n, 2)),
+            _dev(frac, "frac", torch.float32, (n, 2)), _dev(depth, "depth", torch.float32, (n,)),
+            _dev(mask, "mask", torch.uint8, (n,)), _stream(stream))
+    c = _dev(coords, "coords", torch.int32, (n, 4))
+    if points == "cell_centres":
+        _check(lib.p3d_project_points(c, n, int(resolution), camarr, batch, int(height),
+                                      int(width), *args))
+    else:
+        _check(lib.p3d_project_points_ex(c, n, int(resolution), POINTS[points], camarr, batch,
+                                         int(height), int(width), *args))
+
+
+def p3d_requantize_coords(src, src_resolution, grid, dst, mode="round_nodes", stream=None):
+    """Enqueue p3d_requantize_coords: int32 [n, 4] (b, x, y, z) on a
+    src_resolution grid -> dst int32 [n, 4] on `grid`; mode "round_nodes"
+    (round(u (grid-1))) or "floor_cells" (floor(u grid))."""
+    n = int(src.shape[0])
+    _check(lib.p3d_requantize_coords(_dev(src, "src", torch.int32, (n, 4)), n,
+                                     int(src_resolution), int(grid), REQUANT[mode],
+                                     _dev(dst, "dst", torch.int32, (n, 4)), _stream(stream)))
 
 
 def p3d_bilinear_sample(feat, grid, out, batch_index=None, stream=None):
@@ -184,27 +216,43 @@ def p3d_bilinear_sample(feat, grid, out, batch_index=None, stream=None):
 
 
 def p3d_proj_cond(coords, n, resolution, cams, feat, weight, out, bias=None, n_null=0,
-                  mask=None, stream=None):
-    """Enqueue p3d_proj_cond. feat: [B, H, W, C]; weight: [D, C_w] (torch
-    Linear layout; C_w is checked against C by the library); bias: [D] or
-    None; out: [n + n_null, D]; all of one dtype (float32 or bfloat16);
-    mask: uint8 [n] or None."""
+                  mask=None, stream=None, points="cell_centres"):
+    """Enqueue p3d_proj_cond (one map, cell centres) or p3d_proj_cond_ex.
+    feat: [B, H, W, C], or a list of two such maps (own H, W, C; samples
+    concatenated, map 0 first); weight: [D, C_w] (torch Linear layout; C_w is
+    checked against the summed C by the library); bias: [D] or None; out:
+    [n + n_null, D]; all of one dtype (float32 or bfloat16); mask: uint8 [n]
+    or None; points: "cell_centres" or "grid_nodes"."""
     camarr, batch = _cams(cams)
-    if feat.dim() != 4:
-        raise ValueError("feat must be [B, H, W, C], got %s" % (tuple(feat.shape),))
+    feats = list(feat) if isinstance(feat, (list, tuple)) else [feat]
+    for f in feats:
+        if f.dim() != 4:
+            raise ValueError("feat must be [B, H, W, C], got %s" % (tuple(f.shape),))
+        if f.shape[0] != batch:
+            raise ValueError("feat has %d batch items but %d cameras were given"
+                             % (f.shape[0], batch))
+        if f.dtype != feats[0].dtype:
+            raise TypeError("all maps must have one dtype")
     if weight.dim() != 2:
         raise ValueError("weight must be [out_dim, in_dim], got %s" % (tuple(weight.shape),))
-    B, H, W, C = feat.shape
-    if B != batch:
-        raise ValueError("feat has %d batch items but %d cameras were given" % (B, batch))
     D, Cw = weight.shape
-    dt = _DT.get(feat.dtype)
+    dt = _DT.get(feats[0].dtype)
     if dt is None:
-        raise TypeError("feat must be float32 or bfloat16, got %s" % feat.dtype)
+        raise TypeError("feat must be float32 or bfloat16, got %s" % feats[0].dtype)
     n, n_null = int(n), int(n_null)
-    _check(lib.p3d_proj_cond(
-        _dev(coords, "coords", torch.int32, (n, 4)), n, int(resolution), camarr, batch,
-        _dev(feat, "feat"), dt, H, W, C, _dev(weight, "weight", feat.dtype), D, Cw,
-        _dev(bias, "bias", feat.dtype, (D,)), n_null,
-        _dev(out, "out", feat.dtype, (n + n_null, D)), _dev(mask, "mask", torch.uint8, (n,)),
-        _stream(stream)))
+    dtype = feats[0].dtype
+    common = (_dev(weight, "weight", dtype), D, Cw, _dev(bias, "bias", dtype, (D,)), n_null,
+              _dev(out, "out", dtype, (n + n_null, D)), _dev(mask, "mask", torch.uint8, (n,)),
+              _stream(stream))
+    c = _dev(coords, "coords", torch.int32, (n, 4))
+    if len(feats) == 1 and points == "cell_centres":
+        B, H, W, C = feats[0].shape
+        _check(lib.p3d_proj_cond(c, n, int(resolution), camarr, batch, _dev(feats[0], "feat"), dt,
+                                 H, W, C, *common))
+        return
+    maps = (p3d_map * len(feats))()
+    for i, f in enumerate(feats):
+        maps[i].feat = _dev(f, "feat[%d]" % i)
+        maps[i].height, maps[i].width, maps[i].channels = f.shape[1], f.shape[2], f.shape[3]
+    _check(lib.p3d_proj_cond_ex(c, n, int(resolution), POINTS[points], camarr, batch, dt, maps,
+                                len(feats), *common))

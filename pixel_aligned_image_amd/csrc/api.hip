@@ -19,6 +19,7 @@ thread_local std::string g_err;
 
 constexpr int64_t kMaxTokens = int64_t(1) << 30;   // keeps tile counts in int32
 constexpr int32_t kMaxOutDim = 1 << 20;            // keeps a tile's offsets in int32
+constexpr int32_t kMaxGrid = 1 << 20;              // requantization grids
 
 p3d_status fail(p3d_status s, const char* fmt, ...) {
     char buf[512];
@@ -45,25 +46,38 @@ p3d_status hip_fail(const char* what, hipError_t e) {
     return fail(P3D_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
 }
 
+// Size of one feature map of the call's batch.
+p3d_status check_map_size(const char* fn, const char* what, int32_t batch, int32_t H,
+                          int32_t W) {
+    if (H < 1 || W < 1)
+        return fail(P3D_ERR_INVALID_ARG, "%s: %s height/width must be >= 1, got %dx%d", fn, what,
+                    H, W);
+    if ((int64_t)batch * H * W > INT32_MAX)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: %s batch*height*width must be < 2^31 (row indices are int32), got %lld",
+                    fn, what, (long long)((int64_t)batch * H * W));
+    return P3D_OK;
+}
+
 // Shared checks of the token / camera arguments.
 p3d_status check_tokens(const char* fn, const int32_t* coords, int64_t n, int32_t R,
-                        const p3d_camera* cams, int32_t batch, int32_t H, int32_t W,
+                        p3d_points points, const p3d_camera* cams, int32_t batch,
                         CamTable* tab) {
     if (n < 0) return fail(P3D_ERR_INVALID_ARG, "%s: n must be >= 0, got %lld", fn, (long long)n);
     if (n > kMaxTokens)
         return fail(P3D_ERR_UNSUPPORTED, "%s: n must be <= %lld, got %lld", fn,
                     (long long)kMaxTokens, (long long)n);
     if (R < 1) return fail(P3D_ERR_INVALID_ARG, "%s: resolution must be >= 1, got %d", fn, R);
+    if (points != P3D_POINTS_CELL_CENTRES && points != P3D_POINTS_GRID_NODES)
+        return fail(P3D_ERR_INVALID_ARG, "%s: points must be CELL_CENTRES or GRID_NODES, got %d",
+                    fn, (int)points);
+    if (points == P3D_POINTS_GRID_NODES && R < 2)
+        return fail(P3D_ERR_INVALID_ARG,
+                    "%s: grid-node points need resolution >= 2 (linspace end points), got %d",
+                    fn, R);
     if (batch < 1 || batch > P3D_MAX_BATCH)
         return fail(P3D_ERR_INVALID_ARG, "%s: batch must be in [1, %d], got %d", fn,
                     P3D_MAX_BATCH, batch);
-    if (H < 1 || W < 1)
-        return fail(P3D_ERR_INVALID_ARG, "%s: feature map height/width must be >= 1, got %dx%d",
-                    fn, H, W);
-    if ((int64_t)batch * H * W > INT32_MAX)
-        return fail(P3D_ERR_UNSUPPORTED,
-                    "%s: batch*height*width must be < 2^31 (row indices are int32), got %lld",
-                    fn, (long long)((int64_t)batch * H * W));
     if (!coords) {
         const int64_t r3 = (int64_t)R * R * R;
         if (n > 0 && (R > 1290 || r3 * batch != n))   // 1290^3 * 256 still fits int64
@@ -145,19 +159,58 @@ p3d_status p3d_make_camera(double fov_deg, double distance, p3d_camera* out) {
     return ok();
 }
 
-p3d_status p3d_project_points(const int32_t* coords, int64_t n, int32_t resolution,
-                              const p3d_camera* cams, int32_t batch, int32_t height,
-                              int32_t width, float* grid, int32_t* pixel, float* frac,
-                              float* depth, uint8_t* mask, void* stream) {
+p3d_status p3d_project_points_ex(const int32_t* coords, int64_t n, int32_t resolution,
+                                 p3d_points points, const p3d_camera* cams, int32_t batch,
+                                 int32_t height, int32_t width, float* grid, int32_t* pixel,
+                                 float* frac, float* depth, uint8_t* mask, void* stream) {
     const char* fn = "p3d_project_points";
     CamTable tab;
-    p3d_status st = check_tokens(fn, coords, n, resolution, cams, batch, height, width, &tab);
+    p3d_status st = check_tokens(fn, coords, n, resolution, points, cams, batch, &tab);
+    if (st != P3D_OK) return st;
+    st = check_map_size(fn, "feature map", batch, height, width);
     if (st != P3D_OK) return st;
     if (!aligned(grid, 8) || !aligned(pixel, 8) || !aligned(frac, 8))
         return fail(P3D_ERR_UNSUPPORTED, "%s: grid, pixel and frac must be 8-byte aligned", fn);
     if (n == 0) return ok();
-    ProjectArgs a{coords, n, resolution, batch, height, width, grid, pixel, frac, depth, mask};
+    ProjectArgs a{coords, n,     resolution, (int32_t)points, batch, height, width,
+                  grid,   pixel, frac,       depth,           mask};
     hipError_t e = launch_project(a, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+p3d_status p3d_project_points(const int32_t* coords, int64_t n, int32_t resolution,
+                              const p3d_camera* cams, int32_t batch, int32_t height,
+                              int32_t width, float* grid, int32_t* pixel, float* frac,
+                              float* depth, uint8_t* mask, void* stream) {
+    return p3d_project_points_ex(coords, n, resolution, P3D_POINTS_CELL_CENTRES, cams, batch,
+                                 height, width, grid, pixel, frac, depth, mask, stream);
+}
+
+p3d_status p3d_requantize_coords(const int32_t* src, int64_t n, int32_t src_resolution,
+                                 int32_t grid, p3d_requant mode, int32_t* dst, void* stream) {
+    const char* fn = "p3d_requantize_coords";
+    if (n < 0) return fail(P3D_ERR_INVALID_ARG, "%s: n must be >= 0, got %lld", fn, (long long)n);
+    if (n > kMaxTokens)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: n must be <= %lld, got %lld", fn,
+                    (long long)kMaxTokens, (long long)n);
+    if (mode != P3D_REQUANT_ROUND_NODES && mode != P3D_REQUANT_FLOOR_CELLS)
+        return fail(P3D_ERR_INVALID_ARG, "%s: mode must be ROUND_NODES or FLOOR_CELLS, got %d",
+                    fn, (int)mode);
+    if (src_resolution < 1 || src_resolution > kMaxGrid || grid < 1 || grid > kMaxGrid)
+        return fail(P3D_ERR_INVALID_ARG,
+                    "%s: src_resolution and grid must be in [1, %d], got %d and %d", fn,
+                    kMaxGrid, src_resolution, grid);
+    if (mode == P3D_REQUANT_ROUND_NODES && grid < 2)
+        return fail(P3D_ERR_INVALID_ARG, "%s: nearest-node rounding needs grid >= 2, got %d", fn,
+                    grid);
+    if (!aligned(src, 16) || !aligned(dst, 16))
+        return fail(P3D_ERR_UNSUPPORTED, "%s: src and dst must be 16-byte aligned ([n,4] int32)",
+                    fn);
+    if (n == 0) return ok();
+    if (!src || !dst) return fail(P3D_ERR_INVALID_ARG, "%s: src and dst must be non-NULL", fn);
+    RequantArgs a{src, dst, n, src_resolution, grid, (int32_t)mode};
+    hipError_t e = launch_requantize(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }
@@ -203,53 +256,117 @@ p3d_status p3d_bilinear_sample(const void* feat, p3d_dtype feat_dtype, int32_t b
     return ok();
 }
 
+p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution,
+                            p3d_points points, const p3d_camera* cams, int32_t batch,
+                            p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                            const void* weight, int32_t out_dim, int32_t weight_in,
+                            const void* bias, int64_t n_null, void* out, uint8_t* mask,
+                            void* stream) {
+    const char* fn = "p3d_proj_cond";
+    CamTable tab;
+    p3d_status st = check_tokens(fn, coords, n, resolution, points, cams, batch, &tab);
+    if (st != P3D_OK) return st;
+    if (!maps || n_maps < 1 || n_maps > 2)
+        return fail(P3D_ERR_INVALID_ARG, "%s: maps must be a host array of 1 or 2 maps, got %d",
+                    fn, maps ? n_maps : 0);
+    if (dtype != P3D_F32 && dtype != P3D_BF16)
+        return fail(P3D_ERR_DTYPE, "%s: dtype must be F32 or BF16, got %d", fn, (int)dtype);
+    const int epv = dtype == P3D_BF16 ? 8 : 4;
+    int64_t channels = 0;
+    for (int32_t m = 0; m < n_maps; ++m) {
+        char what[32];
+        snprintf(what, sizeof what, n_maps > 1 ? "maps[%d]" : "feature map", m);
+        st = check_map_size(fn, what, batch, maps[m].height, maps[m].width);
+        if (st != P3D_OK) return st;
+        if (maps[m].channels < 1)
+            return fail(P3D_ERR_INVALID_ARG, "%s: %s channels must be >= 1, got %d", fn, what,
+                        maps[m].channels);
+        if (maps[m].channels % epv)
+            return fail(P3D_ERR_UNSUPPORTED,
+                        "%s: %s channels must be a multiple of %d for %s (16-byte rows), got %d",
+                        fn, what, epv, dtype_name(dtype), maps[m].channels);
+        if (!aligned(maps[m].feat, 16))
+            return fail(P3D_ERR_UNSUPPORTED, "%s: %s feat must be 16-byte aligned", fn, what);
+        channels += maps[m].channels;
+    }
+    if (n_maps == 2 && maps[0].channels % 64)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: with two maps, maps[0].channels must be a multiple of 64, got %d", fn,
+                    maps[0].channels);
+    if (channels > INT32_MAX / 2)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: too many channels (%lld)", fn,
+                    (long long)channels);
+    if (n_null < 0 || n_null > kMaxTokens)
+        return fail(P3D_ERR_INVALID_ARG, "%s: n_null must be in [0, %lld], got %lld", fn,
+                    (long long)kMaxTokens, (long long)n_null);
+    if (out_dim < 1)
+        return fail(P3D_ERR_INVALID_ARG, "%s: out_dim must be >= 1, got %d", fn, out_dim);
+    if (out_dim > kMaxOutDim)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: out_dim must be <= %d, got %d", fn, kMaxOutDim,
+                    out_dim);
+    if (weight_in != channels) {
+        const p3d_map& m0 = maps[0];
+        if (n_maps == 1)
+            return fail(P3D_ERR_SHAPE,
+                        "%s: proj_linear weight is [%d, %d] but the feature map [%d, %d, %d, %d] "
+                        "has %d channels: the weight's input width must equal the map's channels",
+                        fn, out_dim, weight_in, batch, m0.height, m0.width, m0.channels,
+                        m0.channels);
+        const p3d_map& m1 = maps[1];
+        return fail(P3D_ERR_SHAPE,
+                    "%s: proj_linear weight is [%d, %d] but the feature maps [%d, %d, %d, %d] and "
+                    "[%d, %d, %d, %d] concatenate to %lld channels: the weight's input width must "
+                    "equal the summed channels",
+                    fn, out_dim, weight_in, batch, m0.height, m0.width, m0.channels, batch,
+                    m1.height, m1.width, m1.channels, (long long)channels);
+    }
+    if (out_dim % epv)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: out_dim must be a multiple of %d for %s (16-byte rows), got %d", fn, epv,
+                    dtype_name(dtype), out_dim);
+    if (!aligned(weight, 16) || !aligned(out, 16) || !aligned(bias, 16))
+        return fail(P3D_ERR_UNSUPPORTED, "%s: feat, weight, bias and out must be 16-byte aligned",
+                    fn);
+    if (n == 0 && n_null == 0) return ok();
+    if (!out) return fail(P3D_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (n > 0 && (!maps[0].feat || (n_maps == 2 && !maps[1].feat) || !weight))
+        return fail(P3D_ERR_INVALID_ARG, "%s: feat and weight must be non-NULL", fn);
+    ProjCondArgs a{};
+    a.coords = coords;
+    a.n = n;
+    a.R = resolution;
+    a.points = (int32_t)points;
+    a.batch = batch;
+    a.feat = maps[0].feat;
+    a.H = maps[0].height;
+    a.W = maps[0].width;
+    a.C = maps[0].channels;
+    if (n_maps == 2) {
+        a.feat1 = maps[1].feat;
+        a.H1 = maps[1].height;
+        a.W1 = maps[1].width;
+        a.C1 = maps[1].channels;
+    }
+    a.weight = weight;
+    a.bias = bias;
+    a.D = out_dim;
+    a.n_null = n_null;
+    a.out = out;
+    a.mask = mask;
+    hipError_t e = launch_proj_cond(a, dtype, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 p3d_status p3d_proj_cond(const int32_t* coords, int64_t n, int32_t resolution,
                          const p3d_camera* cams, int32_t batch, const void* feat,
                          p3d_dtype dtype, int32_t height, int32_t width, int32_t channels,
                          const void* weight, int32_t out_dim, int32_t weight_in,
                          const void* bias, int64_t n_null, void* out, uint8_t* mask,
                          void* stream) {
-    const char* fn = "p3d_proj_cond";
-    CamTable tab;
-    p3d_status st = check_tokens(fn, coords, n, resolution, cams, batch, height, width, &tab);
-    if (st != P3D_OK) return st;
-    if (dtype != P3D_F32 && dtype != P3D_BF16)
-        return fail(P3D_ERR_DTYPE, "%s: dtype must be F32 or BF16, got %d", fn, (int)dtype);
-    if (n_null < 0 || n_null > kMaxTokens)
-        return fail(P3D_ERR_INVALID_ARG, "%s: n_null must be in [0, %lld], got %lld", fn,
-                    (long long)kMaxTokens, (long long)n_null);
-    if (channels < 1 || out_dim < 1)
-        return fail(P3D_ERR_INVALID_ARG, "%s: channels and out_dim must be >= 1, got %d, %d", fn,
-                    channels, out_dim);
-    if (out_dim > kMaxOutDim)
-        return fail(P3D_ERR_UNSUPPORTED, "%s: out_dim must be <= %d, got %d", fn, kMaxOutDim,
-                    out_dim);
-    if (weight_in != channels)
-        return fail(P3D_ERR_SHAPE,
-                    "%s: proj_linear weight is [%d, %d] but the feature map [%d, %d, %d, %d] has "
-                    "%d channels: the weight's input width must equal the map's channels",
-                    fn, out_dim, weight_in, batch, height, width, channels, channels);
-    const int epv = dtype == P3D_BF16 ? 8 : 4;
-    if (channels % epv)
-        return fail(P3D_ERR_UNSUPPORTED,
-                    "%s: channels must be a multiple of %d for %s (16-byte rows), got %d", fn,
-                    epv, dtype_name(dtype), channels);
-    if (out_dim % epv)
-        return fail(P3D_ERR_UNSUPPORTED,
-                    "%s: out_dim must be a multiple of %d for %s (16-byte rows), got %d", fn, epv,
-                    dtype_name(dtype), out_dim);
-    if (!aligned(feat, 16) || !aligned(weight, 16) || !aligned(out, 16) || !aligned(bias, 16))
-        return fail(P3D_ERR_UNSUPPORTED, "%s: feat, weight, bias and out must be 16-byte aligned",
-                    fn);
-    if (n == 0 && n_null == 0) return ok();
-    if (!out) return fail(P3D_ERR_INVALID_ARG, "%s: out is NULL", fn);
-    if (n > 0 && (!feat || !weight))
-        return fail(P3D_ERR_INVALID_ARG, "%s: feat and weight must be non-NULL", fn);
-    ProjCondArgs a{coords, n, resolution, batch, feat, height, width, channels,
-                   weight, bias, out_dim, n_null, out, mask};
-    hipError_t e = launch_proj_cond(a, dtype, tab, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(fn, e);
-    return ok();
+    const p3d_map map{feat, height, width, channels};
+    return p3d_proj_cond_ex(coords, n, resolution, P3D_POINTS_CELL_CENTRES, cams, batch, dtype,
+                            &map, 1, weight, out_dim, weight_in, bias, n_null, out, mask, stream);
 }
 
 }  // extern "C"

@@ -48,6 +48,18 @@ __device__ __forceinline__ float cell_centre(int32_t c, int32_t R) {
     return ((float)c + 0.5f) / (float)R - 0.5f;
 }
 
+// Node c of the endpoint-inclusive projection grid linspace(-1, 1, R) at half
+// scale (cascade requantization commit): c/(R - 1) - 1/2, binary32; R >= 2.
+__device__ __forceinline__ float grid_node(int32_t c, int32_t R) {
+    return (float)c / (float)(R - 1) - 0.5f;
+}
+
+// World coordinate of integer position c: cell centre or grid node
+// (p3d_points; uniform across a launch).
+__device__ __forceinline__ float token_point(int32_t c, int32_t R, int32_t points) {
+    return points == P3D_POINTS_GRID_NODES ? grid_node(c, R) : cell_centre(c, R);
+}
+
 struct Projected {
     float gx, gy, depth;
     int32_t b;      // batch item after clamping into [0, batch)
@@ -55,14 +67,14 @@ struct Projected {
 };
 
 __device__ __forceinline__ Projected project_cell(int32_t b, int32_t cx, int32_t cy, int32_t cz,
-                                                  int32_t R, const CamTable& cams,
-                                                  int32_t batch) {
+                                                  int32_t R, int32_t points,
+                                                  const CamTable& cams, int32_t batch) {
     Projected p;
     const bool valid = (b >= 0) && (b < batch);
     b = b < 0 ? 0 : (b >= batch ? batch - 1 : b);
-    const float px = cell_centre(cx, R);
-    const float py = cell_centre(cy, R);
-    const float pz = cell_centre(cz, R);
+    const float px = token_point(cx, R, points);
+    const float py = token_point(cy, R, points);
+    const float pz = token_point(cz, R, points);
     const float f = cams.cam[b].focal;
     const float depth = cams.cam[b].distance - pz;
     const float gx = (f * px) / depth;
@@ -147,7 +159,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 struct ProjectArgs {
     const int32_t* coords;
     int64_t n;
-    int32_t R, batch, H, W;
+    int32_t R, points, batch, H, W;
     float* grid;
     int32_t* pixel;
     float* frac;
@@ -167,9 +179,11 @@ struct SampleArgs {
 struct ProjCondArgs {
     const int32_t* coords;
     int64_t n;
-    int32_t R, batch;
-    const void* feat;
+    int32_t R, points, batch;
+    const void* feat;             // map 0 [batch, H, W, C]
     int32_t H, W, C;
+    const void* feat1;            // map 1 [batch, H1, W1, C1], or C1 == 0
+    int32_t H1, W1, C1;           // K = C + C1; C % 64 == 0 when C1 > 0
     const void* weight;
     const void* bias;
     int32_t D;
@@ -178,7 +192,15 @@ struct ProjCondArgs {
     uint8_t* mask;
 };
 
+struct RequantArgs {
+    const int32_t* src;
+    int32_t* dst;
+    int64_t n;
+    int32_t src_res, grid, mode;
+};
+
 hipError_t launch_project(const ProjectArgs& a, const CamTable& cams, hipStream_t s);
+hipError_t launch_requantize(const RequantArgs& a, hipStream_t s);
 hipError_t launch_sample(const SampleArgs& a, p3d_dtype in, p3d_dtype out, hipStream_t s);
 hipError_t launch_proj_cond(const ProjCondArgs& a, p3d_dtype dt, const CamTable& cams,
                             hipStream_t s);

@@ -1,5 +1,6 @@
-// proj_cond.hip -- p3d_proj_cond: projection -> bilinear gather ->
-// proj_linear on the matrix cores, fused; plus the CFG null-branch fill.
+// proj_cond.hip -- p3d_proj_cond for binary32 maps (projection -> bilinear
+// gather -> proj_linear on the matrix cores, fused), the CFG null-branch
+// fill, and the dispatch between this path and the bf16 kernel.
 //
 // Sources: pixal3d_mrp_mlx tests/ history, pixel-aligned head commit
 // (project_points, bilinear_sample); trellis.cpp PR #38 "Initial support for
@@ -10,13 +11,15 @@
 // GEMM view: Y[M=n, N=D] = S[M, K=C] * W[N, K]^T + bias, where the A operand
 // S is never stored: each workgroup projects its BM tokens, then for every
 // K chunk gathers the four corner rows of each token (16-byte vectors,
-// eight lanes per 128-byte corner segment), blends them in binary32, rounds
-// to the operand type and writes the chunk into LDS, next to the matching
-// chunk of W. The matrix cores (v_mfma_f32_16x16x32_bf16, or
-// v_mfma_f32_16x16x4_f32 for binary32 maps) accumulate in binary32. The
-// next chunk's global loads are issued before the current chunk's MFMAs.
-// Tiles are mapped so that the D-tiles of one token tile run on the same
-// XCD and share its gathered corner rows in that XCD's L2.
+// eight lanes per 128-byte corner segment), blends them in binary32 and
+// writes the chunk into LDS next to the matching chunk of W; the matrix
+// cores (v_mfma_f32_16x16x4_f32) accumulate in binary32. The next chunk's
+// global loads are issued before the current chunk's MFMAs. Tiles are
+// mapped so that the D-tiles of one token tile run on the same XCD and share
+// its gathered corner rows in that XCD's L2. With a second map (NAF commit:
+// the DINOv3 map and its upsampled version, concatenated along K) the tokens
+// are projected once and the corners of both maps are kept in LDS; the K
+// chunks past map 0's channels read map 1.
 #include "p3d_internal.h"
 
 namespace p3d {
@@ -24,64 +27,36 @@ namespace p3d {
 namespace {
 
 constexpr int kThreads = 256;   // 4 waves, 2 (M) x 2 (N)
-
-template <bool Bf16>
-struct Cfg;
-template <>
-struct Cfg<false> {
-    static constexpr int BM = 128, BN = 128, BK = 32, EPV = 4;
-};
+constexpr int BM = 128, BN = 128, BK = 32;       // K chunk: 32 floats = 128 bytes
+constexpr int WM = BM / 2, WN = BN / 2;          // wave tile
+constexpr int MI = WM / 16, NJ = WN / 16;        // 16x16 blocks per wave
+constexpr int A_ITEMS = BM * 8 / kThreads;       // gathered vectors per thread
+constexpr int B_ITEMS = BN * 8 / kThreads;       // weight vectors per thread
 
 // Tile rows in LDS are BK elements = 128 bytes = 8 vectors of 16 bytes; the
 // vector index is XOR-swizzled with the row so that 16 lanes reading one
 // column of vectors from 16 consecutive rows spread over the banks.
 __device__ __forceinline__ int swz(int row, int v) { return row * 8 + (v ^ (row & 7)); }
 
-template <bool Bf16>
+// Bilinear blend of four 4-float vectors, binary32, corner order 00, 01, 10, 11.
 __device__ __forceinline__ uint4 blend4(const uint4 (&q)[4], float w0, float w1, float w2,
                                         float w3) {
+    const float* a = reinterpret_cast<const float*>(&q[0]);
+    const float* b = reinterpret_cast<const float*>(&q[1]);
+    const float* c = reinterpret_cast<const float*>(&q[2]);
+    const float* d = reinterpret_cast<const float*>(&q[3]);
     uint4 o;
-    if constexpr (Bf16) {
-        const uint32_t* a = reinterpret_cast<const uint32_t*>(&q[0]);
-        const uint32_t* b = reinterpret_cast<const uint32_t*>(&q[1]);
-        const uint32_t* c = reinterpret_cast<const uint32_t*>(&q[2]);
-        const uint32_t* d = reinterpret_cast<const uint32_t*>(&q[3]);
-        uint32_t* r = reinterpret_cast<uint32_t*>(&o);
+    float* r = reinterpret_cast<float*>(&o);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float lo = fmaf(w3, bf16lo(d[e]), fmaf(w2, bf16lo(c[e]),
-                                  fmaf(w1, bf16lo(b[e]), w0 * bf16lo(a[e]))));
-            const float hi = fmaf(w3, bf16hi(d[e]), fmaf(w2, bf16hi(c[e]),
-                                  fmaf(w1, bf16hi(b[e]), w0 * bf16hi(a[e]))));
-            r[e] = pack_bf16x2(lo, hi);
-        }
-    } else {
-        const float* a = reinterpret_cast<const float*>(&q[0]);
-        const float* b = reinterpret_cast<const float*>(&q[1]);
-        const float* c = reinterpret_cast<const float*>(&q[2]);
-        const float* d = reinterpret_cast<const float*>(&q[3]);
-        float* r = reinterpret_cast<float*>(&o);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            r[e] = fmaf(w3, d[e], fmaf(w2, c[e], fmaf(w1, b[e], w0 * a[e])));
-    }
+    for (int e = 0; e < 4; ++e) r[e] = fmaf(w3, d[e], fmaf(w2, c[e], fmaf(w1, b[e], w0 * a[e])));
     return o;
 }
 
-template <bool Bf16>
 __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, CamTable cams,
                                                              int32_t m_tiles, int32_t n_tiles,
                                                              int32_t per_xcd) {
-    using C = Cfg<Bf16>;
-    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, EPV = C::EPV;
-    constexpr int WM = BM / 2, WN = BN / 2;          // wave tile
-    constexpr int MI = WM / 16, NJ = WN / 16;        // 16x16 blocks per wave
-    constexpr int A_ITEMS = BM * 8 / kThreads;       // gathered vectors per thread
-    constexpr int B_ITEMS = BN * 8 / kThreads;       // weight vectors per thread
-    typedef typename std::conditional<Bf16, uint16_t, float>::type elem_t;
-
-    __shared__ int32_t s_row[BM][4];
-    __shared__ float s_w[BM][4];
+    __shared__ int32_t s_row[2][BM][4];    // corner rows per map
+    __shared__ float s_w[2][BM][4];
     __shared__ uint4 s_a[BM * 8];
     __shared__ uint4 s_b[BN * 8];
 
@@ -97,44 +72,54 @@ __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, Cam
     const int64_t m0 = (int64_t)mt * BM;
     const int32_t n0 = nt * BN;
 
-    // ---- project the tile's tokens: corner rows + weights into LDS
+    // ---- project the tile's tokens: corner rows + weights of each map
     if (tid < BM) {
         const int64_t t = m0 + tid;
-        if (t < a.n) {
-            int32_t b, x, y, z;
-            token_cell(a.coords, t, a.R, b, x, y, z);
-            const Projected p = project_cell(b, x, y, z, a.R, cams, a.batch);
-            const Corners c = corners_of(p.gx, p.gy, p.b, a.H, a.W);
-            s_row[tid][0] = c.r00; s_row[tid][1] = c.r01;
-            s_row[tid][2] = c.r10; s_row[tid][3] = c.r11;
-            s_w[tid][0] = c.w00; s_w[tid][1] = c.w01;
-            s_w[tid][2] = c.w10; s_w[tid][3] = c.w11;
-            if (a.mask && nt == 0) a.mask[t] = p.mask;
-        } else {
-            s_row[tid][0] = s_row[tid][1] = s_row[tid][2] = s_row[tid][3] = 0;
-            s_w[tid][0] = s_w[tid][1] = s_w[tid][2] = s_w[tid][3] = 0.0f;
+        for (int m = 0; m < (a.C1 > 0 ? 2 : 1); ++m) {
+            if (t < a.n) {
+                int32_t b, x, y, z;
+                token_cell(a.coords, t, a.R, b, x, y, z);
+                const Projected p = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
+                const Corners c = m ? corners_of(p.gx, p.gy, p.b, a.H1, a.W1)
+                                    : corners_of(p.gx, p.gy, p.b, a.H, a.W);
+                s_row[m][tid][0] = c.r00; s_row[m][tid][1] = c.r01;
+                s_row[m][tid][2] = c.r10; s_row[m][tid][3] = c.r11;
+                s_w[m][tid][0] = c.w00; s_w[m][tid][1] = c.w01;
+                s_w[m][tid][2] = c.w10; s_w[m][tid][3] = c.w11;
+                if (m == 0 && a.mask && nt == 0) a.mask[t] = p.mask;
+            } else {
+                s_row[m][tid][0] = s_row[m][tid][1] = s_row[m][tid][2] = s_row[m][tid][3] = 0;
+                s_w[m][tid][0] = s_w[m][tid][1] = s_w[m][tid][2] = s_w[m][tid][3] = 0.0f;
+            }
         }
     }
     __syncthreads();
 
-    const uint4* __restrict__ feat = reinterpret_cast<const uint4*>(a.feat);
+    const uint4* __restrict__ feat0 = reinterpret_cast<const uint4*>(a.feat);
+    const uint4* __restrict__ feat1 = reinterpret_cast<const uint4*>(a.feat1);
     const uint4* __restrict__ wgt = reinterpret_cast<const uint4*>(a.weight);
-    const int vpr = a.C / EPV;                       // vectors per map / weight row
-    const int nk = (a.C + BK - 1) / BK;
+    const int vpr0 = a.C / 4, vpr1 = a.C1 / 4;       // vectors per map row
+    const int vprw = vpr0 + vpr1;                    // vectors per weight row
+    const int k1 = a.C1 > 0 ? a.C / BK : 1 << 30;    // first chunk of map 1
+    const int nk = (a.C + a.C1 + BK - 1) / BK;
 
     uint4 qa[A_ITEMS][4];
     uint4 qb[B_ITEMS];
 
     auto issue_loads = [&](int kc) {
+        const int mp = kc >= k1 ? 1 : 0;                 // map of this chunk (uniform)
+        const uint4* __restrict__ feat = mp ? feat1 : feat0;
+        const int vpr = mp ? vpr1 : vpr0;
+        const int kl = mp ? kc - k1 : kc;                // chunk within the map
 #pragma unroll
         for (int u = 0; u < A_ITEMS; ++u) {
             const int i = tid + u * kThreads;
             const int m = i >> 3, v = i & 7;
-            const int kv = kc * 8 + v;
+            const int kv = kl * 8 + v;
             if (kv < vpr) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    qa[u][k] = feat[(int64_t)s_row[m][k] * vpr + kv];
+                    qa[u][k] = feat[(int64_t)s_row[mp][m][k] * vpr + kv];
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) qa[u][k] = make_uint4(0, 0, 0, 0);
@@ -145,8 +130,8 @@ __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, Cam
             const int i = tid + u * kThreads;
             const int j = i >> 3, v = i & 7;
             const int kv = kc * 8 + v;
-            qb[u] = (kv < vpr && n0 + j < a.D) ? wgt[(int64_t)(n0 + j) * vpr + kv]
-                                               : make_uint4(0, 0, 0, 0);
+            qb[u] = (kv < vprw && n0 + j < a.D) ? wgt[(int64_t)(n0 + j) * vprw + kv]
+                                                : make_uint4(0, 0, 0, 0);
         }
     };
 
@@ -159,10 +144,11 @@ __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, Cam
     issue_loads(0);
     for (int kc = 0; kc < nk; ++kc) {
         uint4 av[A_ITEMS];
+        const int mp = kc >= k1 ? 1 : 0;
 #pragma unroll
         for (int u = 0; u < A_ITEMS; ++u) {
             const int m = (tid + u * kThreads) >> 3;
-            av[u] = blend4<Bf16>(qa[u], s_w[m][0], s_w[m][1], s_w[m][2], s_w[m][3]);
+            av[u] = blend4(qa[u], s_w[mp][m][0], s_w[mp][m][1], s_w[mp][m][2], s_w[mp][m][3]);
         }
         __syncthreads();   // previous chunk's MFMA reads are done
 #pragma unroll
@@ -178,79 +164,52 @@ __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, Cam
         __syncthreads();
         if (kc + 1 < nk) issue_loads(kc + 1);
 
-        if constexpr (Bf16) {
+        // v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16] and
+        // B[l/16][l%16]; the four K quarters of a 16-byte vector are four
+        // MFMAs (K order within the chunk is permuted identically on both
+        // operands, which leaves the dot products unchanged).
 #pragma unroll
-            for (int kk = 0; kk < BK / 32; ++kk) {
-                const int v = kk * 4 + (lane >> 4);
-                bf16x8_t af[MI], bfr[NJ];
+        for (int kq = 0; kq < BK / 16; ++kq) {
+            const int v = kq * 4 + (lane >> 4);
+            float4 af[MI], bfr[NJ];
 #pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const int row = wm * WM + i * 16 + (lane & 15);
-                    af[i] = __builtin_bit_cast(bf16x8_t, s_a[swz(row, v)]);
-                }
+            for (int i = 0; i < MI; ++i) {
+                const int row = wm * WM + i * 16 + (lane & 15);
+                af[i] = __builtin_bit_cast(float4, s_a[swz(row, v)]);
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int row = wn * WN + j * 16 + (lane & 15);
+                bfr[j] = __builtin_bit_cast(float4, s_b[swz(row, v)]);
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const int row = wn * WN + j * 16 + (lane & 15);
-                    bfr[j] = __builtin_bit_cast(bf16x8_t, s_b[swz(row, v)]);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].x, bfr[j].x,
+                                                                    acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].y, bfr[j].y,
+                                                                    acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].z, bfr[j].z,
+                                                                    acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].w, bfr[j].w,
+                                                                    acc[i][j], 0, 0, 0);
                 }
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j],
-                                                                            acc[i][j], 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int kq = 0; kq < BK / 16; ++kq) {
-                const int v = kq * 4 + (lane >> 4);
-                float4 af[MI], bfr[NJ];
-#pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const int row = wm * WM + i * 16 + (lane & 15);
-                    af[i] = __builtin_bit_cast(float4, s_a[swz(row, v)]);
-                }
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const int row = wn * WN + j * 16 + (lane & 15);
-                    bfr[j] = __builtin_bit_cast(float4, s_b[swz(row, v)]);
-                }
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].x, bfr[j].x,
-                                                                        acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].y, bfr[j].y,
-                                                                        acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].z, bfr[j].z,
-                                                                        acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i].w, bfr[j].w,
-                                                                        acc[i][j], 0, 0, 0);
-                    }
-            }
         }
     }
 
-    // ---- epilogue: + bias, round, stage 16 rows at a time through LDS for
+    // ---- epilogue: + bias, stage 16 rows at a time through LDS for
     // coalesced 16-byte row stores. A 16x16 block's lane l holds rows
     // 4*(l/16) + r (r = 0..3) of column l % 16.
     float bias_v[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int col = n0 + wn * WN + j * 16 + (lane & 15);
-        float bv = 0.0f;
-        if (a.bias && col < a.D) {
-            if constexpr (Bf16)
-                bv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(a.bias)[col] << 16);
-            else
-                bv = reinterpret_cast<const float*>(a.bias)[col];
-        }
-        bias_v[j] = bv;
+        bias_v[j] = (a.bias && col < a.D) ? reinterpret_cast<const float*>(a.bias)[col] : 0.0f;
     }
-    constexpr int STAGE_VEC = 16 * WN * (int)sizeof(elem_t) / 16;  // vectors per wave stage
-    elem_t* stage = reinterpret_cast<elem_t*>(s_a) + wave * (16 * WN);
-    constexpr int ROW_VEC = WN * (int)sizeof(elem_t) / 16;          // vectors per staged row
+    constexpr int STAGE_VEC = 16 * WN / 4;           // 16-byte vectors per wave stage
+    constexpr int ROW_VEC = WN / 4;                  // vectors per staged row
+    float* stage = reinterpret_cast<float*>(s_a) + wave * (16 * WN);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         __syncthreads();
@@ -260,24 +219,19 @@ __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, Cam
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * (lane >> 4) + r;
                 const int col = j * 16 + (lane & 15);
-                const float y = acc[i][j][r] + bias_v[j];
-                if constexpr (Bf16)
-                    stage[row * WN + col] = __builtin_bit_cast(uint16_t, (__bf16)y);
-                else
-                    stage[row * WN + col] = y;
+                stage[row * WN + col] = acc[i][j][r] + bias_v[j];
             }
         __syncthreads();
         const uint4* st4 = reinterpret_cast<const uint4*>(stage);
 #pragma unroll
-        for (int q = lane; q < STAGE_VEC; q += 64) {
+        for (int rep = 0; rep < STAGE_VEC / 64; ++rep) {
+            const int q = rep * 64 + lane;
             const int row = q / ROW_VEC, cv = q - row * ROW_VEC;
             const int64_t t = m0 + wm * WM + i * 16 + row;
-            const int col = n0 + wn * WN + cv * EPV;
-            if (t < a.n && col < a.D) {
-                uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<elem_t*>(a.out) +
-                                                      t * a.D + col);
-                *dst = st4[q];
-            }
+            const int col = n0 + wn * WN + cv * 4;
+            if (t < a.n && col < a.D)
+                *reinterpret_cast<uint4*>(reinterpret_cast<float*>(a.out) + t * a.D + col) =
+                    st4[q];
         }
     }
 }
@@ -306,14 +260,13 @@ hipError_t launch_proj_cond(const ProjCondArgs& a, p3d_dtype dt, const CamTable&
     const bool bf16 = dt == P3D_BF16;
     if (bf16 && a.n > 0) return launch_proj_cond_bf16(a, cams, s);   // null rows included
     if (a.n > 0) {
-        const int BM = Cfg<false>::BM, BN = Cfg<false>::BN;
         int32_t m_tiles = (int32_t)((a.n + BM - 1) / BM);
         int32_t n_tiles = (a.D + BN - 1) / BN;
         int32_t per_xcd = (int32_t)(((int64_t)m_tiles * n_tiles + 7) / 8);
         ProjCondArgs args = a;
         CamTable tab = cams;
         void* params[] = {&args, &tab, &m_tiles, &n_tiles, &per_xcd};
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&proj_cond_kernel<false>),
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&proj_cond_kernel),
                                        dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
         if (e != hipSuccess) return e;
     }

@@ -40,6 +40,12 @@
 // Why 128 x 512: every N tile repeats the gather (four corner reads and a
 // blend per token and channel), every M tile re-reads W; with 64K fp32
 // accumulators per CU, 128 x 512 minimises the sum.
+// Two maps (NAF commit: the DINOv3 map and its upsampled version,
+// concatenated along K): the chunks past map 0's channels read map 1. The
+// producers keep one set of per-token corner metadata; after blending the
+// last map-0 chunk and before queueing the first map-1 chunk they recompute
+// it for map 1's size from the token coords (projection costs a few ALU
+// operations; a second set would not fit in the registers).
 // Tile order: workgroup g runs on XCD g % 8; each XCD walks a contiguous
 // range of (token tile, N tile) pairs, N fastest, so the N tiles of a token
 // tile and its neighbours share corner rows in that XCD's L2.
@@ -105,19 +111,61 @@ __device__ __forceinline__ uint4 blend_bf16(const uint4 (&q)[4], const float (&w
 
 typedef uint4 Gq[G_ITEMS][4];
 
-// Producer state: one thread of the four producer waves.
-struct Producer {
-    const uint4* feat;
-    const uint4* wgt;
-    int vpr, D, W, n0, ptid, lane, pw;
-    int gv;                          // vector of each gathered 128-byte segment
-    int4 gt[G_ITEMS];                // (top-left row, steps, tx, ty) per item
+// Corner metadata of token t on an H x W map: (top-left corner row, the 0/1
+// row steps to the right and lower corners, x fraction, y fraction); a token
+// past the end gets weight 0 everywhere (flag 4 in the steps).
+__device__ __forceinline__ int4 token_entry(const ProjCondArgs& a, const CamTable& cams,
+                                            int64_t t, int32_t H, int32_t W, uint8_t* mask) {
+    int4 e = make_int4(0, 4, 0, 0);
+    if (t < a.n) {
+        int32_t b, x, y, z;
+        token_cell(a.coords, t, a.R, b, x, y, z);
+        const Projected pr = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
+        const SrcIdx sx = source_index(pr.gx, W);
+        const SrcIdx sy = source_index(pr.gy, H);
+        e.x = (pr.b * H + sy.i0) * W + sx.i0;
+        e.y = (sx.i1 - sx.i0) | ((sy.i1 - sy.i0) << 1);
+        e.z = __float_as_int(sx.t);
+        e.w = __float_as_int(sy.t);
+        if (mask) *mask = pr.mask;
+    }
+    return e;
+}
 
-    // Queue the four corner vectors of every item of chunk kc. A K tail (C
-    // not a multiple of 64, or the padding chunk) clamps the address and
-    // zeroes the value.
+// Producer state: one thread of the four producer waves. TwoMaps: the gather
+// switches to map 1 part-way through K (kbase, vpr, W and the metadata
+// change); with one map they are constants of the launch.
+template <bool TwoMaps>
+struct Producer {
+    const uint4* feat;               // map of the chunks being gathered
+    const uint4* wgt;
+    int vpr;                         // 16-byte vectors per row of that map
+    int kbase;                       // first K chunk of that map
+    int vprw;                        // 16-byte vectors per W row (all of K)
+    int D, W, n0, ptid, lane, pw;
+    int gv;                          // vector of each gathered 128-byte segment
+    int4 gt[G_ITEMS];                // token_entry of each item
+
+    // Switch the gather to map 1: its base, row length, width and the
+    // items' corner metadata on its grid.
+    __device__ __forceinline__ void to_map1(const ProjCondArgs& a, const CamTable& cams,
+                                            int64_t m0, int k1) {
+        feat = reinterpret_cast<const uint4*>(a.feat1);
+        vpr = a.C1 >> 3;
+        kbase = k1;
+        W = a.W1;
+#pragma unroll
+        for (int u = 0; u < G_ITEMS; ++u)
+            gt[u] = token_entry(a, cams, m0 + ((ptid + u * kProdThreads) >> 3), a.H1, a.W1,
+                                nullptr);
+    }
+
+    // Queue the four corner vectors of every item of chunk kc. A K tail (the
+    // map's channels not a multiple of 64, or the padding chunk) clamps the
+    // address and zeroes the value.
     __device__ __forceinline__ void gather_issue(Gq& gq, int kc) const {
-        const int kv = min(kc * 8 + gv, vpr - 1);
+        const int kl = TwoMaps ? kc - kbase : kc;
+        const int kv = min(kl * 8 + gv, vpr - 1);
 #pragma unroll
         for (int u = 0; u < G_ITEMS; ++u) {
             // the 32-bit row index stays live, not four hoisted 64-bit
@@ -129,8 +177,8 @@ struct Producer {
 #pragma unroll
             for (int k = 0; k < 4; ++k) gq[u][k] = feat[(int64_t)rows[k] * vpr + kv];
         }
-        if ((kc + 1) * 8 > vpr) {                     // uniform: partial or padding chunk
-            const bool dead = kc * 8 + gv >= vpr;
+        if ((kl + 1) * 8 > vpr) {                     // uniform: partial or padding chunk
+            const bool dead = kl * 8 + gv >= vpr;
 #pragma unroll
             for (int u = 0; u < G_ITEMS; ++u)
 #pragma unroll
@@ -161,24 +209,30 @@ struct Producer {
         for (int q = 0; q < W_INSTR; ++q) {
             int col = min(n0 + pw * W_ROWS + q * 8 + (lane >> 3), D - 1);  // rows past D: unused
             asm volatile("" : "+v"(col));
-            const int kv = min(kc * 8 + ((q & 1) ? wv_odd : wv_even), vpr - 1);  // K tail: S is 0
+            const int kv = min(kc * 8 + ((q & 1) ? wv_odd : wv_even), vprw - 1);  // K tail: S is 0
             __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const void*>(wgt + (int64_t)col * vpr + kv),
+                reinterpret_cast<const void*>(wgt + (int64_t)col * vprw + kv),
                 (lds_void*)(sw + (pw * W_ROWS + q * 8) * 8), 16, 0, 0);
         }
     }
 };
 
 // One producer iteration: W of chunk kc+1, S of chunk kc+1 (its corner rows
-// were queued one chunk ago), corner rows of chunk kc+2, then this wave's W
-// loads must have landed before the barrier. The LDS stages are restrict
-// parameters so that the compiler can tell the direct W loads apart from
-// the S stores.
-__device__ __forceinline__ void produce(const Producer& p, int kc, int nk2, Gq& gq,
-                                        uint4* __restrict__ sa_n, uint4* __restrict__ sw_n) {
+// were queued one chunk ago), corner rows of chunk kc+2 (from map 1 from
+// chunk k1 on), then this wave's W loads must have landed before the
+// barrier. The LDS stages are restrict parameters so that the compiler can
+// tell the direct W loads apart from the S stores.
+template <bool TwoMaps>
+__device__ __forceinline__ void produce(Producer<TwoMaps>& p, const ProjCondArgs& a,
+                                        const CamTable& cams, int64_t m0, int k1, int kc,
+                                        int nk2, Gq& gq, uint4* __restrict__ sa_n,
+                                        uint4* __restrict__ sw_n) {
     if (kc + 1 < nk2) {
         p.w_issue(sw_n, kc + 1);
         p.commit(gq, sa_n);
+        if constexpr (TwoMaps) {
+            if (kc + 2 == k1) p.to_map1(a, cams, m0, k1);
+        }
         if (kc + 2 < nk2) {
             p.gather_issue(gq, kc + 2);
             wait_vmcnt<G_ITEMS * 4>();               // the queued gather may stay in flight
@@ -213,6 +267,7 @@ __device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TI], int lane, int cw
     lds_barrier();
 }
 
+template <bool TwoMaps>
 __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a, CamTable cams,
                                                                   int32_t m_tiles,
                                                                   int32_t n_tiles,
@@ -232,7 +287,8 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
     const int32_t mt = tile / n_tiles, nt = tile - mt * n_tiles;
     const int64_t m0 = (int64_t)mt * BM;
     const int32_t n0 = nt * BN;
-    const int nk = (a.C + BK - 1) / BK;
+    const int nk = (a.C + a.C1 + BK - 1) / BK;
+    const int k1 = a.C1 > 0 ? a.C / BK : 1 << 30;     // first chunk of map 1
     const int nk2 = (nk + 1) & ~1;                    // even chunk count: two stages per round
     uint4* out4 = reinterpret_cast<uint4*>(a.out);
     const int dv = a.D >> 3;                          // 16-byte vectors per output row
@@ -244,27 +300,18 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
         int4* s_tok = reinterpret_cast<int4*>(sA1);            // [BM]
         if (ptid < BM) {
             const int64_t t = m0 + ptid;
-            int4 e = make_int4(0, 4, 0, 0);                     // padding token: weights 0
-            if (t < a.n) {
-                int32_t b, x, y, z;
-                token_cell(a.coords, t, a.R, b, x, y, z);
-                const Projected pr = project_cell(b, x, y, z, a.R, cams, a.batch);
-                const SrcIdx sx = source_index(pr.gx, a.W);
-                const SrcIdx sy = source_index(pr.gy, a.H);
-                e.x = (pr.b * a.H + sy.i0) * a.W + sx.i0;
-                e.y = (sx.i1 - sx.i0) | ((sy.i1 - sy.i0) << 1);  // 0/1 steps in x and y
-                e.z = __float_as_int(sx.t);
-                e.w = __float_as_int(sy.t);
-                if (a.mask && nt == 0) a.mask[t] = pr.mask;
-            }
-            s_tok[ptid] = e;
+            uint8_t mk = 0;
+            s_tok[ptid] = token_entry(a, cams, t, a.H, a.W, &mk);
+            if (a.mask && nt == 0 && t < a.n) a.mask[t] = mk;
         }
         __syncthreads();                                          // (1) tokens parked
 
-        Producer p;
+        Producer<TwoMaps> p;
         p.feat = reinterpret_cast<const uint4*>(a.feat);
         p.wgt = reinterpret_cast<const uint4*>(a.weight);
         p.vpr = a.C >> 3;
+        p.kbase = 0;
+        p.vprw = (a.C + a.C1) >> 3;
         p.D = a.D;
         p.W = a.W;
         p.n0 = n0;
@@ -279,12 +326,15 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
         __syncthreads();                                          // (2) sA1 free again
         p.w_issue(sW0, 0);
         p.commit(gq, sA0);
+        if constexpr (TwoMaps) {
+            if (k1 == 1) p.to_map1(a, cams, m0, k1);
+        }
         p.gather_issue(gq, 1);
         wait_vmcnt<G_ITEMS * 4>();
         lds_barrier();                                            // B_0
         for (int kc = 0; kc < nk2; kc += 2) {
-            produce(p, kc, nk2, gq, sA1, sW1);
-            produce(p, kc + 1, nk2, gq, sA0, sW0);
+            produce(p, a, cams, m0, k1, kc, nk2, gq, sA1, sW1);
+            produce(p, a, cams, m0, k1, kc + 1, nk2, gq, sA0, sW0);
         }
         __syncthreads();                                          // consumers staged
 
@@ -366,7 +416,9 @@ hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hi
     ProjCondArgs args = a;
     CamTable tab = cams;
     void* params[] = {&args, &tab, &m_tiles, &n_tiles, &per_xcd, &null_tiles};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_cond_bf16_kernel),
+    const void* fn = a.C1 > 0 ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<true>)
+                              : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false>);
+    return hipLaunchKernel(fn,
                            dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
 }
 

@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void project_kernel(ProjectArgs a, CamTable ca
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < a.n; t += stride) {
         int32_t b, x, y, z;
         token_cell(a.coords, t, a.R, b, x, y, z);
-        const Projected p = project_cell(b, x, y, z, a.R, cams, a.batch);
+        const Projected p = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
         if (a.grid) reinterpret_cast<float2*>(a.grid)[t] = make_float2(p.gx, p.gy);
         if (a.depth) a.depth[t] = p.depth;
         if (a.mask) a.mask[t] = p.mask;

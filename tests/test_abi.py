@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(p3d):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(p3d.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -167,3 +167,70 @@ def test_project_points_validation(p3d):
     st = p3d.lib.p3d_project_points(FAKE, 10, 8, _cams(p3d, [(2.0, 2.0)]), 1, 4, 4, FAKE + 4,
                                     NULL, NULL, NULL, NULL, NULL)
     assert st == 4 and "8-byte aligned" in p3d.p3d_last_error()
+
+
+# ------------------------------------------- grid nodes, requantization, maps
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(n=-1), 1, "n must be"),
+    (dict(mode=5), 1, "ROUND_NODES or FLOOR_CELLS"),
+    (dict(grid=1), 1, "grid >= 2"),
+    (dict(src_res=0), 1, "src_resolution and grid"),
+    (dict(grid=(1 << 20) + 1), 1, "src_resolution and grid"),
+    (dict(src=FAKE + 4), 4, "16-byte aligned"),
+], ids=lambda v: str(v)[:30])
+def test_requantize_validation(p3d, args, status, needle):
+    a = dict(src=FAKE, n=10, src_res=512, grid=64, mode=0, dst=FAKE)
+    a.update(args)
+    st = p3d.lib.p3d_requantize_coords(a["src"], a["n"], a["src_res"], a["grid"], a["mode"],
+                                       a["dst"], NULL)
+    assert st == status, p3d.p3d_last_error()
+    assert needle in p3d.p3d_last_error()
+
+
+def test_requantize_zero_tokens_is_ok(p3d):
+    assert p3d.lib.p3d_requantize_coords(NULL, 0, 512, 64, 0, NULL, NULL) == 0
+    assert p3d.lib.p3d_requantize_coords(NULL, 0, 512, 1, 1, NULL, NULL) == 0
+
+
+def test_project_points_ex_validation(p3d):
+    cams = _cams(p3d, [(2.0, 2.0)])
+    st = p3d.lib.p3d_project_points_ex(FAKE, 8, 1, 1, cams, 1, 4, 4, NULL, NULL, NULL, NULL,
+                                       NULL, NULL)
+    assert st == 1 and "resolution >= 2" in p3d.p3d_last_error()
+    st = p3d.lib.p3d_project_points_ex(FAKE, 8, 8, 3, cams, 1, 4, 4, NULL, NULL, NULL, NULL,
+                                       NULL, NULL)
+    assert st == 1 and "CELL_CENTRES or GRID_NODES" in p3d.p3d_last_error()
+
+
+def _pcx(p3d, maps, **kw):
+    arr = (p3d.p3d_map * max(1, len(maps)))()
+    for i, (f, h, w, c) in enumerate(maps):
+        arr[i].feat, arr[i].height, arr[i].width, arr[i].channels = f, h, w, c
+    a = dict(coords=FAKE, n=16, R=8, points=0, cams=_cams(p3d, [(2.0, 2.0)]), batch=1,
+             dtype=p3d.P3D_BF16, n_maps=len(maps), weight=FAKE, D=64, Cw=128, bias=NULL,
+             n_null=0, out=FAKE, mask=NULL)
+    a.update(kw)
+    st = p3d.lib.p3d_proj_cond_ex(a["coords"], a["n"], a["R"], a["points"], a["cams"],
+                                  a["batch"], a["dtype"], arr, a["n_maps"], a["weight"], a["D"],
+                                  a["Cw"], a["bias"], a["n_null"], a["out"], a["mask"], NULL)
+    return st, p3d.p3d_last_error()
+
+
+def test_proj_cond_ex_validation(p3d):
+    two = [(FAKE, 4, 4, 64), (FAKE, 8, 8, 64)]
+    st, msg = _pcx(p3d, two, n_maps=3)
+    assert st == 1 and "1 or 2 maps" in msg
+    st, msg = _pcx(p3d, [(FAKE, 4, 4, 72), (FAKE, 8, 8, 64)], Cw=136)
+    assert st == 4 and "multiple of 64" in msg
+    st, msg = _pcx(p3d, [(FAKE, 4, 4, 64), (FAKE, 8, 8, 60)], Cw=124)
+    assert st == 4 and "maps[1] channels" in msg
+    st, msg = _pcx(p3d, [(FAKE, 4, 4, 64), (FAKE, 0, 8, 64)])
+    assert st == 1 and "maps[1] height/width" in msg
+    st, msg = _pcx(p3d, two, Cw=96)
+    assert st == 2 and "[64, 96]" in msg and "[1, 4, 4, 64]" in msg and "[1, 8, 8, 64]" in msg
+    st, msg = _pcx(p3d, [(FAKE + 8, 4, 4, 64), (FAKE, 8, 8, 64)])
+    assert st == 4 and "maps[0] feat must be 16-byte aligned" in msg
+    st, msg = _pcx(p3d, two, points=1, R=1)
+    assert st == 1 and "resolution >= 2" in msg
+    st, msg = _pcx(p3d, two, n=0, coords=NULL)
+    assert st == 0, msg

@@ -21,6 +21,10 @@ Prints ONE JSON line. Fields beyond the common ones:
   gather         the standalone bilinear gather on the same points: algorithmic
                  bytes / duration against peak HBM bandwidth.
   null_fill      the null-branch fill alone: bytes written / duration.
+  extra          the adjacent parts, each on its own workload with its own
+                 roofline: cascade requantization (HBM), the fused kernel on
+                 grid-node points after requantization (MFMA), the fused
+                 kernel over two concatenated maps (MFMA).
 """
 import argparse
 import hashlib
@@ -132,6 +136,85 @@ def cpu_baseline(inp, cams_o, target_s=12.0):
                       "CPU %s" % (done, inp["n"], t_total, cpu_model())}
 
 
+def run_extra(p3d, synth, stream, reps, lead_step):
+    """Adjacent parts on their own workloads: requantization of a res-512
+    shell onto the 64-node grid, the fused kernel on those grid nodes, and
+    the fused kernel over the two-map texture-stage workload."""
+    import numpy as np
+    import torch
+
+    def dev(a, as_bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16).view(torch.bfloat16) if as_bf16 else t).cuda()
+
+    def lead():
+        for _ in range(2):
+            lead_step()
+
+    out = {}
+    # ---- cascade: requantize, then grid nodes
+    w = synth.workload("cascade512_grid64_nodes_bf16_c2048_d1536")
+    src = dev(synth.coords(w))
+    n = src.shape[0]
+    q = torch.empty_like(src)
+    rq = lambda: p3d.p3d_requantize_coords(src, w.coords_resolution, w.resolution, q)
+    rq()
+    rq_ms = time_events(rq, reps, stream, lead)
+    rq_bytes = 32 * n
+    feat = dev(synth.feature_map(w), True)
+    weight = dev(synth.weight(w), True)
+    cams = [p3d.p3d_make_camera(a, p3d.p3d_distance_from_fov(a, w.width, 0))
+            for a in synth.fovs(w)]
+    camarr = p3d.make_cameras(cams)
+    y = torch.empty((n, w.out_dim), dtype=torch.bfloat16, device="cuda")
+    fused = lambda: p3d.p3d_proj_cond(q, n, w.resolution, camarr, feat, weight, y,
+                                      points="grid_nodes")
+    for _ in range(reps):
+        fused()
+    nodes_ms = time_events(fused, reps, stream)
+    flops = 2.0 * n * w.k_total * w.out_dim
+    out["requantize"] = {
+        "workload": w.name, "kernel": "requant_kernel", "tokens": n, "mean_ms": rq_ms,
+        "bound": "hbm", "bytes_per_launch": rq_bytes,
+        "achieved": rq_bytes / (rq_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": rq_bytes / (rq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "note": "100k tokens = 3.2 MB: launch-latency bound, far from the HBM roofline"}
+    out["grid_nodes"] = {
+        "workload": w.name, "kernel": "proj_cond_bf16_kernel<false>", "tokens": n,
+        "mean_ms": nodes_ms, "bound": "mfma", "flops_per_launch": flops,
+        "achieved": flops / (nodes_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s", "frac": flops / (nodes_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "cascade_tokens_per_s": n / ((rq_ms + nodes_ms) * 1e-3)}
+    del feat, weight, y, q, src
+    torch.cuda.empty_cache()
+    # ---- two maps
+    w = synth.workload("shell1024_cfg_twomap_bf16_c1024x2_d1536")
+    coords = dev(synth.coords(w))
+    n, nn = w.n_tokens, w.n_null
+    maps = [dev(m, True) for m in synth.feature_maps(w)]
+    weight = dev(synth.weight(w), True)
+    cams = [p3d.p3d_make_camera(a, p3d.p3d_distance_from_fov(a, w.width, 0))
+            for a in synth.fovs(w)]
+    camarr = p3d.make_cameras(cams)
+    y = torch.empty((n + nn, w.out_dim), dtype=torch.bfloat16, device="cuda")
+    two = lambda: p3d.p3d_proj_cond(coords, n, w.resolution, camarr, maps, weight, y,
+                                    n_null=nn)
+    for _ in range(reps):
+        two()
+    two_ms = time_events(two, reps, stream)
+    flops = 2.0 * n * w.k_total * w.out_dim
+    out["two_maps"] = {
+        "workload": w.name, "kernel": "proj_cond_bf16_kernel<true>", "tokens": n,
+        "null_rows": nn, "maps": ["%dx%dx%dx%d" % tuple(m.shape) for m in maps],
+        "mean_ms": two_ms, "tokens_per_s": n / (two_ms * 1e-3), "bound": "mfma",
+        "flops_per_launch": flops, "achieved": flops / (two_ms * 1e-3) / 1e12,
+        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": flops / (two_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    del maps, weight, y, coords
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +223,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the adjacent-part measurements")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per launch (counter scale)")
     args = ap.parse_args()
@@ -314,6 +399,8 @@ def main():
         "input_generation_s": t_gen,
         "source_digest": kernel_source_digest(),
     }
+    if not args.no_extra:
+        line["extra"] = run_extra(p3d, synth, stream, max(args.steps, 20), step)
     if not args.no_cpu_baseline:
         import oracle
         o = oracle.get()

@@ -74,7 +74,15 @@ def _declare(lib):
                                           ctypes.POINTER(_vp), _i32p, _i32p, _i32p, _i32,
                                           _vp, _vp, _i32, _i64, _i64p, _i64, _f64p, _u8p,
                                           _f64p]
+    lib.orc_projection_stats.restype = None
+    lib.orc_projection_stats.argtypes = [_i32p, _i64, _i32, _i32, _f32p, _f32p, _i32, _i32,
+                                         ctypes.POINTER(_vp), _i32p, _i32p, _i32p, _i32,
+                                         _f64p, _f64p]
     return lib
+
+
+STAT_FIELDS = ("tokens", "inside", "sum0", "sum1", "sum_sq0", "sum_sq1", "cos_sum",
+               "cos_count")
 
 
 POINTS = {"cell_centres": 0, "grid_nodes": 1}
@@ -211,6 +219,31 @@ class Oracle:
         return Y
 
     # -------------------------------------------------------- whole path ---
+    def projection_stats(self, coords, n, resolution, focal, dist, feat,
+                         points="cell_centres"):
+        """Raw diagnostic sums over tokens [0, n) (dict of STAT_FIELDS);
+        feat is one map or a list of two."""
+        feats = [np.ascontiguousarray(f) for f in (feat if isinstance(feat, (list, tuple))
+                                                    else [feat])]
+        is_bf16 = feats[0].dtype == np.uint16
+        B = feats[0].shape[0]
+        Hs = np.array([f.shape[1] for f in feats], np.int32)
+        Ws = np.array([f.shape[2] for f in feats], np.int32)
+        Cs = np.array([f.shape[3] for f in feats], np.int32)
+        if coords is not None:
+            coords = np.ascontiguousarray(coords, dtype=np.int32)
+            assert coords.shape == (n, 4)
+        focal = np.ascontiguousarray(focal, dtype=np.float32).reshape(-1)
+        dist = np.ascontiguousarray(dist, dtype=np.float32).reshape(-1)
+        out = np.zeros(8, np.float64)
+        S = np.empty(int(Cs.sum()), np.float64)
+        fp = (_vp * len(feats))(*[f.ctypes.data for f in feats])
+        self.lib.orc_projection_stats(_ptr(coords, _i32p), n, resolution, POINTS[points],
+                                      _ptr(focal, _f32p), _ptr(dist, _f32p), B, len(feats), fp,
+                                      _ptr(Hs, _i32p), _ptr(Ws, _i32p), _ptr(Cs, _i32p),
+                                      int(is_bf16), _ptr(out, _f64p), _ptr(S, _f64p))
+        return dict(zip(STAT_FIELDS, out.tolist()))
+
     def proj_cond_rows(self, coords, n, resolution, focal, dist, feat, weight, bias,
                        n_null, rows, points="cell_centres"):
         """Rows `rows` (indices into [0, n + n_null)) of the whole path:
@@ -252,6 +285,21 @@ class Oracle:
                                        _ptr(rows, _i64p), rows.size, _ptr(Y, _f64p),
                                        _ptr(mask, _u8p), _ptr(S, _f64p))
         return Y, mask
+
+
+def stats_summary(raw, channels):
+    """Derived figures from the raw sums: coverage, per-half mean and std
+    (population), mean cosine between the halves (None when not defined)."""
+    t = raw["tokens"]
+    out = {"coverage": raw["inside"] / t if t else None}
+    for h, c in enumerate(channels):
+        cnt = t * c
+        mean = raw["sum%d" % h] / cnt if cnt else None
+        out["mean%d" % h] = mean
+        out["std%d" % h] = (max(raw["sum_sq%d" % h] / cnt - mean * mean, 0.0) ** 0.5
+                            if cnt else None)
+    out["cosine"] = raw["cos_sum"] / raw["cos_count"] if raw["cos_count"] else None
+    return out
 
 
 _default = None

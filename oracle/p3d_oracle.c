@@ -27,6 +27,9 @@
  *               texture stages sample two maps (the DINOv3 map and its
  *               NAF-upsampled version) and feed the concatenation, hence
  *               proj_in_channels = 2048.
+ *   [PR38-diag] same PR, commits adding projection diagnostics (coverage;
+ *               per-half mean/std and the halves' cosine similarity) and the
+ *               cross-resolution agreement of samples at the same points.
  *
  * Precision. Whatever decides an integer (pixel index, in-image mask) is
  * computed in binary32 with one IEEE rounding per operation, in the order
@@ -43,6 +46,11 @@
  *     exactly in integers (no ties occur at the pages' sizes);
  *   - two maps: the sample is map 0's channels followed by map 1's, each map
  *     sampled at the same normalised point on its own height and width;
+ *   - diagnostics: coverage = tokens with mask 1 / tokens; the per-half
+ *     mean/std run over every token and channel of that half's samples as
+ *     fed to proj_linear (bf16-rounded for bf16 maps); the cosine is taken
+ *     per token between the two halves (equal channel counts) and averaged
+ *     over the tokens where both halves are non-zero;
  *   - camera at (0, 0, +d) looking down -Z: depth = d - z;
  *   - FOV is the full angle: focal = 1/tan(fov/2) in normalised image units;
  *   - image y grows downwards: gy = -(f*y)/depth;
@@ -451,4 +459,65 @@ void orc_proj_cond_rows(const int32_t* coords, int64_t n, int32_t R,
     const void* feats[1] = {feat};
     orc_proj_cond_rows_ex(coords, n, R, 0, focal, dist, batch, 1, feats, &H, &W, &C, is_bf16,
                           weight, bias, D, n_null, rows, nrows, Y, mask, S_scratch);
+}
+
+/* --------------------------------------------------------- diagnostics ---
+ * [PR38-diag]: figures that expose a wrong camera, grid or map layout, none
+ * of which fails at run time. Over tokens [0, n) (samples as in the whole
+ * path, before proj_linear):
+ *   out[0] tokens n          out[1] tokens with mask 1
+ *   out[2+h] sum of the samples of map h over all tokens and its channels
+ *   out[4+h] sum of their squares
+ *   out[6]   sum over tokens of cos(S0, S1) = <S0, S1> / (|S0| |S1|), for
+ *            two maps with equal channels, over tokens with |S0|, |S1| > 0
+ *   out[7]   the number of tokens in out[6]
+ * Accumulated in binary64 in token order. */
+void orc_projection_stats(const int32_t* coords, int64_t n, int32_t R, int32_t points,
+                          const float* focal, const float* dist, int32_t batch,
+                          int32_t n_maps, const void* const* feats, const int32_t* Hs,
+                          const int32_t* Ws, const int32_t* Cs, int32_t is_bf16,
+                          double* out, double* S_scratch)
+{
+    for (int k = 0; k < 8; ++k) out[k] = 0.0;
+    int32_t C = 0;
+    for (int32_t m = 0; m < n_maps; ++m) C += Cs[m];
+    const int cosine = (n_maps == 2 && Cs[0] == Cs[1]);
+    for (int64_t t = 0; t < n; ++t) {
+        int32_t cell[4];
+        token_cell(coords, t, R, cell);
+        float gx, gy, dep;
+        uint8_t msk;
+        int32_t b;
+        project_one(cell, R, points, focal, dist, batch, &gx, &gy, &dep, &msk, &b);
+        double* s = S_scratch;
+        int32_t off = 0;
+        for (int32_t m = 0; m < n_maps; ++m) {
+            sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, &s[off]);
+            off += Cs[m];
+        }
+        if (is_bf16)
+            for (int32_t c = 0; c < C; ++c) s[c] = (double)orc_bf16_to_f32(orc_f64_to_bf16(s[c]));
+        out[0] += 1.0;
+        out[1] += (double)msk;
+        off = 0;
+        for (int32_t m = 0; m < n_maps; ++m) {
+            for (int32_t c = 0; c < Cs[m]; ++c) {
+                out[2 + m] += s[off + c];
+                out[4 + m] += s[off + c] * s[off + c];
+            }
+            off += Cs[m];
+        }
+        if (cosine) {
+            double dot = 0.0, n0 = 0.0, n1 = 0.0;
+            for (int32_t c = 0; c < Cs[0]; ++c) {
+                dot += s[c] * s[Cs[0] + c];
+                n0 += s[c] * s[c];
+                n1 += s[Cs[0] + c] * s[Cs[0] + c];
+            }
+            if (n0 > 0.0 && n1 > 0.0) {
+                out[6] += dot / (sqrt(n0) * sqrt(n1));
+                out[7] += 1.0;
+            }
+        }
+    }
 }

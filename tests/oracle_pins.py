@@ -558,5 +558,115 @@ def pin_two_map_linearity(o):
     assert _rel(Y, Ya + Yb, np.abs(Y).max()) < 1e-12
 
 
+# ------------------------------------------------------------ diagnostics ---
+def _torch_samples(o, feats, coords, n, R, focal, dist, points, bf16):
+    """Per map, torch grid_sample (bilinear, border, align_corners=False) of
+    the map at the oracle's projected points; bf16 maps give bf16-rounded
+    samples, as fed to proj_linear."""
+    import torch
+    p = o.project(coords, n, R, focal, dist, 4, 4, points=points)
+    bidx = coords[:, 0] if coords is not None else np.zeros(n, np.int64)
+    out = []
+    for f in feats:
+        v = o.bf16_to_f32(f) if bf16 else f
+        inp = torch.from_numpy(np.ascontiguousarray(v)).permute(0, 3, 1, 2).contiguous()
+        S = np.empty((n, f.shape[3]), np.float64)
+        for b in range(f.shape[0]):
+            sel = np.nonzero(bidx == b)[0]
+            if sel.size == 0:
+                continue
+            gr = torch.from_numpy(p["grid"][sel]).reshape(1, 1, -1, 2)
+            r = torch.nn.functional.grid_sample(inp[b:b + 1], gr, mode="bilinear",
+                                                padding_mode="border",
+                                                align_corners=False)[0, :, 0, :].T
+            if bf16:
+                r = r.to(torch.bfloat16)
+            S[sel] = r.double().numpy()
+        out.append(S)
+    return out, p["mask"]
+
+
+def pin_stats_torch_numpy(o):
+    """Coverage, per-half sums and the mean cosine against torch grid_sample
+    samples reduced with numpy, for two maps of different sizes, fp32 and
+    bf16, with tokens outside the frame and behind the camera."""
+    rng = np.random.default_rng(31)
+    R, n = 12, 300
+    coords = np.concatenate([rng.integers(0, 2, (n, 1)), rng.integers(-4, R + 4, (n, 3))],
+                            1).astype(np.int32)
+    fo, do = o.cameras([45.0, 60.0], [1.2, 0.55])
+    for bf16 in (False, True):
+        m0 = rng.standard_normal((2, 7, 9, 16)).astype(np.float32)
+        m1 = rng.standard_normal((2, 20, 13, 16)).astype(np.float32) + 0.3
+        feats = [o.f32_to_bf16(m0), o.f32_to_bf16(m1)] if bf16 else [m0, m1]
+        for points in ("cell_centres", "grid_nodes"):
+            st = o.projection_stats(coords, n, R, fo, do, feats, points=points)
+            (S0, S1), mask = _torch_samples(o, feats, coords, n, R, fo, do, points, bf16)
+            assert st["tokens"] == n and st["inside"] == mask.sum()
+            assert 0 < mask.sum() < n
+            for h, S in enumerate((S0, S1)):
+                assert abs(st["sum%d" % h] - S.sum()) <= 1e-5 * np.abs(S).sum()
+                assert abs(st["sum_sq%d" % h] - (S * S).sum()) <= 1e-5 * (S * S).sum()
+            n0, n1 = np.linalg.norm(S0, axis=1), np.linalg.norm(S1, axis=1)
+            ok = (n0 > 0) & (n1 > 0)
+            cos = (S0 * S1).sum(1)[ok] / (n0[ok] * n1[ok])
+            assert st["cos_count"] == ok.sum()
+            assert abs(st["cos_sum"] - cos.sum()) <= 1e-5 * n, (st["cos_sum"], cos.sum())
+
+
+def pin_stats_scaled_copies(o):
+    """A map and a scaled copy of it on the same grid: the cosine is exactly
+    +1 (or -1 for a negative scale) at every token, mean and std scale with
+    it; constant maps give their constants as means, std 0, and the sign of
+    their product as cosine."""
+    rng = np.random.default_rng(37)
+    m0 = rng.standard_normal((1, 11, 8, 24)).astype(np.float32)
+    coords = np.concatenate([np.zeros((80, 1)), rng.integers(0, 10, (80, 3))], 1).astype(np.int32)
+    f, d = o.camera(40.0, 1.5)
+    for a in (3.0, -0.5):
+        st = o.projection_stats(coords, 80, 10, [f], [d], [m0, (a * m0).astype(np.float32)])
+        assert st["cos_count"] == 80
+        assert abs(st["cos_sum"] - 80 * np.sign(a)) < 1e-9
+        mag = abs(a) * math.sqrt(80 * 24 * st["sum_sq0"])    # >= sum |a S0|
+        assert abs(st["sum1"] - a * st["sum0"]) <= 1e-6 * mag
+        assert abs(st["sum_sq1"] - a * a * st["sum_sq0"]) <= 1e-6 * st["sum_sq1"]
+    c0 = np.full((1, 3, 5, 8), 0.25, np.float32)
+    c1 = np.full((1, 6, 4, 8), -2.0, np.float32)
+    st = o.projection_stats(coords, 80, 10, [f], [d], [c0, c1])
+    # binary32 bilinear weights sum to 1 within a few ulp
+    assert abs(st["sum0"] - 0.25 * 80 * 8) < 1e-6 * 0.25 * 80 * 8
+    assert abs(st["sum1"] + 2.0 * 80 * 8) < 1e-6 * 2.0 * 80 * 8
+    assert abs(st["sum_sq0"] - 0.0625 * 80 * 8) < 1e-6 * 0.0625 * 80 * 8
+    assert abs(st["sum_sq1"] - 4.0 * 80 * 8) < 1e-6 * 4.0 * 80 * 8
+    assert st["cos_count"] == 80 and abs(st["cos_sum"] + 80) < 1e-12
+
+
+def pin_stats_coverage_corners(o):
+    """At the closed-form distance the two near cube corners leave the frame
+    and the two far ones stay inside (coverage is a ratio, not a pass/fail);
+    a token behind the camera counts as outside."""
+    R = 64
+    f, d = o.camera(40.0, o.distance_from_fov(40.0, 512, 0))
+    cells = np.array([[0, R - 1, R - 1, R - 1], [0, 0, 0, R - 1],
+                      [0, R - 1, R - 1, 0], [0, 0, 0, 0]], np.int32)
+    m = np.ones((1, 4, 4, 8), np.float32)
+    st = o.projection_stats(cells, 4, R, [f], [d], m)
+    assert st["tokens"] == 4 and st["inside"] == 2
+    f2, d2 = o.camera(40.0, 0.3)          # z = +0.49 cells sit behind this camera
+    st = o.projection_stats(np.array([[0, 32, 32, R - 1], [0, 32, 32, 0]], np.int32), 2, R,
+                            [f2], [d2], m)
+    assert st["inside"] == 1
+
+
+def pin_stats_zero_map(o):
+    """A half that samples to zero has no direction: no cosine is counted."""
+    coords = np.array([[0, 1, 2, 3], [0, 3, 3, 3]], np.int32)
+    f, d = o.camera(40.0, 2.0)
+    z = np.zeros((1, 4, 4, 8), np.float32)
+    st = o.projection_stats(coords, 2, 5, [f], [d], [z, z + 1])
+    assert st["cos_count"] == 0 and st["cos_sum"] == 0 and st["sum0"] == 0
+    assert abs(st["sum1"] - 16) < 1e-6
+
+
 ALL_PINS = {name[len("pin_"):]: fn for name, fn in sorted(globals().items())
             if name.startswith("pin_") and callable(fn)}

@@ -73,6 +73,18 @@ MUTANTS = [
     ("two_maps_order_reversed",
      "sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, s + off);",
      "sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, s + (C - off - Cs[m]));"),
+    ("stats_maps_share_first_size",
+     "sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, &s[off]);",
+     "sample_one(feats[m], is_bf16, b, Hs[0], Ws[0], Cs[m], gx, gy, &s[off]);"),
+    ("stats_sum_sq_not_squared", "out[4 + m] += s[off + c] * s[off + c];",
+     "out[4 + m] += s[off + c];"),
+    ("stats_cosine_unnormalised", "out[6] += dot / (sqrt(n0) * sqrt(n1));", "out[6] += dot;"),
+    ("stats_cosine_same_half", "dot += s[c] * s[Cs[0] + c];", "dot += s[c] * s[c];"),
+    ("stats_coverage_counts_all", "out[1] += (double)msk;", "out[1] += 1.0;"),
+    ("stats_halves_swapped", "out[2 + m] += s[off + c];", "out[3 - m] += s[off + c];"),
+    ("stats_unrounded_bf16",
+     "        if (is_bf16)\n            for (int32_t c = 0; c < C; ++c) s[c] = (double)orc_bf16_to_f32(orc_f64_to_bf16(s[c]));\n        out[0] += 1.0;",
+     "        out[0] += 1.0;"),
 ]
 
 RUNNER = r"""

@@ -295,6 +295,50 @@ p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution
                             const void* bias, int64_t n_null,
                             void* out, uint8_t* mask, void* stream);
 
+/* ------------------------------------------------------------------------
+ * p3d_projection_stats -- projection diagnostics (PR #38, commits adding the
+ * per-stage projection statistics and the cross-resolution agreement). The
+ * conditioning has no run-time failure mode: a wrong camera, grid or map
+ * layout still yields finite features. These figures expose it:
+ *   coverage             tokens inside the frame / tokens (a ratio: the
+ *                        cube's near corners leave the frame legitimately);
+ *   per-half mean, std   of the samples of each map (as fed to proj_linear:
+ *                        bf16-rounded for BF16 maps) over all tokens and
+ *                        that map's channels -- halves that describe the
+ *                        same points must share a scale;
+ *   cosine               per token, cos(S0, S1) between the two maps'
+ *                        samples (equal channel counts), averaged over the
+ *                        tokens where both are non-zero -- the halves, or a
+ *                        512 and a 1024 map of one image, must correlate.
+ * The same projection and sampling as p3d_proj_cond_ex; nothing is written
+ * but the sums below, from which the figures follow:
+ *   coverage = inside / tokens
+ *   mean_h   = sum[h] / (tokens * C_h)
+ *   std_h    = sqrt(sum_sq[h] / (tokens * C_h) - mean_h^2)
+ *   cosine   = cos_sum / cos_count
+ * Sums are binary64, accumulated with device atomics (their order, and so
+ * the last bits, varies between runs). With one map, or two of unequal
+ * channels, cos_sum = cos_count = 0.
+ *
+ *   coords .. batch      as p3d_project_points_ex
+ *   dtype, maps, n_maps  as p3d_proj_cond_ex (any channel split)
+ *   stats                DEVICE pointer to one p3d_proj_stats, 8-byte
+ *                        aligned; overwritten (zeroed on the stream first)
+ * --------------------------------------------------------------------- */
+typedef struct p3d_proj_stats {
+    double tokens;
+    double inside;
+    double sum[2];
+    double sum_sq[2];
+    double cos_sum;
+    double cos_count;
+} p3d_proj_stats;
+
+p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolution,
+                                p3d_points points, const p3d_camera* cams, int32_t batch,
+                                p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                p3d_proj_stats* stats, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,7 +6,7 @@ given are on the GPU, contiguous and of the declared dtype, and passes their
 device pointers plus torch's current HIP stream. All computation happens in
 the HIP kernels of libp3d; there is no fallback. If ``libp3d.so`` is missing
 the import fails loudly (build it with ``__graft_entry__.build()`` or
-``python -m pixel_aligned_image_amd.build``).
+``python pixel_aligned_image_amd/build.py``).
 
 torch is imported before libp3d is loaded so that the library binds to the
 same HIP runtime as torch (both carry the soname libamdhip64.so.7).
@@ -19,7 +19,8 @@ import torch
 __all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_version",
            "p3d_status_string", "p3d_last_error", "p3d_distance_from_fov", "p3d_make_camera",
            "p3d_project_points", "p3d_bilinear_sample", "p3d_proj_cond",
-           "p3d_requantize_coords", "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
+           "p3d_requantize_coords", "p3d_projection_stats", "stats_summary",
+           "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libp3d.so")
 
@@ -51,7 +52,7 @@ class P3DError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libp3d.so is not built at %s; run __graft_entry__.build() "
-                          "(or python -m pixel_aligned_image_amd.build)" % LIB_PATH)
+                          "(or python pixel_aligned_image_amd/build.py)" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     cam_p = ctypes.POINTER(p3d_camera)
@@ -78,6 +79,9 @@ def _load():
                                         vp, vp, vp, vp, vp]
     L.p3d_requantize_coords.restype = ctypes.c_int
     L.p3d_requantize_coords.argtypes = [vp, i64, i32, i32, ctypes.c_int, vp, vp]
+    L.p3d_projection_stats.restype = ctypes.c_int
+    L.p3d_projection_stats.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
+                                       ctypes.POINTER(p3d_map), i32, vp, vp]
     L.p3d_proj_cond_ex.restype = ctypes.c_int
     L.p3d_proj_cond_ex.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
                                    ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp, vp,
@@ -256,3 +260,45 @@ def p3d_proj_cond(coords, n, resolution, cams, feat, weight, out, bias=None, n_n
         maps[i].height, maps[i].width, maps[i].channels = f.shape[1], f.shape[2], f.shape[3]
     _check(lib.p3d_proj_cond_ex(c, n, int(resolution), POINTS[points], camarr, batch, dt, maps,
                                 len(feats), *common))
+
+
+STAT_FIELDS = ("tokens", "inside", "sum0", "sum1", "sum_sq0", "sum_sq1", "cos_sum",
+               "cos_count")        # the eight doubles of p3d_proj_stats, in order
+
+
+def p3d_projection_stats(coords, n, resolution, cams, feat, stats, points="cell_centres",
+                         stream=None):
+    """Enqueue p3d_projection_stats. feat: one [B, H, W, C] map or a list of
+    two; stats: float64 device tensor of 8 elements (p3d_proj_stats, in
+    STAT_FIELDS order), overwritten."""
+    camarr, batch = _cams(cams)
+    feats = list(feat) if isinstance(feat, (list, tuple)) else [feat]
+    dt = _DT.get(feats[0].dtype)
+    if dt is None or any(f.dtype != feats[0].dtype for f in feats):
+        raise TypeError("maps must all be float32 or all bfloat16")
+    maps = (p3d_map * len(feats))()
+    for i, f in enumerate(feats):
+        if f.dim() != 4 or f.shape[0] != batch:
+            raise ValueError("map %d must be [%d, H, W, C], got %s" % (i, batch, tuple(f.shape)))
+        maps[i].feat = _dev(f, "feat[%d]" % i)
+        maps[i].height, maps[i].width, maps[i].channels = f.shape[1], f.shape[2], f.shape[3]
+    n = int(n)
+    _check(lib.p3d_projection_stats(_dev(coords, "coords", torch.int32, (n, 4)), n,
+                                    int(resolution), POINTS[points], camarr, batch, dt, maps,
+                                    len(feats), _dev(stats, "stats", torch.float64, (8,)),
+                                    _stream(stream)))
+
+
+def stats_summary(raw, channels):
+    """Coverage, per-map mean and std, mean cosine from the raw sums (a dict
+    of STAT_FIELDS, e.g. dict(zip(STAT_FIELDS, stats.tolist())))."""
+    t = raw["tokens"]
+    out = {"coverage": raw["inside"] / t if t else None}
+    for h, c in enumerate(channels):
+        cnt = t * c
+        mean = raw["sum%d" % h] / cnt if cnt else None
+        out["mean%d" % h] = mean
+        out["std%d" % h] = (max(raw["sum_sq%d" % h] / cnt - mean * mean, 0.0) ** 0.5
+                            if cnt else None)
+    out["cosine"] = raw["cos_sum"] / raw["cos_count"] if raw["cos_count"] else None
+    return out

@@ -358,6 +358,59 @@ p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution
     return ok();
 }
 
+p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolution,
+                                p3d_points points, const p3d_camera* cams, int32_t batch,
+                                p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                p3d_proj_stats* stats, void* stream) {
+    const char* fn = "p3d_projection_stats";
+    CamTable tab;
+    p3d_status st = check_tokens(fn, coords, n, resolution, points, cams, batch, &tab);
+    if (st != P3D_OK) return st;
+    if (!maps || n_maps < 1 || n_maps > 2)
+        return fail(P3D_ERR_INVALID_ARG, "%s: maps must be a host array of 1 or 2 maps, got %d",
+                    fn, maps ? n_maps : 0);
+    if (dtype != P3D_F32 && dtype != P3D_BF16)
+        return fail(P3D_ERR_DTYPE, "%s: dtype must be F32 or BF16, got %d", fn, (int)dtype);
+    const int epv = dtype == P3D_BF16 ? 8 : 4;
+    for (int32_t m = 0; m < n_maps; ++m) {
+        char what[32];
+        snprintf(what, sizeof what, n_maps > 1 ? "maps[%d]" : "feature map", m);
+        st = check_map_size(fn, what, batch, maps[m].height, maps[m].width);
+        if (st != P3D_OK) return st;
+        if (maps[m].channels < 1 || maps[m].channels % epv)
+            return fail(P3D_ERR_UNSUPPORTED,
+                        "%s: %s channels must be a positive multiple of %d for %s, got %d", fn,
+                        what, epv, dtype_name(dtype), maps[m].channels);
+        if (!aligned(maps[m].feat, 16))
+            return fail(P3D_ERR_UNSUPPORTED, "%s: %s feat must be 16-byte aligned", fn, what);
+        if (n > 0 && !maps[m].feat)
+            return fail(P3D_ERR_INVALID_ARG, "%s: %s feat is NULL", fn, what);
+    }
+    if (!stats) return fail(P3D_ERR_INVALID_ARG, "%s: stats is NULL", fn);
+    if (!aligned(stats, 8))
+        return fail(P3D_ERR_UNSUPPORTED, "%s: stats must be 8-byte aligned", fn);
+    StatsArgs a{};
+    a.coords = coords;
+    a.n = n;
+    a.R = resolution;
+    a.points = (int32_t)points;
+    a.batch = batch;
+    a.feat0 = maps[0].feat;
+    a.H0 = maps[0].height;
+    a.W0 = maps[0].width;
+    a.C0 = maps[0].channels;
+    if (n_maps == 2) {
+        a.feat1 = maps[1].feat;
+        a.H1 = maps[1].height;
+        a.W1 = maps[1].width;
+        a.C1 = maps[1].channels;
+    }
+    a.stats = stats;
+    hipError_t e = launch_stats(a, dtype == P3D_BF16, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 p3d_status p3d_proj_cond(const int32_t* coords, int64_t n, int32_t resolution,
                          const p3d_camera* cams, int32_t batch, const void* feat,
                          p3d_dtype dtype, int32_t height, int32_t width, int32_t channels,

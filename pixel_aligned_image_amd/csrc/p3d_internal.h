@@ -199,7 +199,19 @@ struct RequantArgs {
     int32_t src_res, grid, mode;
 };
 
+struct StatsArgs {
+    const int32_t* coords;
+    int64_t n;
+    int32_t R, points, batch;
+    const void* feat0;
+    int32_t H0, W0, C0;
+    const void* feat1;            // or C1 == 0
+    int32_t H1, W1, C1;
+    p3d_proj_stats* stats;
+};
+
 hipError_t launch_project(const ProjectArgs& a, const CamTable& cams, hipStream_t s);
+hipError_t launch_stats(const StatsArgs& a, bool bf16, const CamTable& cams, hipStream_t s);
 hipError_t launch_requantize(const RequantArgs& a, hipStream_t s);
 hipError_t launch_sample(const SampleArgs& a, p3d_dtype in, p3d_dtype out, hipStream_t s);
 hipError_t launch_proj_cond(const ProjCondArgs& a, p3d_dtype dt, const CamTable& cams,

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(p3d):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     lib = ctypes.CDLL(p3d.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -234,3 +234,28 @@ def test_proj_cond_ex_validation(p3d):
     assert st == 1 and "resolution >= 2" in msg
     st, msg = _pcx(p3d, two, n=0, coords=NULL)
     assert st == 0, msg
+
+
+def test_projection_stats_validation(p3d):
+    cams = _cams(p3d, [(2.0, 2.0)])
+
+    def call(maps, stats=FAKE, n=16, dtype=1, n_maps=None):
+        arr = (p3d.p3d_map * max(1, len(maps)))()
+        for i, (f, h, w, c) in enumerate(maps):
+            arr[i].feat, arr[i].height, arr[i].width, arr[i].channels = f, h, w, c
+        st = p3d.lib.p3d_projection_stats(FAKE, n, 8, 0, cams, 1, dtype, arr,
+                                          len(maps) if n_maps is None else n_maps, stats, NULL)
+        return st, p3d.p3d_last_error()
+
+    st, msg = call([(FAKE, 4, 4, 64)], stats=NULL)
+    assert st == 1 and "stats is NULL" in msg
+    st, msg = call([(FAKE, 4, 4, 64)], stats=FAKE + 4)
+    assert st == 4 and "8-byte aligned" in msg
+    st, msg = call([(FAKE, 4, 4, 60)])
+    assert st == 4 and "multiple of 8" in msg
+    st, msg = call([(FAKE, 4, 4, 64), (FAKE, 4, 4, 64)], n_maps=3)
+    assert st == 1 and "1 or 2 maps" in msg
+    st, msg = call([(FAKE, 4, 4, 64)], dtype=4)
+    assert st == 3 and "dtype" in msg
+    st, msg = call([(NULL, 4, 4, 64)])
+    assert st == 1 and "feat is NULL" in msg

@@ -24,7 +24,8 @@ Prints ONE JSON line. Fields beyond the common ones:
   extra          the adjacent parts, each on its own workload with its own
                  roofline: cascade requantization (HBM), the fused kernel on
                  grid-node points after requantization (MFMA), the fused
-                 kernel over two concatenated maps (MFMA).
+                 kernel over two concatenated maps (MFMA), the projection
+                 diagnostics over those two maps (HBM gather + reduction).
 """
 import argparse
 import hashlib
@@ -210,6 +211,30 @@ def run_extra(p3d, synth, stream, reps, lead_step):
         "flops_per_launch": flops, "achieved": flops / (two_ms * 1e-3) / 1e12,
         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
         "frac": flops / (two_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    # ---- diagnostics over the same two maps: coverage, per-map mean/std,
+    # cosine between the maps' samples
+    stats = torch.empty(8, dtype=torch.float64, device="cuda")
+    diag = lambda: p3d.p3d_projection_stats(coords, n, w.resolution, camarr, maps, stats)
+    for _ in range(reps):
+        diag()
+    diag_ms = time_events(diag, reps, stream)
+    raw = dict(zip(p3d.STAT_FIELDS, stats.cpu().numpy().tolist()))
+    # algorithmic bytes: coords + each map's unique corner rows + the sums
+    bidx = synth.coords(w)[:, 0].copy()
+    uniq = 0
+    for m in maps:
+        pix = torch.empty((n, 2), dtype=torch.int32, device="cuda")
+        p3d.p3d_project_points(coords, n, w.resolution, camarr, m.shape[1], m.shape[2],
+                               pixel=pix)
+        uniq += unique_corner_rows(pix.cpu().numpy(), bidx, m.shape[1], m.shape[2]) * \
+            m.shape[3] * 2
+    dbytes = 16 * n + uniq + 64
+    out["diagnostics"] = {
+        "workload": w.name, "kernel": "stats_kernel<true>", "tokens": n, "mean_ms": diag_ms,
+        "bound": "hbm", "bytes_per_launch": dbytes,
+        "achieved": dbytes / (diag_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": dbytes / (diag_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "figures": p3d.stats_summary(raw, [m.shape[3] for m in maps])}
     del maps, weight, y, coords
     torch.cuda.empty_cache()
     return out

@@ -3,16 +3,18 @@
 // cross-resolution agreement): coverage, per-map sums and sums of squares of
 // the samples, and the per-token cosine between two maps' samples.
 //
-// An HBM-bound gather with a reduction instead of a store. A wave takes 64
-// tokens at a time: each lane projects one of them, then the wave walks the
-// 64 tokens, broadcasting each token's corner metadata from its lane
+// An HBM-bound gather with a reduction instead of a store. A wave takes TPW
+// tokens at a time: lanes 0..TPW-1 project one each, then the wave walks the
+// TPW tokens, broadcasting each token's corner metadata from its lane
 // (readlane) and gathering its corner rows with the lanes spread over the
 // channels (16-byte vectors, 64 lanes = 1 KB of a row per instruction). Map 0
 // and map 1 vectors at the same channel offset sit in the same lane, so the
 // cosine's dot product and norms need no shuffles until the per-token wave
 // reduction. Samples are blended and rounded exactly as the fused kernel
-// feeds them to proj_linear; sums are binary64 and leave the wave through one
-// device atomic per figure.
+// feeds them to proj_linear; sums are binary64, reduced over the workgroup
+// in LDS and added to the result with one device atomic per figure per
+// workgroup (atomics on eight addresses serialise, so their count is kept to
+// a few thousand).
 #include "p3d_internal.h"
 
 namespace p3d {
@@ -20,6 +22,11 @@ namespace p3d {
 namespace {
 
 constexpr int kThreads = 256;
+// Tokens per wave and step. Each token keeps a whole wave's loads in flight
+// (16 per lane for two 1024-channel bf16 maps), so concurrency comes from the
+// number of waves: 16 tokens per wave gives 100k tokens ~6000 waves.
+constexpr int TPW = 16;
+constexpr int kMaxBlocks = 1024;   // 16 waves per CU; atomics: 8 per block
 
 // Corner metadata of token t on an H x W map (top-left row, 0/1 steps right
 // and down, fractions); the same construction as the fused kernel's.
@@ -110,12 +117,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a, CamTable c
     double s0 = 0.0, q0 = 0.0, s1 = 0.0, q1 = 0.0;   // per lane
     double cos_sum = 0.0, cos_cnt = 0.0, inside = 0.0, tokens = 0.0;   // wave-uniform
 
-    for (int64_t base = wave * 64; base < a.n; base += waves * 64) {
-        // ---- lane j projects token base + j
+    for (int64_t base = wave * TPW; base < a.n; base += waves * TPW) {
+        // ---- lane j < TPW projects token base + j
         const int64_t t = base + lane;
         Meta m0{0, 0, 0.0f, 0.0f}, m1{0, 0, 0.0f, 0.0f};
         int in = 0;
-        if (t < a.n) {
+        if (lane < TPW && t < a.n) {
             int32_t b, x, y, z;
             token_cell(a.coords, t, a.R, b, x, y, z);
             const Projected p = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
@@ -123,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a, CamTable c
             if (two) m1 = meta_of(p, a.H1, a.W1);
             in = p.mask;
         }
-        const int64_t cnt = a.n - base < 64 ? a.n - base : 64;
+        const int64_t cnt = a.n - base < TPW ? a.n - base : TPW;
         inside += (double)__builtin_popcountll(__ballot(in));
         tokens += (double)cnt;
         // ---- the wave walks its tokens
@@ -180,24 +187,20 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a, CamTable c
             }
         }
     }
-    // ---- one atomic per figure per wave
-    s0 = wave_sum(s0);
-    q0 = wave_sum(q0);
-    s1 = wave_sum(s1);
-    q1 = wave_sum(q1);
-    if (lane == 0 && tokens > 0.0) {
-        unsafeAtomicAdd(&a.stats->tokens, tokens);
-        unsafeAtomicAdd(&a.stats->inside, inside);
-        unsafeAtomicAdd(&a.stats->sum[0], s0);
-        unsafeAtomicAdd(&a.stats->sum_sq[0], q0);
-        if (two) {
-            unsafeAtomicAdd(&a.stats->sum[1], s1);
-            unsafeAtomicAdd(&a.stats->sum_sq[1], q1);
-        }
-        if (cosine) {
-            unsafeAtomicAdd(&a.stats->cos_sum, cos_sum);
-            unsafeAtomicAdd(&a.stats->cos_count, cos_cnt);
-        }
+    // ---- workgroup reduction, then one atomic per figure
+    __shared__ double part[kThreads / 64][8];
+    const double fig[8] = {tokens, inside, wave_sum(s0), wave_sum(s1), wave_sum(q0),
+                           wave_sum(q1), cos_sum, cos_cnt};
+    if (lane == 0)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) part[threadIdx.x >> 6][k] = fig[k];
+    __syncthreads();
+    if (threadIdx.x < 8) {
+        double v = 0.0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) v += part[w][threadIdx.x];
+        // figures a launch does not produce stay exactly 0 (zeroed first)
+        if (v != 0.0) unsafeAtomicAdd(reinterpret_cast<double*>(a.stats) + threadIdx.x, v);
     }
 }
 
@@ -212,10 +215,11 @@ hipError_t launch_stats(const StatsArgs& a, bool bf16, const CamTable& cams, hip
                                        dim3(64), params, 0, s);
         if (e != hipSuccess || a.n == 0) return e;
     }
-    // enough waves to keep every CU's loads in flight; each wave takes 64
-    // tokens at a time
-    const int64_t blocks_needed = (a.n + 64 * (kThreads / 64) - 1) / (64 * (kThreads / 64));
-    int64_t blocks = blocks_needed < 2048 ? blocks_needed : 2048;
+    // one step of TPW tokens per wave where the grid allows; larger inputs
+    // loop (grid-stride)
+    const int64_t per_block = (int64_t)TPW * (kThreads / 64);
+    const int64_t blocks_needed = (a.n + per_block - 1) / per_block;
+    int64_t blocks = blocks_needed < kMaxBlocks ? blocks_needed : kMaxBlocks;
     CamTable tab = cams;
     void* params[] = {&args, &tab};
     const void* fn = bf16 ? reinterpret_cast<const void*>(&stats_kernel<true>)

@@ -78,6 +78,14 @@ def _declare(lib):
     lib.orc_projection_stats.argtypes = [_i32p, _i64, _i32, _i32, _f32p, _f32p, _i32, _i32,
                                          ctypes.POINTER(_vp), _i32p, _i32p, _i32p, _i32,
                                          _f64p, _f64p]
+    lib.orc_proj_sample_rows.restype = None
+    lib.orc_proj_sample_rows.argtypes = [_i32p, _i64, _i32, _i32, _f32p, _f32p, _i32, _i32,
+                                         ctypes.POINTER(_vp), _i32p, _i32p, _i32p, _i32,
+                                         _i64p, _i64, _f64p, _u8p]
+    lib.orc_linear_grouped.restype = None
+    lib.orc_linear_grouped.argtypes = [_f64p, _i64, _i32, _i32, ctypes.POINTER(_vp),
+                                       ctypes.POINTER(_vp), _i32, _i32,
+                                       ctypes.POINTER(_vp), _f64p]
     return lib
 
 
@@ -243,6 +251,63 @@ class Oracle:
                                       _ptr(Hs, _i32p), _ptr(Ws, _i32p), _ptr(Cs, _i32p),
                                       int(is_bf16), _ptr(out, _f64p), _ptr(S, _f64p))
         return dict(zip(STAT_FIELDS, out.tolist()))
+
+    def proj_sample_rows(self, coords, n, resolution, focal, dist, feat, rows,
+                         points="cell_centres"):
+        """The samples S of tokens `rows` as the whole path forms them before
+        proj_linear: float64 [len(rows), sum C] (bf16-rounded values for bf16
+        maps) and the mask. feat: one map or a list of two."""
+        feats = [np.ascontiguousarray(f) for f in (feat if isinstance(feat, (list, tuple))
+                                                    else [feat])]
+        is_bf16 = feats[0].dtype == np.uint16
+        B = feats[0].shape[0]
+        Hs = np.array([f.shape[1] for f in feats], np.int32)
+        Ws = np.array([f.shape[2] for f in feats], np.int32)
+        Cs = np.array([f.shape[3] for f in feats], np.int32)
+        if coords is not None:
+            coords = np.ascontiguousarray(coords, dtype=np.int32)
+            assert coords.shape == (n, 4)
+        focal = np.ascontiguousarray(focal, dtype=np.float32).reshape(-1)
+        dist = np.ascontiguousarray(dist, dtype=np.float32).reshape(-1)
+        rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        assert rows.size == 0 or (rows.min() >= 0 and rows.max() < n)
+        S = np.empty((rows.size, int(Cs.sum())), np.float64)
+        mask = np.empty(rows.size, np.uint8)
+        fp = (_vp * len(feats))(*[f.ctypes.data for f in feats])
+        self.lib.orc_proj_sample_rows(_ptr(coords, _i32p), n, resolution, POINTS[points],
+                                      _ptr(focal, _f32p), _ptr(dist, _f32p), B, len(feats), fp,
+                                      _ptr(Hs, _i32p), _ptr(Ws, _i32p), _ptr(Cs, _i32p),
+                                      int(is_bf16), _ptr(rows, _i64p), rows.size,
+                                      _ptr(S, _f64p), _ptr(mask, _u8p))
+        return S, mask
+
+    def linear_grouped(self, S, weights, biases=None, residuals=None):
+        """Per block g: Y_g = S @ W_g^T + b_g (+ residual_g), float64
+        [G, rows, D]. weights: list of [D, K] (f32 or bf16 bits); biases:
+        list (entries may be None) or None; residuals: list of float64
+        [rows, D] (entries may be None) or None."""
+        S = np.ascontiguousarray(S, dtype=np.float64)
+        ws = [np.ascontiguousarray(w) for w in weights]
+        G = len(ws)
+        D, K = ws[0].shape
+        assert S.shape[1] == K and all(w.shape == (D, K) and w.dtype == ws[0].dtype for w in ws)
+        is_bf16 = ws[0].dtype == np.uint16
+        bs = None
+        if biases is not None:
+            bs = [None if b is None else np.ascontiguousarray(b) for b in biases]
+            assert all(b is None or (b.shape == (D,) and b.dtype == ws[0].dtype) for b in bs)
+        rs = None
+        if residuals is not None:
+            rs = [None if r is None else np.ascontiguousarray(r, dtype=np.float64)
+                  for r in residuals]
+            assert all(r is None or r.shape == (S.shape[0], D) for r in rs)
+        Y = np.empty((G, S.shape[0], D), np.float64)
+        wp = (_vp * G)(*[w.ctypes.data for w in ws])
+        bp = None if bs is None else (_vp * G)(*[None if b is None else b.ctypes.data for b in bs])
+        rp = None if rs is None else (_vp * G)(*[None if r is None else r.ctypes.data for r in rs])
+        self.lib.orc_linear_grouped(_ptr(S, _f64p), S.shape[0], K, G, wp, bp, int(is_bf16), D,
+                                    rp, _ptr(Y, _f64p))
+        return Y
 
     def proj_cond_rows(self, coords, n, resolution, focal, dist, feat, weight, bias,
                        n_null, rows, points="cell_centres"):

@@ -30,6 +30,10 @@
  *   [PR38-diag] same PR, commits adding projection diagnostics (coverage;
  *               per-half mean/std and the halves' cosine similarity) and the
  *               cross-resolution agreement of samples at the same points.
+ *   [PR38-proj] same PR, commit adding proj mode to the DiT: every block
+ *               carries its own proj_linear whose output is added into that
+ *               block's residual, over a projection that is fixed for the
+ *               stage.
  *
  * Precision. Whatever decides an integer (pixel index, in-image mask) is
  * computed in binary32 with one IEEE rounding per operation, in the order
@@ -46,6 +50,9 @@
  *     exactly in integers (no ties occur at the pages' sizes);
  *   - two maps: the sample is map 0's channels followed by map 1's, each map
  *     sampled at the same normalised point on its own height and width;
+ *   - per-block linears: the stage's samples S are gathered once and every
+ *     block applies Y_g = W_g S + b_g; with a residual, the block's running
+ *     value R_g becomes round(R_g + W_g S + b_g), one rounding;
  *   - diagnostics: coverage = tokens with mask 1 / tokens; the per-half
  *     mean/std run over every token and channel of that half's samples as
  *     fed to proj_linear (bf16-rounded for bf16 maps); the cosine is taken
@@ -519,5 +526,57 @@ void orc_projection_stats(const int32_t* coords, int64_t n, int32_t R, int32_t p
                 out[7] += 1.0;
             }
         }
+    }
+}
+
+/* ------------------------------------------------------ gather once ---
+ * The samples S of tokens rows[k] (the whole path before proj_linear):
+ * S_out [nrows, sum Cs] binary64, bf16-rounded values for bf16 maps. */
+void orc_proj_sample_rows(const int32_t* coords, int64_t n, int32_t R, int32_t points,
+                          const float* focal, const float* dist, int32_t batch,
+                          int32_t n_maps, const void* const* feats, const int32_t* Hs,
+                          const int32_t* Ws, const int32_t* Cs, int32_t is_bf16,
+                          const int64_t* rows, int64_t nrows, double* S_out, uint8_t* mask)
+{
+    int32_t C = 0;
+    for (int32_t m = 0; m < n_maps; ++m) C += Cs[m];
+    (void)n;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t k = 0; k < nrows; ++k) {
+        int32_t cell[4];
+        token_cell(coords, rows[k], R, cell);
+        float gx, gy, dep;
+        uint8_t msk;
+        int32_t b;
+        project_one(cell, R, points, focal, dist, batch, &gx, &gy, &dep, &msk, &b);
+        double* s = S_out + k * (int64_t)C;
+        int32_t off = 0;
+        for (int32_t m = 0; m < n_maps; ++m) {
+            sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy,
+                       S_out + k * (int64_t)C + off);
+            off += Cs[m];
+        }
+        if (is_bf16)
+            for (int32_t c = 0; c < C; ++c) s[c] = (double)orc_bf16_to_f32(orc_f64_to_bf16(s[c]));
+        if (mask) mask[k] = msk;
+    }
+}
+
+/* ------------------------------------------------- per-block linears ---
+ * [PR38-proj]: for each block g, Y_g[k][d] = sum_c W_g[d][c] S[k][c] + b_g[d]
+ * over the given S rows (binary64); with a residual (res_g != NULL, the
+ * block's running values at the same rows, binary64), the result is
+ * res_g + that. weights / biases: arrays of G parameter pointers (bias
+ * entries may be NULL), each [D][K] / [D], f32 or bf16 bits.
+ * Y [G][nrows][D]. */
+void orc_linear_grouped(const double* S, int64_t nrows, int32_t K, int32_t G,
+                        const void* const* weights, const void* const* biases,
+                        int32_t is_bf16, int32_t D, const double* const* res, double* Y)
+{
+    for (int32_t g = 0; g < G; ++g) {
+        double* y = Y + (int64_t)g * nrows * D;
+        orc_linear(S, nrows, K, weights[g], biases ? biases[g] : NULL, is_bf16, D, y);
+        if (res && res[g])
+            for (int64_t i = 0; i < nrows * (int64_t)D; ++i) y[i] += res[g][i];
     }
 }

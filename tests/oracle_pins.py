@@ -668,5 +668,74 @@ def pin_stats_zero_map(o):
     assert abs(st["sum1"] - 16) < 1e-6
 
 
+# ------------------------------------------------- gather once, per-block ---
+def pin_proj_sample_torch(o):
+    """The gathered samples S (one or two maps, bf16-rounded for bf16 maps)
+    equal torch grid_sample of each map at the projected points, map 0's
+    channels first."""
+    rng = np.random.default_rng(41)
+    R, n = 10, 120
+    coords = np.concatenate([rng.integers(0, 2, (n, 1)), rng.integers(-2, R + 2, (n, 3))],
+                            1).astype(np.int32)
+    fo, do = o.cameras([38.0, 52.0], [None, 1.3])
+    m0 = rng.standard_normal((2, 6, 11, 8)).astype(np.float32)
+    m1 = rng.standard_normal((2, 17, 9, 24)).astype(np.float32)
+    for bf16 in (False, True):
+        feats = [o.f32_to_bf16(m0), o.f32_to_bf16(m1)] if bf16 else [m0, m1]
+        for points in ("cell_centres", "grid_nodes"):
+            S, mask = o.proj_sample_rows(coords, n, R, fo, do, feats, np.arange(n),
+                                         points=points)
+            (T0, T1), tm = _torch_samples(o, feats, coords, n, R, fo, do, points, bf16)
+            T = np.concatenate([T0, T1], 1)
+            # scale: the interpolated magnitude sum_k w_k |F_k| (torch, on |map|)
+            (A0, A1), _ = _torch_samples(o, [np.abs(m0), np.abs(m1)], coords, n, R, fo, do,
+                                         points, False)
+            mag = np.concatenate([A0, A1], 1)
+            assert np.array_equal(mask, tm)
+            tol = 2.0 ** -8 if bf16 else 1e-6
+            assert np.all(np.abs(S - T) <= tol * (mag + np.abs(T)) + 1e-30), (bf16, points)
+
+
+def pin_linear_grouped_numpy(o):
+    """Per block g: numpy float64 S @ W_g^T + b_g (+ the block's residual)."""
+    rng = np.random.default_rng(43)
+    S = rng.standard_normal((33, 24))
+    for bf16 in (False, True):
+        ws = [rng.standard_normal((16, 24)).astype(np.float32) for _ in range(3)]
+        bs = [rng.standard_normal(16).astype(np.float32), None, rng.standard_normal(16).astype(
+            np.float32)]
+        if bf16:
+            ws = [o.f32_to_bf16(w) for w in ws]
+            bs = [None if b is None else o.f32_to_bf16(b) for b in bs]
+        wv = [(o.bf16_to_f32(w) if bf16 else w).astype(np.float64) for w in ws]
+        bv = [None if b is None else (o.bf16_to_f32(b) if bf16 else b).astype(np.float64)
+              for b in bs]
+        res = [rng.standard_normal((33, 16)), None, rng.standard_normal((33, 16))]
+        Y = o.linear_grouped(S, ws, bs, res)
+        for g in range(3):
+            want = S @ wv[g].T + (0 if bv[g] is None else bv[g]) + (0 if res[g] is None
+                                                                  else res[g])
+            assert np.max(np.abs(Y[g] - want)) <= 1e-12 * np.abs(want).max(), (bf16, g)
+        Y2 = o.linear_grouped(S, ws)
+        for g in range(3):
+            assert np.max(np.abs(Y2[g] - S @ wv[g].T)) <= 1e-12 * np.abs(Y2[g]).max()
+
+
+def pin_grouped_block_is_the_path(o):
+    """Gather once, then block g's linear without residual equals the whole
+    path run with that block's weight and bias."""
+    rng = np.random.default_rng(47)
+    feat = o.f32_to_bf16(rng.standard_normal((1, 12, 12, 16)).astype(np.float32))
+    coords = np.concatenate([np.zeros((40, 1)), rng.integers(0, 8, (40, 3))], 1).astype(np.int32)
+    f, d = o.camera(40.0, 1.8)
+    ws = [o.f32_to_bf16(rng.standard_normal((8, 16)).astype(np.float32)) for _ in range(2)]
+    bs = [o.f32_to_bf16(rng.standard_normal(8).astype(np.float32)) for _ in range(2)]
+    S, _ = o.proj_sample_rows(coords, 40, 8, [f], [d], feat, np.arange(40))
+    Y = o.linear_grouped(S, ws, bs)
+    for g in range(2):
+        want, _ = o.proj_cond_rows(coords, 40, 8, [f], [d], feat, ws[g], bs[g], 0, np.arange(40))
+        assert np.max(np.abs(Y[g] - want)) <= 1e-12 * np.abs(want).max()
+
+
 ALL_PINS = {name[len("pin_"):]: fn for name, fn in sorted(globals().items())
             if name.startswith("pin_") and callable(fn)}

@@ -73,6 +73,16 @@ MUTANTS = [
     ("two_maps_order_reversed",
      "sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, s + off);",
      "sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, s + (C - off - Cs[m]));"),
+    ("grouped_bias_of_block_0",
+     "orc_linear(S, nrows, K, weights[g], biases ? biases[g] : NULL, is_bf16, D, y);",
+     "orc_linear(S, nrows, K, weights[g], biases ? biases[0] : NULL, is_bf16, D, y);"),
+    ("grouped_weight_of_block_0",
+     "orc_linear(S, nrows, K, weights[g], biases ? biases[g] : NULL, is_bf16, D, y);",
+     "orc_linear(S, nrows, K, weights[0], biases ? biases[g] : NULL, is_bf16, D, y);"),
+    ("grouped_residual_dropped", "y[i] += res[g][i];", "y[i] += 0.0 * res[g][i];"),
+    ("sample_rows_map1_offset_dropped",
+     "                       S_out + k * (int64_t)C + off);",
+     "                       S_out + k * (int64_t)C);"),
     ("stats_maps_share_first_size",
      "sample_one(feats[m], is_bf16, b, Hs[m], Ws[m], Cs[m], gx, gy, &s[off]);",
      "sample_one(feats[m], is_bf16, b, Hs[0], Ws[0], Cs[m], gx, gy, &s[off]);"),

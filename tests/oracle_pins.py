@@ -692,7 +692,9 @@ def pin_proj_sample_torch(o):
                                          points, False)
             mag = np.concatenate([A0, A1], 1)
             assert np.array_equal(mask, tm)
-            tol = 2.0 ** -8 if bf16 else 1e-6
+            # fp32: the sampling tolerance (torch forms the source index in
+            # another operation order); bf16: one rounding of the sample
+            tol = 2.0 ** -8 if bf16 else 1e-5
             assert np.all(np.abs(S - T) <= tol * (mag + np.abs(T)) + 1e-30), (bf16, points)
 
 

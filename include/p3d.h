@@ -33,7 +33,10 @@
  *       floors u * grid;
  *     commit adding the NAF upsampler -- the shape and texture stages sample
  *       the DINOv3 map and its NAF-upsampled version (another size) at the
- *       same points and concatenate them, hence proj_in_channels = 2048.
+ *       same points and concatenate them, hence proj_in_channels = 2048;
+ *     commit adding proj mode to the DiT -- every block has its own
+ *       proj_linear whose output is added into that block's residual, over a
+ *       projection that stays fixed for the stage.
  *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers owned by the caller. The library
@@ -87,6 +90,8 @@ typedef struct p3d_camera {
 /* Largest batch (number of images / cameras) one call accepts. Cameras
  * travel to the device inside the kernel arguments. */
 #define P3D_MAX_BATCH 256
+/* Most blocks one p3d_proj_linear_grouped call applies. */
+#define P3D_MAX_GROUPS 64
 
 /* ------------------------------------------------------------------------
  * Host helpers (no device work, no stream).
@@ -338,6 +343,43 @@ p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolu
                                 p3d_points points, const p3d_camera* cams, int32_t batch,
                                 p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
                                 p3d_proj_stats* stats, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Gather once per stage, apply every block's proj_linear every step (PR #38,
+ * proj-mode commit): the samples do not change within a stage, so they are
+ * gathered once (p3d_proj_sample) and each denoising step runs all blocks'
+ * linears over them in one launch (p3d_proj_linear_grouped).
+ *
+ * p3d_proj_sample -- the gather half of p3d_proj_cond_ex: project every token
+ * and write its samples S[n, C0 + C1] (map 0's channels, then map 1's) in
+ * `dtype`; BF16 samples are rounded to nearest even exactly as the fused path
+ * rounds them before proj_linear. mask [n] uint8 or NULL.
+ *   coords .. maps, n_maps   as p3d_proj_cond_ex (two maps: maps[0].channels
+ *                            need only be a multiple of 8 (BF16) / 4 (F32))
+ *   S        [n, C0 + C1] device, 16-byte aligned
+ * --------------------------------------------------------------------- */
+p3d_status p3d_proj_sample(const int32_t* coords, int64_t n, int32_t resolution,
+                           p3d_points points, const p3d_camera* cams, int32_t batch,
+                           p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                           void* S, uint8_t* mask, void* stream);
+
+/* p3d_proj_linear_grouped -- for each block g in [0, groups):
+ *   accumulate == 0:  outs[g][t] = W_g S[t] + b_g
+ *   accumulate != 0:  outs[g][t] = outs[g][t] + W_g S[t] + b_g
+ * with binary32 accumulation on the matrix cores and one rounding to bf16 at
+ * the end (the residual add included). BF16 only.
+ *   S        [n, K] bf16 device (from p3d_proj_sample), 16-byte aligned
+ *   weights  HOST array [groups] of device [out_dim, K] bf16 pointers
+ *   biases   HOST array [groups] of device [out_dim] bf16 pointers (entries
+ *            may be NULL), or NULL for none
+ *   outs     HOST array [groups] of device [n, out_dim] bf16 pointers
+ *            (distinct, not overlapping S)
+ *   1 <= groups <= P3D_MAX_GROUPS; K % 8 == 0; out_dim % 8 == 0
+ * --------------------------------------------------------------------- */
+p3d_status p3d_proj_linear_grouped(const void* S, int64_t n, int32_t K, p3d_dtype dtype,
+                                   int32_t groups, const void* const* weights,
+                                   const void* const* biases, int32_t out_dim,
+                                   void* const* outs, int32_t accumulate, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,7 @@ __all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_versi
            "p3d_status_string", "p3d_last_error", "p3d_distance_from_fov", "p3d_make_camera",
            "p3d_project_points", "p3d_bilinear_sample", "p3d_proj_cond",
            "p3d_requantize_coords", "p3d_projection_stats", "stats_summary",
+           "p3d_proj_sample", "p3d_proj_linear_grouped", "P3D_MAX_GROUPS",
            "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libp3d.so")
@@ -27,6 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libp3d.so")
 P3D_OK, P3D_ERR_INVALID_ARG, P3D_ERR_SHAPE, P3D_ERR_DTYPE, P3D_ERR_UNSUPPORTED, P3D_ERR_HIP = range(6)
 P3D_F32, P3D_BF16 = 0, 1
 P3D_MAX_BATCH = 256
+P3D_MAX_GROUPS = 64
 POINTS = {"cell_centres": 0, "grid_nodes": 1}          # p3d_points
 REQUANT = {"round_nodes": 0, "floor_cells": 1}          # p3d_requant
 
@@ -82,6 +84,13 @@ def _load():
     L.p3d_projection_stats.restype = ctypes.c_int
     L.p3d_projection_stats.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
                                        ctypes.POINTER(p3d_map), i32, vp, vp]
+    L.p3d_proj_sample.restype = ctypes.c_int
+    L.p3d_proj_sample.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
+                                  ctypes.POINTER(p3d_map), i32, vp, vp, vp]
+    L.p3d_proj_linear_grouped.restype = ctypes.c_int
+    L.p3d_proj_linear_grouped.argtypes = [vp, i64, i32, ctypes.c_int, i32,
+                                          ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
+                                          ctypes.POINTER(vp), i32, vp]
     L.p3d_proj_cond_ex.restype = ctypes.c_int
     L.p3d_proj_cond_ex.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
                                    ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp, vp,
@@ -302,3 +311,54 @@ def stats_summary(raw, channels):
                             if cnt else None)
     out["cosine"] = raw["cos_sum"] / raw["cos_count"] if raw["cos_count"] else None
     return out
+
+
+def _maps(feat, batch):
+    feats = list(feat) if isinstance(feat, (list, tuple)) else [feat]
+    dt = _DT.get(feats[0].dtype)
+    if dt is None or any(f.dtype != feats[0].dtype for f in feats):
+        raise TypeError("maps must all be float32 or all bfloat16")
+    maps = (p3d_map * len(feats))()
+    for i, f in enumerate(feats):
+        if f.dim() != 4 or f.shape[0] != batch:
+            raise ValueError("map %d must be [%d, H, W, C], got %s" % (i, batch, tuple(f.shape)))
+        maps[i].feat = _dev(f, "feat[%d]" % i)
+        maps[i].height, maps[i].width, maps[i].channels = f.shape[1], f.shape[2], f.shape[3]
+    return feats, maps, dt
+
+
+def p3d_proj_sample(coords, n, resolution, cams, feat, S, mask=None, points="cell_centres",
+                    stream=None):
+    """Enqueue p3d_proj_sample: S [n, sum C] (dtype of the maps) receives the
+    samples the fused path would feed to proj_linear; feat is one map or a
+    list of two."""
+    camarr, batch = _cams(cams)
+    feats, maps, dt = _maps(feat, batch)
+    n = int(n)
+    K = sum(f.shape[3] for f in feats)
+    _check(lib.p3d_proj_sample(_dev(coords, "coords", torch.int32, (n, 4)), n, int(resolution),
+                               POINTS[points], camarr, batch, dt, maps, len(feats),
+                               _dev(S, "S", feats[0].dtype, (n, K)),
+                               _dev(mask, "mask", torch.uint8, (n,)), _stream(stream)))
+
+
+def p3d_proj_linear_grouped(S, weights, outs, biases=None, accumulate=False, stream=None):
+    """Enqueue p3d_proj_linear_grouped: for every block g, outs[g] = W_g S +
+    b_g (accumulate: outs[g] += ...). S: bf16 [n, K]; weights: list of bf16
+    [D, K]; biases: list (entries may be None) or None; outs: list of bf16
+    [n, D]."""
+    n, K = S.shape
+    G = len(weights)
+    D = weights[0].shape[0]
+    if len(outs) != G or (biases is not None and len(biases) != G):
+        raise ValueError("weights, biases and outs need one entry per block")
+    wp = (ctypes.c_void_p * G)(*[_dev(w, "weights[%d]" % g, torch.bfloat16, (D, K))
+                                 for g, w in enumerate(weights)])
+    op = (ctypes.c_void_p * G)(*[_dev(o, "outs[%d]" % g, torch.bfloat16, (n, D))
+                                 for g, o in enumerate(outs)])
+    bp = None
+    if biases is not None:
+        bp = (ctypes.c_void_p * G)(*[_dev(b, "biases[%d]" % g, torch.bfloat16, (D,))
+                                     for g, b in enumerate(biases)])
+    _check(lib.p3d_proj_linear_grouped(_dev(S, "S", torch.bfloat16, (n, K)), n, K, P3D_BF16, G,
+                                       wp, bp, D, op, int(bool(accumulate)), _stream(stream)))

@@ -250,8 +250,20 @@ p3d_status p3d_bilinear_sample(const void* feat, p3d_dtype feat_dtype, int32_t b
     if (n == 0) return ok();
     if (!feat || !grid || !out)
         return fail(P3D_ERR_INVALID_ARG, "%s: feat, grid and out must be non-NULL", fn);
-    SampleArgs a{feat, batch, height, width, channels, grid, batch_index, n, out};
-    hipError_t e = launch_sample(a, feat_dtype, out_dtype, static_cast<hipStream_t>(stream));
+    SampleArgs a{};
+    a.feat = feat;
+    a.batch = batch;
+    a.H = height;
+    a.W = width;
+    a.C = channels;
+    a.grid = grid;
+    a.bidx = batch_index;
+    a.n = n;
+    a.out = out;
+    a.out_stride = channels;
+    static const CamTable no_cams{};
+    hipError_t e = launch_sample(a, feat_dtype, out_dtype, no_cams,
+                                 static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }
@@ -407,6 +419,114 @@ p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolu
     }
     a.stats = stats;
     hipError_t e = launch_stats(a, dtype == P3D_BF16, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+p3d_status p3d_proj_sample(const int32_t* coords, int64_t n, int32_t resolution,
+                           p3d_points points, const p3d_camera* cams, int32_t batch,
+                           p3d_dtype dtype, const p3d_map* maps, int32_t n_maps, void* S,
+                           uint8_t* mask, void* stream) {
+    const char* fn = "p3d_proj_sample";
+    CamTable tab;
+    p3d_status st = check_tokens(fn, coords, n, resolution, points, cams, batch, &tab);
+    if (st != P3D_OK) return st;
+    if (!maps || n_maps < 1 || n_maps > 2)
+        return fail(P3D_ERR_INVALID_ARG, "%s: maps must be a host array of 1 or 2 maps, got %d",
+                    fn, maps ? n_maps : 0);
+    if (dtype != P3D_F32 && dtype != P3D_BF16)
+        return fail(P3D_ERR_DTYPE, "%s: dtype must be F32 or BF16, got %d", fn, (int)dtype);
+    const int epv = dtype == P3D_BF16 ? 8 : 4;
+    int64_t channels = 0;
+    for (int32_t m = 0; m < n_maps; ++m) {
+        char what[32];
+        snprintf(what, sizeof what, n_maps > 1 ? "maps[%d]" : "feature map", m);
+        st = check_map_size(fn, what, batch, maps[m].height, maps[m].width);
+        if (st != P3D_OK) return st;
+        if (maps[m].channels < 1 || maps[m].channels % epv)
+            return fail(P3D_ERR_UNSUPPORTED,
+                        "%s: %s channels must be a positive multiple of %d for %s, got %d", fn,
+                        what, epv, dtype_name(dtype), maps[m].channels);
+        if (!aligned(maps[m].feat, 16))
+            return fail(P3D_ERR_UNSUPPORTED, "%s: %s feat must be 16-byte aligned", fn, what);
+        if (n > 0 && !maps[m].feat)
+            return fail(P3D_ERR_INVALID_ARG, "%s: %s feat is NULL", fn, what);
+        channels += maps[m].channels;
+    }
+    if (!aligned(S, 16)) return fail(P3D_ERR_UNSUPPORTED, "%s: S must be 16-byte aligned", fn);
+    if (n == 0) return ok();
+    if (!S) return fail(P3D_ERR_INVALID_ARG, "%s: S is NULL", fn);
+    int32_t col = 0;
+    for (int32_t m = 0; m < n_maps; ++m) {
+        SampleArgs a{};
+        a.feat = maps[m].feat;
+        a.batch = batch;
+        a.H = maps[m].height;
+        a.W = maps[m].width;
+        a.C = maps[m].channels;
+        a.coords = coords;
+        a.R = resolution;
+        a.points = (int32_t)points;
+        a.project = true;
+        a.n = n;
+        a.out = S;
+        a.out_stride = channels;
+        a.out_col = col;
+        a.mask = m == 0 ? mask : nullptr;
+        hipError_t e = launch_sample(a, dtype, dtype, tab, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(fn, e);
+        col += maps[m].channels;
+    }
+    return ok();
+}
+
+p3d_status p3d_proj_linear_grouped(const void* S, int64_t n, int32_t K, p3d_dtype dtype,
+                                   int32_t groups, const void* const* weights,
+                                   const void* const* biases, int32_t out_dim,
+                                   void* const* outs, int32_t accumulate, void* stream) {
+    const char* fn = "p3d_proj_linear_grouped";
+    if (n < 0) return fail(P3D_ERR_INVALID_ARG, "%s: n must be >= 0, got %lld", fn, (long long)n);
+    if (n > kMaxTokens)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: n must be <= %lld, got %lld", fn,
+                    (long long)kMaxTokens, (long long)n);
+    if (dtype != P3D_BF16)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: only BF16 S and weights are supported, got %s", fn,
+                    dtype_name(dtype));
+    if (groups < 1 || groups > P3D_MAX_GROUPS)
+        return fail(P3D_ERR_INVALID_ARG, "%s: groups must be in [1, %d], got %d", fn,
+                    P3D_MAX_GROUPS, groups);
+    if (K < 8 || K % 8)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: K must be a positive multiple of 8, got %d", fn, K);
+    if (out_dim < 8 || out_dim % 8 || out_dim > kMaxOutDim)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: out_dim must be a positive multiple of 8 up to %d, got %d", fn,
+                    kMaxOutDim, out_dim);
+    if (!weights || !outs)
+        return fail(P3D_ERR_INVALID_ARG, "%s: weights and outs must be host arrays [%d]", fn,
+                    groups);
+    if (!aligned(S, 16)) return fail(P3D_ERR_UNSUPPORTED, "%s: S must be 16-byte aligned", fn);
+    GroupedArgs a{};
+    for (int32_t g = 0; g < groups; ++g) {
+        if (!weights[g] || !outs[g])
+            return fail(P3D_ERR_INVALID_ARG, "%s: weights[%d] and outs[%d] must be non-NULL", fn,
+                        g, g);
+        const void* b = biases ? biases[g] : nullptr;
+        if (!aligned(weights[g], 16) || !aligned(outs[g], 16) || !aligned(b, 16))
+            return fail(P3D_ERR_UNSUPPORTED,
+                        "%s: weights[%d], biases[%d] and outs[%d] must be 16-byte aligned", fn, g,
+                        g, g);
+        a.W[g] = weights[g];
+        a.bias[g] = b;
+        a.out[g] = outs[g];
+    }
+    if (n == 0) return ok();
+    if (!S) return fail(P3D_ERR_INVALID_ARG, "%s: S is NULL", fn);
+    a.S = S;
+    a.n = n;
+    a.K = K;
+    a.G = groups;
+    a.D = out_dim;
+    hipError_t e = launch_grouped(a, accumulate != 0, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }

@@ -170,10 +170,16 @@ struct ProjectArgs {
 struct SampleArgs {
     const void* feat;
     int32_t batch, H, W, C;
-    const float* grid;
+    const float* grid;            // points (grid mode), or
     const int32_t* bidx;
+    const int32_t* coords;        // tokens to project (project mode)
+    int32_t R, points;
+    bool project;
     int64_t n;
-    void* out;
+    void* out;                    // row t, columns [out_col, out_col + C)
+    int64_t out_stride;           // elements per output row
+    int32_t out_col;
+    uint8_t* mask;                // project mode: in-image mask, or NULL
 };
 
 struct ProjCondArgs {
@@ -210,10 +216,21 @@ struct StatsArgs {
     p3d_proj_stats* stats;
 };
 
+struct GroupedArgs {
+    const void* S;                // [n, K] bf16
+    int64_t n;
+    int32_t K, G, D;
+    const void* W[P3D_MAX_GROUPS];      // [D, K] bf16 each
+    const void* bias[P3D_MAX_GROUPS];   // [D] bf16 or NULL
+    void* out[P3D_MAX_GROUPS];          // [n, D] bf16
+};
+
 hipError_t launch_project(const ProjectArgs& a, const CamTable& cams, hipStream_t s);
+hipError_t launch_grouped(const GroupedArgs& a, bool accumulate, hipStream_t s);
 hipError_t launch_stats(const StatsArgs& a, bool bf16, const CamTable& cams, hipStream_t s);
 hipError_t launch_requantize(const RequantArgs& a, hipStream_t s);
-hipError_t launch_sample(const SampleArgs& a, p3d_dtype in, p3d_dtype out, hipStream_t s);
+hipError_t launch_sample(const SampleArgs& a, p3d_dtype in, p3d_dtype out, const CamTable& cams,
+                         hipStream_t s);
 hipError_t launch_proj_cond(const ProjCondArgs& a, p3d_dtype dt, const CamTable& cams,
                             hipStream_t s);
 // bf16 fused kernel; writes the null rows too when a.n > 0

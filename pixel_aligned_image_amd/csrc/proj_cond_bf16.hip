@@ -49,47 +49,16 @@
 // Tile order: workgroup g runs on XCD g % 8; each XCD walks a contiguous
 // range of (token tile, N tile) pairs, N fastest, so the N tiles of a token
 // tile and its neighbours share corner rows in that XCD's L2.
-#include "p3d_internal.h"
+#include "bf16_tile.h"
 
 namespace p3d {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
+using namespace tile;
 
-constexpr int N_CONS = 8, N_PROD = 4;
-constexpr int kThreads = 64 * (N_CONS + N_PROD);
-constexpr int kProdThreads = 64 * N_PROD;
-constexpr int BM = 128, BN = 512, BK = 64;
-constexpr int WN = BN / N_CONS;     // features per consumer wave
-constexpr int TI = BM / 16;         // token blocks per consumer wave
-constexpr int FJ = WN / 16;         // feature blocks per consumer wave
 constexpr int G_ITEMS = BM * (BK / 8) / kProdThreads;   // gathered vectors per producer thread
-constexpr int W_ROWS = BN / N_PROD;                     // W rows loaded per producer wave
-constexpr int W_INSTR = W_ROWS * (BK / 8) / 64;         // direct W loads per producer lane
 constexpr int NULL_VEC = BM * BN / 8;                   // 16-byte vectors of a null block
-
-// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maxima (gfx9 layout:
-// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Workgroup barrier for LDS hand-offs only: this wave's LDS accesses have
-// completed, then s_barrier. Unlike __syncthreads() it does not wait for
-// outstanding global loads (that fence drains vmcnt), so the gather queued
-// for a later chunk stays in flight across it; whoever hands over data that
-// arrived by direct-to-LDS loads waits for those explicitly first.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// LDS slot of 16-byte vector v (0..7) of tile row `row` (128-byte rows).
-// Sixteen lanes reading vector v of sixteen consecutive rows then hit
-// sixteen distinct 16-byte slots of a 256-byte bank window (64 banks).
-__device__ __forceinline__ int slot(int row, int v) { return row * 8 + (v ^ ((row >> 1) & 7)); }
 
 __device__ __forceinline__ uint4 blend_bf16(const uint4 (&q)[4], const float (&w)[4]) {
     const uint32_t* a = reinterpret_cast<const uint32_t*>(&q[0]);
@@ -199,21 +168,9 @@ struct Producer {
         }
     }
 
-    // This wave's W rows of chunk kc into sw: row pw*W_ROWS + q*8 + lane/8,
-    // LDS slot lane%8, which holds logical vector (lane%8) ^ ((row/2) % 8);
-    // that swizzle only depends on the parity of q.
+    // This wave's W rows of chunk kc into sw (direct loads; see w_issue).
     __device__ __forceinline__ void w_issue(uint4* __restrict__ sw, int kc) const {
-        const int wv_even = (lane & 7) ^ ((lane >> 4) & 7);
-        const int wv_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
-#pragma unroll
-        for (int q = 0; q < W_INSTR; ++q) {
-            int col = min(n0 + pw * W_ROWS + q * 8 + (lane >> 3), D - 1);  // rows past D: unused
-            asm volatile("" : "+v"(col));
-            const int kv = min(kc * 8 + ((q & 1) ? wv_odd : wv_even), vprw - 1);  // K tail: S is 0
-            __builtin_amdgcn_global_load_lds(
-                reinterpret_cast<const void*>(wgt + (int64_t)col * vprw + kv),
-                (lds_void*)(sw + (pw * W_ROWS + q * 8) * 8), 16, 0, 0);
-        }
+        tile::w_issue(wgt, vprw, D, n0, pw, lane, sw, kc);
     }
 };
 
@@ -238,30 +195,6 @@ __device__ __forceinline__ void produce(Producer<TwoMaps>& p, const ProjCondArgs
             wait_vmcnt<G_ITEMS * 4>();               // the queued gather may stay in flight
         } else {
             wait_vmcnt<0>();
-        }
-    }
-    lds_barrier();
-}
-
-// Consumer: the chunk's 2 x 8 x 4 MFMAs. The other consumer wave on the SIMD
-// covers the LDS latency of the fragment reads.
-__device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TI], int lane, int cw,
-                                        const uint4* __restrict__ sa,
-                                        const uint4* __restrict__ sw) {
-    const int n = lane & 15, g4 = lane >> 4;
-#pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-        const int v = s * 4 + g4;
-        bf16x8_t wf[FJ];
-#pragma unroll
-        for (int j = 0; j < FJ; ++j)
-            wf[j] = __builtin_bit_cast(bf16x8_t, sw[slot(cw * WN + j * 16 + n, v)]);
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-            const bf16x8_t sf = __builtin_bit_cast(bf16x8_t, sa[slot(i * 16 + n, v)]);
-#pragma unroll
-            for (int j = 0; j < FJ; ++j)
-                acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], sf, acc[j][i], 0, 0, 0);
         }
     }
     lds_barrier();
@@ -369,41 +302,8 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
         consume(acc, lane, cw, sA1, sW1);
     }
 
-    // ---- epilogue: + bias, round to bf16, stage the 128 x 64 tile in the
-    // free W stages (token-major 128-byte rows, same slot swizzle), 16-byte
-    // row stores. Lane l of block (j, i) holds features 4*(l/16) + r of
-    // token l % 16.
-    const int fbase = n0 + cw * WN;
-    uint4* stage4 = (cw < N_CONS / 2 ? sW0 : sW1) + (cw % (N_CONS / 2)) * (BM * 8);
-    uint2* stage2 = reinterpret_cast<uint2*>(stage4);
-    const uint16_t* bias16 = reinterpret_cast<const uint16_t*>(a.bias);
-#pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-        float bv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int f = fbase + j * 16 + 4 * (lane >> 4) + r;
-            bv[r] = (bias16 && f < a.D) ? __uint_as_float((uint32_t)bias16[f] << 16) : 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-            const int t = i * 16 + (lane & 15);
-            const int f = j * 16 + 4 * (lane >> 4);
-            uint2 pk;
-            pk.x = pack_bf16x2(acc[j][i][0] + bv[0], acc[j][i][1] + bv[1]);
-            pk.y = pack_bf16x2(acc[j][i][2] + bv[2], acc[j][i][3] + bv[3]);
-            stage2[slot(t, f >> 3) * 2 + ((f >> 2) & 1)] = pk;
-        }
-    }
-    __syncthreads();                                              // consumers staged
-#pragma unroll
-    for (int r = 0; r < BM * 8 / 64; ++r) {
-        const int q = r * 64 + lane;
-        const int t = q >> 3, cv = q & 7;
-        const int64_t tok = m0 + t;
-        const int colv = (fbase >> 3) + cv;
-        if (tok < a.n && colv < dv) out4[tok * dv + colv] = stage4[slot(t, cv)];
-    }
+    store_tile<false>(acc, lane, cw, n0, m0, a.n, a.D,
+                      reinterpret_cast<const uint16_t*>(a.bias), a.out, sW0, sW1);
 }
 
 }  // namespace

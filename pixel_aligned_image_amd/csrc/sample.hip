@@ -9,6 +9,10 @@
 // binary32 and written with non-temporal 16-byte stores. Consecutive point
 // runs share most corner rows; tiles are mapped so that each XCD walks a
 // contiguous range of runs and those shared rows hit its own L2.
+//
+// The same kernel serves p3d_proj_sample (project mode): the points come from
+// projecting the tokens, and each map's samples go to their columns of a
+// wider S row (two maps: one launch per map).
 #include "p3d_internal.h"
 
 namespace p3d {
@@ -36,9 +40,9 @@ __device__ __forceinline__ void widen(const uint4& q, float* v, bool bf16) {
     }
 }
 
-template <bool InBf16, bool OutBf16>
-__global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, int64_t tiles,
-                                                          int64_t per_xcd) {
+template <bool InBf16, bool OutBf16, bool Project>
+__global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, CamTable cams,
+                                                          int64_t tiles, int64_t per_xcd) {
     // XCD-aware order: workgroup g runs on XCD g % 8; give each XCD a
     // contiguous range of tiles.
     const int64_t g = blockIdx.x;
@@ -52,9 +56,20 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, int64_t 
     const int ntok = (int)((a.n - t0) < kTok ? (a.n - t0) : kTok);
     if (threadIdx.x < ntok) {
         const int64_t t = t0 + threadIdx.x;
-        const float2 gp = reinterpret_cast<const float2*>(a.grid)[t];
-        int32_t b = a.bidx ? a.bidx[t] : 0;
-        b = b < 0 ? 0 : (b >= a.batch ? a.batch - 1 : b);
+        float2 gp;
+        int32_t b;
+        if constexpr (Project) {
+            int32_t x, y, z;
+            token_cell(a.coords, t, a.R, b, x, y, z);
+            const Projected p = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
+            gp = make_float2(p.gx, p.gy);
+            b = p.b;
+            if (a.mask) a.mask[t] = p.mask;
+        } else {
+            gp = reinterpret_cast<const float2*>(a.grid)[t];
+            b = a.bidx ? a.bidx[t] : 0;
+            b = b < 0 ? 0 : (b >= a.batch ? a.batch - 1 : b);
+        }
         const Corners c = corners_of(gp.x, gp.y, b, a.H, a.W);
         s_row[threadIdx.x][0] = c.r00; s_row[threadIdx.x][1] = c.r01;
         s_row[threadIdx.x][2] = c.r10; s_row[threadIdx.x][3] = c.r11;
@@ -103,11 +118,13 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, int64_t 
                 o.y = pack_bf16x2(r[2], r[3]);
                 o.z = pack_bf16x2(r[4], r[5]);
                 o.w = pack_bf16x2(r[6], r[7]);
-                uint4* dst = reinterpret_cast<uint4*>(a.out) + t * vpr + vec[u];
+                uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) +
+                                                      t * a.out_stride + a.out_col) + vec[u];
                 store_nt16(dst, o);
             } else {
-                float4* dst = reinterpret_cast<float4*>(a.out) +
-                              (t * a.C + (int64_t)vec[u] * kEpv) / 4;
+                float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) +
+                                                        t * a.out_stride + a.out_col +
+                                                        (int64_t)vec[u] * kEpv);
                 store_nt16(dst, make_uint4(__float_as_uint(r[0]), __float_as_uint(r[1]),
                                            __float_as_uint(r[2]), __float_as_uint(r[3])));
                 if (kEpv == 8)
@@ -120,20 +137,25 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, int64_t 
 
 }  // namespace
 
-hipError_t launch_sample(const SampleArgs& a, p3d_dtype in, p3d_dtype out, hipStream_t s) {
+hipError_t launch_sample(const SampleArgs& a, p3d_dtype in, p3d_dtype out, const CamTable& cams,
+                         hipStream_t s) {
     const int64_t tiles = (a.n + kTok - 1) / kTok;
     const int64_t per_xcd = (tiles + 7) / 8;
     const int64_t blocks = per_xcd * 8;
     SampleArgs args = a;
+    CamTable tab = cams;
     int64_t t = tiles, p = per_xcd;
-    void* params[] = {&args, &t, &p};
+    void* params[] = {&args, &tab, &t, &p};
     const void* fn;
-    if (in == P3D_BF16 && out == P3D_BF16)
-        fn = reinterpret_cast<const void*>(&sample_kernel<true, true>);
+    if (a.project)
+        fn = in == P3D_BF16 ? reinterpret_cast<const void*>(&sample_kernel<true, true, true>)
+                            : reinterpret_cast<const void*>(&sample_kernel<false, false, true>);
+    else if (in == P3D_BF16 && out == P3D_BF16)
+        fn = reinterpret_cast<const void*>(&sample_kernel<true, true, false>);
     else if (in == P3D_BF16)
-        fn = reinterpret_cast<const void*>(&sample_kernel<true, false>);
+        fn = reinterpret_cast<const void*>(&sample_kernel<true, false, false>);
     else
-        fn = reinterpret_cast<const void*>(&sample_kernel<false, false>);
+        fn = reinterpret_cast<const void*>(&sample_kernel<false, false, false>);
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), params, 0, s);
 }
 

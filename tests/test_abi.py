@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(p3d):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(p3d.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -259,3 +259,53 @@ def test_projection_stats_validation(p3d):
     assert st == 3 and "dtype" in msg
     st, msg = call([(NULL, 4, 4, 64)])
     assert st == 1 and "feat is NULL" in msg
+
+
+def test_proj_linear_grouped_validation(p3d):
+    def call(**kw):
+        a = dict(S=FAKE, n=100, K=64, dtype=1, G=2, D=64, acc=0, weights=[FAKE, FAKE],
+                 biases=None, outs=[FAKE, FAKE])
+        a.update(kw)
+        vp = ctypes.c_void_p
+        w = (vp * max(1, len(a["weights"])))(*a["weights"]) if a["weights"] is not None else None
+        o = (vp * max(1, len(a["outs"])))(*a["outs"]) if a["outs"] is not None else None
+        b = (vp * len(a["biases"]))(*a["biases"]) if a["biases"] is not None else None
+        st = p3d.lib.p3d_proj_linear_grouped(a["S"], a["n"], a["K"], a["dtype"], a["G"], w, b,
+                                             a["D"], o, a["acc"], NULL)
+        return st, p3d.p3d_last_error()
+
+    assert call(dtype=0) == (4, call(dtype=0)[1]) and "only BF16" in call(dtype=0)[1]
+    st, msg = call(G=0)
+    assert st == 1 and "groups must be in [1, 64]" in msg
+    st, msg = call(G=65)
+    assert st == 1 and "groups" in msg
+    st, msg = call(K=60)
+    assert st == 4 and "K must be" in msg
+    st, msg = call(D=100)
+    assert st == 4 and "out_dim must be" in msg
+    st, msg = call(weights=None)
+    assert st == 1 and "host arrays" in msg
+    st, msg = call(weights=[FAKE, NULL])
+    assert st == 1 and "weights[1]" in msg
+    st, msg = call(outs=[FAKE + 8, FAKE])
+    assert st == 4 and "16-byte aligned" in msg
+    st, msg = call(biases=[NULL, FAKE + 2])
+    assert st == 4 and "biases[1]" in msg
+    st, msg = call(n=-1)
+    assert st == 1
+    assert call(n=0, S=NULL)[0] == 0
+
+
+def test_proj_sample_validation(p3d):
+    cams = _cams(p3d, [(2.0, 2.0)])
+    arr = (p3d.p3d_map * 2)()
+    for i, (h, w, c) in enumerate([(4, 4, 64), (8, 8, 72)]):
+        arr[i].feat, arr[i].height, arr[i].width, arr[i].channels = FAKE, h, w, c
+    st = p3d.lib.p3d_proj_sample(FAKE, 16, 8, 0, cams, 1, 1, arr, 2, FAKE + 8, NULL, NULL)
+    assert st == 4 and "S must be 16-byte aligned" in p3d.p3d_last_error()
+    st = p3d.lib.p3d_proj_sample(FAKE, 16, 8, 0, cams, 1, 1, arr, 2, NULL, NULL, NULL)
+    assert st == 1 and "S is NULL" in p3d.p3d_last_error()
+    arr[1].channels = 70
+    st = p3d.lib.p3d_proj_sample(FAKE, 16, 8, 0, cams, 1, 1, arr, 2, FAKE, NULL, NULL)
+    assert st == 4 and "maps[1] channels" in p3d.p3d_last_error()
+    assert p3d.lib.p3d_proj_sample(NULL, 0, 8, 0, cams, 1, 1, arr, 1, NULL, NULL, NULL) == 0

@@ -25,7 +25,9 @@ Prints ONE JSON line. Fields beyond the common ones:
                  roofline: cascade requantization (HBM), the fused kernel on
                  grid-node points after requantization (MFMA), the fused
                  kernel over two concatenated maps (MFMA), the projection
-                 diagnostics over those two maps (HBM gather + reduction).
+                 diagnostics over those two maps (HBM gather + reduction),
+                 gathering those samples once into S (HBM) and the per-block
+                 proj_linear of 30 DiT blocks over S with residual add (MFMA).
 """
 import argparse
 import hashlib
@@ -235,7 +237,36 @@ def run_extra(p3d, synth, stream, reps, lead_step):
         "achieved": dbytes / (diag_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": dbytes / (diag_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "figures": p3d.stats_summary(raw, [m.shape[3] for m in maps])}
-    del maps, weight, y, coords
+    # ---- gather once per stage, then every block's proj_linear per step
+    K = sum(m.shape[3] for m in maps)
+    S = torch.empty((n, K), dtype=torch.bfloat16, device="cuda")
+    gat = lambda: p3d.p3d_proj_sample(coords, n, w.resolution, camarr, maps, S)
+    for _ in range(reps):
+        gat()
+    gat_ms = time_events(gat, reps, stream)
+    gbytes = 16 * n + uniq + n * K * 2
+    out["gather_once"] = {
+        "workload": w.name, "kernel": "sample_kernel<true, true, true> (one launch per map)",
+        "tokens": n, "mean_ms": gat_ms, "bound": "hbm", "bytes_per_launch": gbytes,
+        "achieved": gbytes / (gat_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": gbytes / (gat_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    G = 30
+    rng = np.random.default_rng(801)
+    Wg = [torch.from_numpy(synth.bf16_bits((rng.standard_normal((w.out_dim, K)) * 0.02).astype(
+        np.float32))).view(torch.int16).view(torch.bfloat16).cuda() for _ in range(G)]
+    outs = [torch.zeros((n, w.out_dim), dtype=torch.bfloat16, device="cuda") for _ in range(G)]
+    grp = lambda: p3d.p3d_proj_linear_grouped(S, Wg, outs, accumulate=True)
+    for _ in range(max(3, reps // 4)):
+        grp()
+    grp_ms = time_events(grp, max(5, reps // 4), stream)
+    gflops = 2.0 * n * K * w.out_dim * G
+    out["grouped"] = {
+        "workload": w.name + " x 30 blocks", "kernel": "grouped_kernel<true>", "tokens": n,
+        "blocks": G, "mean_ms": grp_ms, "bound": "mfma", "flops_per_launch": gflops,
+        "achieved": gflops / (grp_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s", "frac": gflops / (grp_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "note": "residual add: every block's output is read and rewritten (S 2048 -> 1536)"}
+    del maps, weight, y, coords, S, Wg, outs
     torch.cuda.empty_cache()
     return out
 

@@ -47,15 +47,27 @@ DEFAULT_WORKLOAD = "shell1024_cfg_bf16_c2048_d1536"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_digest():
-    """sha256 over the HIP sources of libp3d: counters taken on one build are
-    reused only while this matches."""
+# source files each measured kernel is built from (its counters stay valid
+# while these are unchanged)
+KERNEL_SOURCES = {
+    "proj_cond_bf16_kernel": ["proj_cond_bf16.hip", "bf16_tile.h", "p3d_internal.h"],
+    "proj_cond_kernel": ["proj_cond.hip", "p3d_internal.h"],
+    "sample_kernel": ["sample.hip", "p3d_internal.h"],
+}
+
+
+def kernel_source_digest(kernel=None):
+    """sha256 over the sources of `kernel` (all HIP sources of libp3d when
+    None) and include/p3d.h: counters taken on one build are reused only
+    while this matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "pixel_aligned_image_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    names = KERNEL_SOURCES.get(kernel) or sorted(
+        f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    for name in sorted(names):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "p3d.h"), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -68,7 +80,7 @@ def recorded_traffic(kernel, workload):
     text = open(path).read()
     m_digest = re.search(r"source_digest:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_digest and m_bytes) or m_digest.group(1) != kernel_source_digest():
+    if not (m_digest and m_bytes) or m_digest.group(1) != kernel_source_digest(kernel):
         return None
     return float(m_bytes.group(1))
 
@@ -453,7 +465,7 @@ def main():
                       "achieved": null_bytes / (null_ms * 1e-3) / 1e9 if null_ms else None,
                       "unit": "GB/s", "bytes_per_launch": null_bytes},
         "input_generation_s": t_gen,
-        "source_digest": kernel_source_digest(),
+        "source_digest": {k: kernel_source_digest(k) for k in (kname, "sample_kernel")},
     }
     if not args.no_extra:
         line["extra"] = run_extra(p3d, synth, stream, max(args.steps, 20), step)

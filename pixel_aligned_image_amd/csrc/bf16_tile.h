@@ -100,6 +100,9 @@ __device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TI], int lane, int cw
 // same slot swizzle) and write 16-byte row pieces. Lane l of block (j, i)
 // holds features 4*(l/16) + r of token l % 16. out is [n, D] bf16; rows at or
 // past n are not touched.
+constexpr int OLD_BATCH = 4;        // residual loads in flight together (registers)
+static_assert(TI % OLD_BATCH == 0, "residual batches");
+
 template <bool Accumulate>
 __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TI], int lane, int cw,
                                            int32_t n0, int64_t m0, int64_t n, int32_t D,
@@ -112,26 +115,39 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TI], int lan
     const uint16_t* out16 = reinterpret_cast<const uint16_t*>(out);
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
-        float bv[4];
+        // D is a multiple of 8, so a lane's four features are all below D or
+        // all past it. The loads are unconditional, from clamped addresses,
+        // with the values selected afterwards: a batch of loads then goes out
+        // together and shares one wait (conditional loads each wait alone).
         const int f0 = fbase + j * 16 + 4 * (lane >> 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            bv[r] = (bias16 && f0 + r < D) ? __uint_as_float((uint32_t)bias16[f0 + r] << 16) : 0.0f;
+        const bool fin = f0 < D;
+        const int fc = fin ? f0 : D - 4;
+        uint2 b2 = make_uint2(0, 0);
+        if (bias16) b2 = *reinterpret_cast<const uint2*>(bias16 + fc);
+        if (!fin) b2 = make_uint2(0, 0);
+        const float bv[4] = {bf16lo(b2.x), bf16hi(b2.x), bf16lo(b2.y), bf16hi(b2.y)};
+        uint2 old[TI];
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
+            if (Accumulate && i % OLD_BATCH == 0) {
+                // the residual values of the next OLD_BATCH token blocks
+#pragma unroll
+                for (int u = i; u < i + OLD_BATCH; ++u) {
+                    const int64_t tok = m0 + u * 16 + (lane & 15);
+                    old[u] = *reinterpret_cast<const uint2*>(out16 + (tok < n ? tok : n - 1) * D + fc);
+                }
+            }
             const int t = i * 16 + (lane & 15);
             const int f = j * 16 + 4 * (lane >> 4);
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = acc[j][i][r] + bv[r];
             if constexpr (Accumulate) {
-                if (m0 + t < n && f0 < D) {
-                    const uint2 old = *reinterpret_cast<const uint2*>(out16 + (m0 + t) * D + f0);
-                    y[0] += bf16lo(old.x);
-                    y[1] += bf16hi(old.x);
-                    y[2] += bf16lo(old.y);
-                    y[3] += bf16hi(old.y);
-                }
+                // rows past n and features past D are never stored
+                y[0] += bf16lo(old[i].x);
+                y[1] += bf16hi(old[i].x);
+                y[2] += bf16lo(old[i].y);
+                y[3] += bf16hi(old[i].y);
             }
             uint2 pk;
             pk.x = pack_bf16x2(y[0], y[1]);

@@ -52,23 +52,68 @@ __device__ __forceinline__ void lds_barrier() {
 // sixteen distinct 16-byte slots of a 256-byte bank window (64 banks).
 __device__ __forceinline__ int slot(int row, int v) { return row * 8 + (v ^ ((row >> 1) & 7)); }
 
-// This wave's W rows of chunk kc into sw: row pw*W_ROWS + q*8 + lane/8,
-// LDS slot lane%8, which holds logical vector (lane%8) ^ ((row/2) % 8);
-// that swizzle only depends on the parity of q.
-__device__ __forceinline__ void w_issue(const uint4* wgt, int vprw, int D, int n0, int pw,
-                                        int lane, uint4* __restrict__ sw, int kc) {
-    const int wv_even = (lane & 7) ^ ((lane >> 4) & 7);
-    const int wv_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
-#pragma unroll
-    for (int q = 0; q < W_INSTR; ++q) {
-        int col = min(n0 + pw * W_ROWS + q * 8 + (lane >> 3), D - 1);  // rows past D: unused
-        asm volatile("" : "+v"(col));
-        const int kv = min(kc * 8 + ((q & 1) ? wv_odd : wv_even), vprw - 1);  // K tail: S is 0
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(wgt + (int64_t)col * vprw + kv),
-            (lds_void*)(sw + (pw * W_ROWS + q * 8) * 8), 16, 0, 0);
+// A producer wave's share of the tile's W stream: rows row0 .. row0+127
+// (row0 = n0 + pw*W_ROWS), one 64-channel chunk at a time, into the LDS
+// stage. Load q moves rows q*8 .. q*8+7 (lane l: row q*8 + l/8) with
+// global_load_lds_dwordx4; lane l lands in LDS slot l%8 of its row, which
+// holds logical vector (l%8) ^ ((row/2) % 8), a swizzle that only depends on
+// the parity of q.
+// Fast path (every row below D, the chunk inside K): the address is a
+// uniform base (row0, chunk kc, load q: scalar registers) plus one of two
+// per-lane 32-bit offsets fixed for the tile, so a load costs no vector
+// instructions. Otherwise rows past D repeat row D-1 (their outputs are never
+// stored) and the vector index is clamped to the row (the matching S values
+// are zero).
+struct WLoader {
+    const uint4* wgt;
+    const char* base;                // row row0 of W (uniform)
+    uint32_t voff_even, voff_odd;    // per lane: row lane/8, swizzled vector
+    int row_bytes, vprw, D, row0, pw, lane;
+    bool full;                       // rows row0 .. row0 + W_ROWS - 1 all below D
+
+    __device__ __forceinline__ void init(const void* w, int vprw_, int D_, int n0, int pw_,
+                                         int lane_) {
+        wgt = reinterpret_cast<const uint4*>(w);
+        vprw = vprw_;
+        D = D_;
+        pw = pw_;
+        lane = lane_;
+        row0 = n0 + pw * W_ROWS;
+        row_bytes = vprw * 16;
+        base = reinterpret_cast<const char*>(w) + (int64_t)row0 * row_bytes;
+        // every offset must fit 32 bits: W_ROWS rows of W
+        full = row0 + W_ROWS <= D && (int64_t)W_ROWS * row_bytes < ((int64_t)1 << 31);
+        const int wv_even = (lane & 7) ^ ((lane >> 4) & 7);
+        const int wv_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
+        voff_even = (uint32_t)((lane >> 3) * row_bytes + wv_even * 16);
+        voff_odd = (uint32_t)((lane >> 3) * row_bytes + wv_odd * 16);
     }
-}
+
+    __device__ __forceinline__ void issue(uint4* __restrict__ sw, int kc) const {
+        uint4* dst = sw + pw * W_ROWS * 8;
+        if (full && (kc + 1) * 8 <= vprw) {
+            const char* b = base + kc * 128;
+#pragma unroll
+            for (int q = 0; q < W_INSTR; ++q) {
+                const char* bq = b + (int64_t)q * 8 * row_bytes;
+                __builtin_amdgcn_global_load_lds(
+                    reinterpret_cast<const void*>(bq + ((q & 1) ? voff_odd : voff_even)),
+                    (lds_void*)(dst + q * 64), 16, 0, 0);
+            }
+        } else {
+            const int wv_even = (lane & 7) ^ ((lane >> 4) & 7);
+            const int wv_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
+#pragma unroll
+            for (int q = 0; q < W_INSTR; ++q) {
+                const int col = min(row0 + q * 8 + (lane >> 3), D - 1);
+                const int kv = min(kc * 8 + ((q & 1) ? wv_odd : wv_even), vprw - 1);
+                __builtin_amdgcn_global_load_lds(
+                    reinterpret_cast<const void*>(wgt + (int64_t)col * vprw + kv),
+                    (lds_void*)(dst + q * 64), 16, 0, 0);
+            }
+        }
+    }
+};
 
 // Consumer: the chunk's 2 x 8 x 4 MFMAs. The other consumer wave on the SIMD
 // covers the LDS latency of the fragment reads.

@@ -25,14 +25,36 @@ constexpr int S_ITEMS = BM * (BK / 8) / kProdThreads;   // S vectors per produce
 
 struct DenseProducer {
     const uint4* S;
-    const uint4* wgt;
-    int vprs, D, n0, ptid, lane, pw, gv;
+    int vprs, ptid, gv;
     int64_t m0, last;               // first token of the tile, last valid token
+    const char* sbase;              // row m0 of S (uniform)
+    uint32_t off[S_ITEMS];          // per item: (row - m0) * row bytes + 16 gv
+    bool off32;                     // the tile's rows of S span under 2 GiB
+    WLoader wl;
 
-    // Queue S vector gv of chunk kc for the thread's items. Rows past the
-    // last token repeat it (their outputs are never stored); a K tail zeroes
-    // the value.
+    // Rows past the last token repeat it (their outputs are never stored).
+    __device__ __forceinline__ void set_items() {
+        sbase = reinterpret_cast<const char*>(S) + m0 * (int64_t)vprs * 16;
+        off32 = (int64_t)BM * vprs * 16 < ((int64_t)1 << 31);
+#pragma unroll
+        for (int u = 0; u < S_ITEMS; ++u) {
+            int64_t row = m0 + ((ptid + u * kProdThreads) >> 3);
+            row = row < last ? row : last;
+            off[u] = (uint32_t)((row - m0) * vprs * 16 + gv * 16);
+        }
+    }
+
+    // Queue S vector gv of chunk kc for the thread's items: a uniform base
+    // plus the items' 32-bit offsets. A K tail clamps the vector index and
+    // commit() zeroes the value (zeroing here would make the loads'
+    // registers wait).
     __device__ __forceinline__ void s_issue(uint4 (&q)[S_ITEMS], int kc) const {
+        if (off32 && (kc + 1) * 8 <= vprs) {
+            const char* b = sbase + kc * 128;
+#pragma unroll
+            for (int u = 0; u < S_ITEMS; ++u) q[u] = *reinterpret_cast<const uint4*>(b + off[u]);
+            return;
+        }
         const int kv = min(kc * 8 + gv, vprs - 1);
 #pragma unroll
         for (int u = 0; u < S_ITEMS; ++u) {
@@ -40,22 +62,14 @@ struct DenseProducer {
             row = row < last ? row : last;
             q[u] = S[row * vprs + kv];
         }
-        if ((kc + 1) * 8 > vprs) {                    // uniform: partial or padding chunk
-            const bool dead = kc * 8 + gv >= vprs;
-#pragma unroll
-            for (int u = 0; u < S_ITEMS; ++u)
-                if (dead) q[u] = make_uint4(0, 0, 0, 0);
-        }
     }
 
-    __device__ __forceinline__ void commit(const uint4 (&q)[S_ITEMS],
+    __device__ __forceinline__ void commit(const uint4 (&q)[S_ITEMS], int kc,
                                            uint4* __restrict__ sa) const {
+        const bool dead = kc * 8 + gv >= vprs;
 #pragma unroll
-        for (int u = 0; u < S_ITEMS; ++u) sa[slot((ptid + u * kProdThreads) >> 3, gv)] = q[u];
-    }
-
-    __device__ __forceinline__ void w_issue(uint4* __restrict__ sw, int kc) const {
-        tile::w_issue(wgt, vprs, D, n0, pw, lane, sw, kc);
+        for (int u = 0; u < S_ITEMS; ++u)
+            sa[slot((ptid + u * kProdThreads) >> 3, gv)] = dead ? make_uint4(0, 0, 0, 0) : q[u];
     }
 };
 
@@ -65,8 +79,10 @@ __device__ __forceinline__ void produce(const DenseProducer& p, int kc, int nk2,
                                         uint4 (&q)[S_ITEMS], uint4* __restrict__ sa_n,
                                         uint4* __restrict__ sw_n) {
     if (kc + 1 < nk2) {
-        p.w_issue(sw_n, kc + 1);
-        p.commit(q, sa_n);
+        // W first: with no blend to overlap, waiting for S before queueing W
+        // only delays the W loads
+        p.wl.issue(sw_n, kc + 1);
+        p.commit(q, kc + 1, sa_n);
         if (kc + 2 < nk2) {
             p.s_issue(q, kc + 2);
             wait_vmcnt<S_ITEMS>();                   // the queued S may stay in flight
@@ -102,20 +118,18 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs a, int32_
     if (wave >= N_CONS) {
         DenseProducer p;
         p.S = reinterpret_cast<const uint4*>(a.S);
-        p.wgt = reinterpret_cast<const uint4*>(a.W[grp]);
         p.vprs = a.K >> 3;
-        p.D = a.D;
-        p.n0 = n0;
         p.ptid = tid - N_CONS * 64;
-        p.lane = lane;
-        p.pw = wave - N_CONS;
         p.gv = p.ptid & 7;
         p.m0 = m0;
         p.last = a.n - 1;
+        p.set_items();
+        p.wl.init(a.W[grp], a.K >> 3, a.D, n0, __builtin_amdgcn_readfirstlane(wave - N_CONS),
+                  lane);
         uint4 q[S_ITEMS];
         p.s_issue(q, 0);
-        p.w_issue(sW0, 0);
-        p.commit(q, sA0);
+        p.wl.issue(sW0, 0);
+        p.commit(q, 0, sA0);
         p.s_issue(q, 1);
         wait_vmcnt<S_ITEMS>();
         lds_barrier();                                            // B_0

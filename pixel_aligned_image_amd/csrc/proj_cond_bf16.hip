@@ -103,17 +103,45 @@ __device__ __forceinline__ int4 token_entry(const ProjCondArgs& a, const CamTabl
 
 // Producer state: one thread of the four producer waves. TwoMaps: the gather
 // switches to map 1 part-way through K (kbase, vpr, W and the metadata
-// change); with one map they are constants of the launch.
-template <bool TwoMaps>
+// change); with one map they are constants of the launch. Off32: every map
+// is under 4 GiB, so a corner vector's byte offset in its map fits 32 bits.
+// Per tile (and again at the map switch) each item keeps its four corner
+// offsets and its four bilinear weights; a chunk's gather is then a uniform
+// base (map, chunk: scalar registers) plus those offsets, with no vector
+// address arithmetic, and the blend reuses the weights.
+template <bool TwoMaps, bool Off32>
 struct Producer {
     const uint4* feat;               // map of the chunks being gathered
-    const uint4* wgt;
     int vpr;                         // 16-byte vectors per row of that map
     int kbase;                       // first K chunk of that map
-    int vprw;                        // 16-byte vectors per W row (all of K)
-    int D, W, n0, ptid, lane, pw;
+    int W;                           // that map's width (row step between image rows)
+    int ptid;
     int gv;                          // vector of each gathered 128-byte segment
-    int4 gt[G_ITEMS];                // token_entry of each item
+    int4 gt[G_ITEMS];                // token_entry of each item (used without Off32)
+    uint32_t off[G_ITEMS][4];        // corner rows' byte offsets + 16 gv (Off32)
+    float wt[G_ITEMS][4];            // bilinear weights, 0 for a padding token
+    WLoader wl;
+
+    // Offsets and weights of the items from their corner metadata gt.
+    __device__ __forceinline__ void set_items() {
+#pragma unroll
+        for (int u = 0; u < G_ITEMS; ++u) {
+            const int32_t r00 = gt[u].x, steps = gt[u].y;
+            const int32_t dx = steps & 1, dyw = (steps & 2) ? W : 0;
+            const int32_t rows[4] = {r00, r00 + dx, r00 + dyw, r00 + dyw + dx};
+            if constexpr (Off32) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    off[u][k] = (uint32_t)rows[k] * (uint32_t)(vpr * 16) + (uint32_t)(gv * 16);
+            }
+            const float tx = __int_as_float(gt[u].z), ty = __int_as_float(gt[u].w);
+            wt[u][0] = (1.0f - tx) * (1.0f - ty);
+            wt[u][1] = tx * (1.0f - ty);
+            wt[u][2] = (1.0f - tx) * ty;
+            wt[u][3] = tx * ty;
+            if (steps & 4) wt[u][0] = 0.0f;           // padding token: all weights 0
+        }
+    }
 
     // Switch the gather to map 1: its base, row length, width and the
     // items' corner metadata on its grid.
@@ -127,13 +155,38 @@ struct Producer {
         for (int u = 0; u < G_ITEMS; ++u)
             gt[u] = token_entry(a, cams, m0 + ((ptid + u * kProdThreads) >> 3), a.H1, a.W1,
                                 nullptr);
+        set_items();
     }
 
     // Queue the four corner vectors of every item of chunk kc. A K tail (the
     // map's channels not a multiple of 64, or the padding chunk) clamps the
-    // address and zeroes the value.
+    // address; commit() zeroes those values (zeroing here would make the
+    // loads' registers wait).
     __device__ __forceinline__ void gather_issue(Gq& gq, int kc) const {
         const int kl = TwoMaps ? kc - kbase : kc;
+        if constexpr (Off32) {
+            const char* b = reinterpret_cast<const char*>(feat) + kl * 128;
+            if ((kl + 1) * 8 <= vpr) {
+#pragma unroll
+                for (int u = 0; u < G_ITEMS; ++u)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        gq[u][k] = *reinterpret_cast<const uint4*>(b + off[u][k]);
+            } else {
+                // K tail: the vector index kv clamped to the row, from the map
+                // base. off - 16 gv is the row's byte offset, and adding 16 kv
+                // stays inside the map (under 4 GiB): neither step wraps
+                const char* f = reinterpret_cast<const char*>(feat);
+                const uint32_t kv16 = (uint32_t)min(kl * 8 + gv, vpr - 1) * 16u;
+                const uint32_t gv16 = (uint32_t)gv * 16u;
+#pragma unroll
+                for (int u = 0; u < G_ITEMS; ++u)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        gq[u][k] = *reinterpret_cast<const uint4*>(f + (off[u][k] - gv16 + kv16));
+            }
+            return;
+        }
         const int kv = min(kl * 8 + gv, vpr - 1);
 #pragma unroll
         for (int u = 0; u < G_ITEMS; ++u) {
@@ -146,31 +199,19 @@ struct Producer {
 #pragma unroll
             for (int k = 0; k < 4; ++k) gq[u][k] = feat[(int64_t)rows[k] * vpr + kv];
         }
-        if ((kl + 1) * 8 > vpr) {                     // uniform: partial or padding chunk
-            const bool dead = kl * 8 + gv >= vpr;
-#pragma unroll
-            for (int u = 0; u < G_ITEMS; ++u)
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (dead) gq[u][k] = make_uint4(0, 0, 0, 0);
-        }
     }
 
-    // Blend the queued vectors (bilinear weights computed as in the
-    // standalone sampler) and store the bf16 S chunk into sa.
-    __device__ __forceinline__ void commit(const Gq& gq, uint4* __restrict__ sa) const {
+    // Blend the queued vectors of chunk kc (bilinear weights computed as in
+    // the standalone sampler) and store the bf16 S chunk into sa; vectors
+    // past the map's channels store zeros.
+    __device__ __forceinline__ void commit(const Gq& gq, int kc, uint4* __restrict__ sa) const {
+        const int kl = TwoMaps ? kc - kbase : kc;
+        const bool dead = kl * 8 + gv >= vpr;
 #pragma unroll
         for (int u = 0; u < G_ITEMS; ++u) {
-            const float tx = __int_as_float(gt[u].z), ty = __int_as_float(gt[u].w);
-            float w[4] = {(1.0f - tx) * (1.0f - ty), tx * (1.0f - ty), (1.0f - tx) * ty, tx * ty};
-            if (gt[u].y & 4) w[0] = 0.0f;             // padding token: all weights 0
-            sa[slot((ptid + u * kProdThreads) >> 3, gv)] = blend_bf16(gq[u], w);
+            const uint4 v = blend_bf16(gq[u], wt[u]);
+            sa[slot((ptid + u * kProdThreads) >> 3, gv)] = dead ? make_uint4(0, 0, 0, 0) : v;
         }
-    }
-
-    // This wave's W rows of chunk kc into sw (direct loads; see w_issue).
-    __device__ __forceinline__ void w_issue(uint4* __restrict__ sw, int kc) const {
-        tile::w_issue(wgt, vprw, D, n0, pw, lane, sw, kc);
     }
 };
 
@@ -179,14 +220,19 @@ struct Producer {
 // chunk k1 on), then this wave's W loads must have landed before the
 // barrier. The LDS stages are restrict parameters so that the compiler can
 // tell the direct W loads apart from the S stores.
-template <bool TwoMaps>
-__device__ __forceinline__ void produce(Producer<TwoMaps>& p, const ProjCondArgs& a,
+template <bool TwoMaps, bool Off32>
+__device__ __forceinline__ void produce(Producer<TwoMaps, Off32>& p, const ProjCondArgs& a,
                                         const CamTable& cams, int64_t m0, int k1, int kc,
                                         int nk2, Gq& gq, uint4* __restrict__ sa_n,
                                         uint4* __restrict__ sw_n) {
     if (kc + 1 < nk2) {
-        p.w_issue(sw_n, kc + 1);
-        p.commit(gq, sa_n);
+        // Only this chunk's corners are in flight here: wait for them
+        // explicitly, then queue W, then blend. Without the explicit wait the
+        // compiler waits before the blend, for the W loads queued just before
+        // it as well.
+        wait_vmcnt<0>();
+        p.wl.issue(sw_n, kc + 1);
+        p.commit(gq, kc + 1, sa_n);
         if constexpr (TwoMaps) {
             if (kc + 2 == k1) p.to_map1(a, cams, m0, k1);
         }
@@ -200,7 +246,7 @@ __device__ __forceinline__ void produce(Producer<TwoMaps>& p, const ProjCondArgs
     lds_barrier();
 }
 
-template <bool TwoMaps>
+template <bool TwoMaps, bool Off32>
 __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a, CamTable cams,
                                                                   int32_t m_tiles,
                                                                   int32_t n_tiles,
@@ -239,26 +285,24 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
         }
         __syncthreads();                                          // (1) tokens parked
 
-        Producer<TwoMaps> p;
+        Producer<TwoMaps, Off32> p;
         p.feat = reinterpret_cast<const uint4*>(a.feat);
-        p.wgt = reinterpret_cast<const uint4*>(a.weight);
         p.vpr = a.C >> 3;
         p.kbase = 0;
-        p.vprw = (a.C + a.C1) >> 3;
-        p.D = a.D;
         p.W = a.W;
-        p.n0 = n0;
         p.ptid = ptid;
-        p.lane = lane;
-        p.pw = wave - N_CONS;
         p.gv = ptid & 7;
+        p.wl.init(a.weight, (a.C + a.C1) >> 3, a.D, n0,
+                  __builtin_amdgcn_readfirstlane(wave - N_CONS), lane);
 #pragma unroll
         for (int u = 0; u < G_ITEMS; ++u) p.gt[u] = s_tok[(ptid + u * kProdThreads) >> 3];
+        p.set_items();
         Gq gq;
         p.gather_issue(gq, 0);
         __syncthreads();                                          // (2) sA1 free again
-        p.w_issue(sW0, 0);
-        p.commit(gq, sA0);
+        wait_vmcnt<0>();
+        p.wl.issue(sW0, 0);
+        p.commit(gq, 0, sA0);
         if constexpr (TwoMaps) {
             if (k1 == 1) p.to_map1(a, cams, m0, k1);
         }
@@ -316,8 +360,14 @@ hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hi
     ProjCondArgs args = a;
     CamTable tab = cams;
     void* params[] = {&args, &tab, &m_tiles, &n_tiles, &per_xcd, &null_tiles};
-    const void* fn = a.C1 > 0 ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<true>)
-                              : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false>);
+    // corner offsets fit 32 bits when the map is under 4 GiB. Two maps keep
+    // the 64-bit addressing: their second set of offsets would not fit the
+    // producers' registers next to the map switch
+    const bool off32 = a.C1 == 0 && (uint64_t)a.batch * (uint64_t)a.H * (uint64_t)a.W *
+                                            (uint64_t)a.C * 2u < ((uint64_t)1 << 32);
+    const void* fn = a.C1 > 0 ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<true, false>)
+                     : off32  ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, true>)
+                              : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, false>);
     return hipLaunchKernel(fn,
                            dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
 }

@@ -119,11 +119,15 @@ struct Producer {
     int gv;                          // vector of each gathered 128-byte segment
     int4 gt[G_ITEMS];                // token_entry of each item (used without Off32)
     uint32_t off[G_ITEMS][4];        // corner rows' byte offsets + 16 gv (Off32)
+    __amdgpu_buffer_rsrc_t rsrc;     // the map as a buffer resource (Off32)
     float wt[G_ITEMS][4];            // bilinear weights, 0 for a padding token
     WLoader wl;
 
     // Offsets and weights of the items from their corner metadata gt.
     __device__ __forceinline__ void set_items() {
+        if constexpr (Off32)
+            rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(feat), (short)0,
+                                                     (int)0xffffffffu, 0x00020000);
 #pragma unroll
         for (int u = 0; u < G_ITEMS; ++u) {
             const int32_t r00 = gt[u].x, steps = gt[u].y;
@@ -165,13 +169,15 @@ struct Producer {
     __device__ __forceinline__ void gather_issue(Gq& gq, int kc) const {
         const int kl = TwoMaps ? kc - kbase : kc;
         if constexpr (Off32) {
-            const char* b = reinterpret_cast<const char*>(feat) + kl * 128;
             if ((kl + 1) * 8 <= vpr) {
+                // buffer loads: map base in a resource, the chunk as the scalar
+                // offset, the item's 32-bit offset as is
 #pragma unroll
                 for (int u = 0; u < G_ITEMS; ++u)
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        gq[u][k] = *reinterpret_cast<const uint4*>(b + off[u][k]);
+                        gq[u][k] = __builtin_bit_cast(
+                            uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off[u][k], kl * 128, 0));
             } else {
                 // K tail: the vector index kv clamped to the row, from the map
                 // base. off - 16 gv is the row's byte offset, and adding 16 kv

@@ -7,7 +7,8 @@
 // tokens at a time: lanes 0..TPW-1 project one each, then the wave walks the
 // TPW tokens, broadcasting each token's corner metadata from its lane
 // (readlane) and gathering its corner rows with the lanes spread over the
-// channels (16-byte vectors, 64 lanes = 1 KB of a row per instruction). Map 0
+// channels (16-byte vectors, 64 lanes = 1 KB of a row per instruction), two
+// tokens at a time so that both tokens' loads are in flight together. Map 0
 // and map 1 vectors at the same channel offset sit in the same lane, so the
 // cosine's dot product and norms need no shuffles until the per-token wave
 // reduction. Samples are blended and rounded exactly as the fused kernel
@@ -133,8 +134,75 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a, CamTable c
         const int64_t cnt = a.n - base < TPW ? a.n - base : TPW;
         inside += (double)__builtin_popcountll(__ballot(in));
         tokens += (double)cnt;
-        // ---- the wave walks its tokens
-        for (int j = 0; j < (int)cnt; ++j) {
+        // ---- the wave walks its tokens two at a time: both tokens' corner
+        // loads are in flight together and their reductions interleave
+        int j = 0;
+        for (; j + 1 < (int)cnt; j += 2) {
+            const Meta a0 = lane_meta(m0, j), b0 = lane_meta(m0, j + 1);
+            const Meta a1 = lane_meta(m1, j), b1 = lane_meta(m1, j + 1);
+            double dA = 0.0, xA = 0.0, yA = 0.0, dB = 0.0, xB = 0.0, yB = 0.0;
+            for (int v = lane; v < vpr0; v += 64) {
+                float pa[EPV], pb[EPV];
+                sample_vec<Bf16>(f0, vpr0, a0, a.W0, v, pa);
+                sample_vec<Bf16>(f0, vpr0, b0, a.W0, v, pb);
+                if (cosine) {
+                    float qa[EPV], qb[EPV];
+                    sample_vec<Bf16>(f1, vpr1, a1, a.W1, v, qa);
+                    sample_vec<Bf16>(f1, vpr1, b1, a.W1, v, qb);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        const double u = pa[e], w = qa[e], u2 = pb[e], w2 = qb[e];
+                        s0 += u + u2;
+                        s1 += w + w2;
+                        dA = fma(u, w, dA);
+                        xA = fma(u, u, xA);
+                        yA = fma(w, w, yA);
+                        dB = fma(u2, w2, dB);
+                        xB = fma(u2, u2, xB);
+                        yB = fma(w2, w2, yB);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        const double u = pa[e], u2 = pb[e];
+                        s0 += u + u2;
+                        q0 = fma(u, u, fma(u2, u2, q0));
+                    }
+                }
+            }
+            if (cosine) {
+                q0 += xA + xB;
+                q1 += yA + yB;
+                dA = wave_sum(dA);
+                dB = wave_sum(dB);
+                xA = wave_sum(xA);
+                xB = wave_sum(xB);
+                yA = wave_sum(yA);
+                yB = wave_sum(yB);
+                if (xA > 0.0 && yA > 0.0) {
+                    cos_sum += dA / (sqrt(xA) * sqrt(yA));
+                    cos_cnt += 1.0;
+                }
+                if (xB > 0.0 && yB > 0.0) {
+                    cos_sum += dB / (sqrt(xB) * sqrt(yB));
+                    cos_cnt += 1.0;
+                }
+            } else if (two) {
+                for (int v = lane; v < vpr1; v += 64) {
+                    float qa[EPV], qb[EPV];
+                    sample_vec<Bf16>(f1, vpr1, a1, a.W1, v, qa);
+                    sample_vec<Bf16>(f1, vpr1, b1, a.W1, v, qb);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        const double w = qa[e], w2 = qb[e];
+                        s1 += w + w2;
+                        q1 = fma(w, w, fma(w2, w2, q1));
+                    }
+                }
+            }
+        }
+        // ---- an odd last token alone
+        if (j < (int)cnt) {
             const Meta t0 = lane_meta(m0, j);
             double dot = 0.0, n0 = 0.0, n1 = 0.0;
             for (int v = lane; v < vpr0; v += 64) {

@@ -280,8 +280,17 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
 
     if (producer) {
         const int ptid = tid - N_CONS * 64;
+        Producer<TwoMaps, Off32> p;
+        p.wl.init(a.weight, (a.C + a.C1) >> 3, a.D, n0,
+                  __builtin_amdgcn_readfirstlane(wave - N_CONS), lane);
+        // W of chunk 0 does not depend on the tokens: queue it before
+        // projecting them, so that its latency overlaps the projection and
+        // the first gather
+        p.wl.issue(sW0, 0);
         // ---- project the tile's tokens; per token park (top-left row, the
-        // row steps to the right / lower corner, the two fractions) in sA1
+        // row steps to the right / lower corner, the two fractions) in sA1.
+        // sA1 is next written after B_0, which every producer passes only
+        // once its reads of this table have completed.
         int4* s_tok = reinterpret_cast<int4*>(sA1);            // [BM]
         if (ptid < BM) {
             const int64_t t = m0 + ptid;
@@ -289,25 +298,20 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
             s_tok[ptid] = token_entry(a, cams, t, a.H, a.W, &mk);
             if (a.mask && nt == 0 && t < a.n) a.mask[t] = mk;
         }
-        __syncthreads();                                          // (1) tokens parked
+        lds_barrier();                                            // tokens parked
 
-        Producer<TwoMaps, Off32> p;
         p.feat = reinterpret_cast<const uint4*>(a.feat);
         p.vpr = a.C >> 3;
         p.kbase = 0;
         p.W = a.W;
         p.ptid = ptid;
         p.gv = ptid & 7;
-        p.wl.init(a.weight, (a.C + a.C1) >> 3, a.D, n0,
-                  __builtin_amdgcn_readfirstlane(wave - N_CONS), lane);
 #pragma unroll
         for (int u = 0; u < G_ITEMS; ++u) p.gt[u] = s_tok[(ptid + u * kProdThreads) >> 3];
         p.set_items();
         Gq gq;
         p.gather_issue(gq, 0);
-        __syncthreads();                                          // (2) sA1 free again
-        wait_vmcnt<0>();
-        p.wl.issue(sW0, 0);
+        wait_vmcnt<0>();                                          // W and corners of chunk 0
         p.commit(gq, 0, sA0);
         if constexpr (TwoMaps) {
             if (k1 == 1) p.to_map1(a, cams, m0, k1);
@@ -344,8 +348,7 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
     for (int j = 0; j < FJ; ++j)
 #pragma unroll
         for (int i = 0; i < TI; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();                                              // (1)
-    __syncthreads();                                              // (2)
+    lds_barrier();                                                // tokens parked
     lds_barrier();                                                // B_0
     for (int kc = 0; kc < nk2; kc += 2) {
         consume(acc, lane, cw, sA0, sW0);

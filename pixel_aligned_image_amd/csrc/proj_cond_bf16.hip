@@ -27,10 +27,14 @@
 //
 // Per 64-channel K chunk k (barrier B_k before it):
 //   consumers: MFMA on S stage k%2 and W stage k%2;
-//   producers: queue W of chunk k+1 into W stage (k+1)%2 (freed at B_k),
-//     blend chunk k+1 (queued a chunk ago) into S stage (k+1)%2, queue the
-//     corner rows of chunk k+2, then wait for their own W loads;
+//   producers: wait for the corner rows of chunk k+1 (queued a chunk ago),
+//     queue W of chunk k+1 into W stage (k+1)%2 (freed at B_k), blend chunk
+//     k+1 into S stage (k+1)%2, queue the corner rows of chunk k+2, then wait
+//     for their own W loads;
 //   B_{k+1}.
+// Per tile, each producer item keeps its corner rows' offsets and its
+// bilinear weights (Producer), so a chunk's gather and W loads need no
+// vector address arithmetic.
 // W tile (512 rows x 128 bytes) arrives through global_load_lds_dwordx4,
 // eight full 128-byte rows per wave instruction (16 rows x 64 bytes, which
 // is what loading MFMA fragments straight from a row-major W would do, moves

@@ -195,7 +195,7 @@ def run_extra(p3d, synth, stream, reps, lead_step):
         "frac": rq_bytes / (rq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "note": "100k tokens = 3.2 MB: launch-latency bound, far from the HBM roofline"}
     out["grid_nodes"] = {
-        "workload": w.name, "kernel": "proj_cond_bf16_kernel<false>", "tokens": n,
+        "workload": w.name, "kernel": "proj_cond_bf16_kernel<false, true>", "tokens": n,
         "mean_ms": nodes_ms, "bound": "mfma", "flops_per_launch": flops,
         "achieved": flops / (nodes_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s", "frac": flops / (nodes_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
@@ -219,7 +219,7 @@ def run_extra(p3d, synth, stream, reps, lead_step):
     two_ms = time_events(two, reps, stream)
     flops = 2.0 * n * w.k_total * w.out_dim
     out["two_maps"] = {
-        "workload": w.name, "kernel": "proj_cond_bf16_kernel<true>", "tokens": n,
+        "workload": w.name, "kernel": "proj_cond_bf16_kernel<true, true>", "tokens": n,
         "null_rows": nn, "maps": ["%dx%dx%dx%d" % tuple(m.shape) for m in maps],
         "mean_ms": two_ms, "tokens_per_s": n / (two_ms * 1e-3), "bound": "mfma",
         "flops_per_launch": flops, "achieved": flops / (two_ms * 1e-3) / 1e12,

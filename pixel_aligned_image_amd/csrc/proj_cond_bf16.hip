@@ -373,14 +373,17 @@ hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hi
     ProjCondArgs args = a;
     CamTable tab = cams;
     void* params[] = {&args, &tab, &m_tiles, &n_tiles, &per_xcd, &null_tiles};
-    // corner offsets fit 32 bits when the map is under 4 GiB. Two maps keep
-    // the 64-bit addressing: their second set of offsets would not fit the
-    // producers' registers next to the map switch
-    const bool off32 = a.C1 == 0 && (uint64_t)a.batch * (uint64_t)a.H * (uint64_t)a.W *
-                                            (uint64_t)a.C * 2u < ((uint64_t)1 << 32);
-    const void* fn = a.C1 > 0 ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<true, false>)
-                     : off32  ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, true>)
-                              : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, false>);
+    // corner offsets fit 32 bits when every map is under 4 GiB
+    const auto map_bytes = [&](int32_t H, int32_t W, int32_t C) {
+        return (uint64_t)a.batch * (uint64_t)H * (uint64_t)W * (uint64_t)C * 2u;
+    };
+    const bool off32 = map_bytes(a.H, a.W, a.C) < ((uint64_t)1 << 32) &&
+                       (a.C1 == 0 || map_bytes(a.H1, a.W1, a.C1) < ((uint64_t)1 << 32));
+    const void* fn =
+        a.C1 > 0 ? (off32 ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<true, true>)
+                          : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<true, false>))
+                 : (off32 ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, true>)
+                          : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, false>));
     return hipLaunchKernel(fn,
                            dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
 }

@@ -206,18 +206,21 @@ def test_proj_cond_extra_workloads(orc, name):
     say("  max|diff|/max|Y| %.3e corr %.8f" % st)
 
 
-def test_proj_cond_map_of_4gib(orc):
-    """A single bf16 map of exactly 4 GiB (1 x 1024 x 1024 x 2048): its corner
+@pytest.mark.parametrize("two_maps", [False, True], ids=["one_map", "two_maps"])
+def test_proj_cond_map_of_4gib(orc, two_maps):
+    """A bf16 map of exactly 4 GiB (1 x 1024 x 1024 x 2048): its corner
     offsets no longer fit 32 bits, so the fused kernel takes its 64-bit
-    gather addressing (smaller maps take the 32-bit one). The map is zero
-    except around the pixels the tokens project to (chosen by the oracle's
-    projection), which hold seeded values; every row is checked."""
+    gather addressing (launches whose maps are all smaller take the 32-bit
+    one). Alone, or as map 1 behind a small seeded 32 x 32 x 64 map 0. The
+    large map is zero except around the pixels the tokens project to (chosen
+    by the oracle's projection), which hold seeded values; every row is
+    checked."""
     B, H, W, C, D, R, n, n_null = 1, 1024, 1024, 2048, 264, 256, 1500, 7
     coords = synth.random_coords(R, B, n, seed=4242)
     fovs = [40.0]
     fo, do = oracle_cameras(orc, fovs, [None], W)
     pix = orc.project(coords, n, R, fo, do, H, W)["pixel"]
-    say("4 GiB map: %d tokens" % n)
+    say("4 GiB map: %d tokens, two maps %s" % (n, two_maps))
     feat = np.zeros((B, H, W, C), np.uint16)
     rng = np.random.default_rng(4243)
     ys = np.clip(pix[:, 1:2] + np.arange(-1, 3), 0, H - 1)
@@ -225,8 +228,12 @@ def test_proj_cond_map_of_4gib(orc):
     rows = np.unique((ys[:, :, None] * W + xs[:, None, :]).reshape(-1))
     flat = feat.reshape(-1, C)
     flat[rows] = synth.bf16_bits(rng.standard_normal((len(rows), C)).astype(np.float32))
-    Wt = synth.bf16_bits((rng.standard_normal((D, C)) * 0.05).astype(np.float32))
+    maps = [feat]
+    if two_maps:
+        maps = [synth.bf16_bits(rng.standard_normal((B, 32, 32, 64)).astype(np.float32)), feat]
+    K = sum(m.shape[3] for m in maps)
+    Wt = synth.bf16_bits((rng.standard_normal((D, K)) * 0.05).astype(np.float32))
     b = synth.bf16_bits((rng.standard_normal(D) * 0.05).astype(np.float32))
-    st = _run(orc, coords, n, R, fovs, [None], [feat], Wt, b, n_null, True,
+    st = _run(orc, coords, n, R, fovs, [None], maps, Wt, b, n_null, True,
               np.arange(n + n_null), "cell_centres", W)
     say("  max|diff|/max|Y| %.3e corr %.8f" % st)

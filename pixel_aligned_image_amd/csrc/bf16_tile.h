@@ -115,9 +115,11 @@ struct WLoader {
     }
 };
 
-// Consumer: the chunk's 2 x 8 x 4 MFMAs. The other consumer wave on the SIMD
+// Consumer: the chunk's 2 x TIt x 4 MFMAs over the first 16 TIt tokens of
+// the stage (TIt = TI for a full tile). The other consumer wave on the SIMD
 // covers the LDS latency of the fragment reads.
-__device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TI], int lane, int cw,
+template <int TIt = TI>
+__device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TIt], int lane, int cw,
                                         const uint4* __restrict__ sa,
                                         const uint4* __restrict__ sw) {
     const int n = lane & 15, g4 = lane >> 4;
@@ -129,7 +131,7 @@ __device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TI], int lane, int cw
         for (int j = 0; j < FJ; ++j)
             wf[j] = __builtin_bit_cast(bf16x8_t, sw[slot(cw * WN + j * 16 + n, v)]);
 #pragma unroll
-        for (int i = 0; i < TI; ++i) {
+        for (int i = 0; i < TIt; ++i) {
             const bf16x8_t sf = __builtin_bit_cast(bf16x8_t, sa[slot(i * 16 + n, v)]);
 #pragma unroll
             for (int j = 0; j < FJ; ++j)
@@ -141,18 +143,20 @@ __device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TI], int lane, int cw
 
 // Epilogue: + bias (bf16 parameters), optionally + the value already in
 // `out` (Accumulate: a residual add, rounded once), round to bf16, stage the
-// wave's 128 x 64 block in the free W stages (token-major 128-byte rows, the
-// same slot swizzle) and write 16-byte row pieces. Lane l of block (j, i)
+// wave's 16 TIt x 64 block in the free W stages (token-major 128-byte rows,
+// the same slot swizzle) and write 16-byte row pieces. Lane l of block (j, i)
 // holds features 4*(l/16) + r of token l % 16. out is [n, D] bf16; rows at or
 // past n are not touched.
 constexpr int OLD_BATCH = 4;        // residual loads in flight together (registers)
 static_assert(TI % OLD_BATCH == 0, "residual batches");
 
-template <bool Accumulate>
-__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TI], int lane, int cw,
+template <bool Accumulate, int TIt = TI>
+__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TIt], int lane, int cw,
                                            int32_t n0, int64_t m0, int64_t n, int32_t D,
                                            const uint16_t* bias16, void* out,
                                            uint4* __restrict__ sW0, uint4* __restrict__ sW1) {
+    constexpr int BATCH = TIt < OLD_BATCH ? TIt : OLD_BATCH;
+    static_assert(TIt % BATCH == 0, "residual batches");
     const int fbase = n0 + cw * WN;
     const int dv = D >> 3;                            // 16-byte vectors per output row
     uint4* stage4 = (cw < N_CONS / 2 ? sW0 : sW1) + (cw % (N_CONS / 2)) * (BM * 8);
@@ -171,13 +175,13 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TI], int lan
         if (bias16) b2 = *reinterpret_cast<const uint2*>(bias16 + fc);
         if (!fin) b2 = make_uint2(0, 0);
         const float bv[4] = {bf16lo(b2.x), bf16hi(b2.x), bf16lo(b2.y), bf16hi(b2.y)};
-        uint2 old[TI];
+        uint2 old[TIt];
 #pragma unroll
-        for (int i = 0; i < TI; ++i) {
-            if (Accumulate && i % OLD_BATCH == 0) {
-                // the residual values of the next OLD_BATCH token blocks
+        for (int i = 0; i < TIt; ++i) {
+            if (Accumulate && i % BATCH == 0) {
+                // the residual values of the next BATCH token blocks
 #pragma unroll
-                for (int u = i; u < i + OLD_BATCH; ++u) {
+                for (int u = i; u < i + BATCH; ++u) {
                     const int64_t tok = m0 + u * 16 + (lane & 15);
                     old[u] = *reinterpret_cast<const uint2*>(out16 + (tok < n ? tok : n - 1) * D + fc);
                 }
@@ -203,7 +207,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TI], int lan
     __syncthreads();                                              // consumers staged
     uint4* out4 = reinterpret_cast<uint4*>(out);
 #pragma unroll
-    for (int r = 0; r < BM * 8 / 64; ++r) {
+    for (int r = 0; r < TIt * 16 * 8 / 64; ++r) {
         const int q = r * 64 + lane;
         const int t = q >> 3, cv = q & 7;
         const int64_t tok = m0 + t;

@@ -53,6 +53,13 @@
 // Tile order: workgroup g runs on XCD g % 8; each XCD walks a contiguous
 // range of (token tile, N tile) pairs, N fastest, so the N tiles of a token
 // tile and its neighbours share corner rows in that XCD's L2.
+// Tail: with one workgroup per CU the tiles run in rounds of one per CU.
+// When the tiles past the last full round fit one round four times over,
+// each of them runs as four 32-token parts (the same code with two token
+// blocks per consumer and one gathered vector per producer thread), queued
+// after every whole tile.
+#include <atomic>
+
 #include "bf16_tile.h"
 
 namespace p3d {
@@ -61,8 +68,13 @@ namespace {
 
 using namespace tile;
 
-constexpr int G_ITEMS = BM * (BK / 8) / kProdThreads;   // gathered vectors per producer thread
-constexpr int NULL_VEC = BM * BN / 8;                   // 16-byte vectors of a null block
+// Tail sub-tiles: 32 tokens (TI_TAIL token blocks) of a 128-token tile.
+constexpr int TI_TAIL = 2;
+constexpr int TAIL_SPLIT = TI / TI_TAIL;                // sub-tiles per tile
+
+// Gathered vectors per producer thread for a tile of TIt token blocks.
+template <int TIt>
+constexpr int g_items() { return TIt * 16 * (BK / 8) / kProdThreads; }
 
 __device__ __forceinline__ uint4 blend_bf16(const uint4 (&q)[4], const float (&w)[4]) {
     const uint32_t* a = reinterpret_cast<const uint32_t*>(&q[0]);
@@ -82,7 +94,8 @@ __device__ __forceinline__ uint4 blend_bf16(const uint4 (&q)[4], const float (&w
     return o;
 }
 
-typedef uint4 Gq[G_ITEMS][4];
+template <int G>
+using Gq = uint4[G][4];
 
 // Corner metadata of token t on an H x W map: (top-left corner row, the 0/1
 // row steps to the right and lower corners, x fraction, y fraction); a token
@@ -113,7 +126,7 @@ __device__ __forceinline__ int4 token_entry(const ProjCondArgs& a, const CamTabl
 // offsets and its four bilinear weights; a chunk's gather is then a uniform
 // base (map, chunk: scalar registers) plus those offsets, with no vector
 // address arithmetic, and the blend reuses the weights.
-template <bool TwoMaps, bool Off32>
+template <bool TwoMaps, bool Off32, int G>
 struct Producer {
     const uint4* feat;               // map of the chunks being gathered
     int vpr;                         // 16-byte vectors per row of that map
@@ -121,10 +134,10 @@ struct Producer {
     int W;                           // that map's width (row step between image rows)
     int ptid;
     int gv;                          // vector of each gathered 128-byte segment
-    int4 gt[G_ITEMS];                // token_entry of each item (used without Off32)
-    uint32_t off[G_ITEMS][4];        // corner rows' byte offsets + 16 gv (Off32)
+    int4 gt[G];                // token_entry of each item (used without Off32)
+    uint32_t off[G][4];        // corner rows' byte offsets + 16 gv (Off32)
     __amdgpu_buffer_rsrc_t rsrc;     // the map as a buffer resource (Off32)
-    float wt[G_ITEMS][4];            // bilinear weights, 0 for a padding token
+    float wt[G][4];            // bilinear weights, 0 for a padding token
     WLoader wl;
 
     // Offsets and weights of the items from their corner metadata gt.
@@ -133,7 +146,7 @@ struct Producer {
             rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(feat), (short)0,
                                                      (int)0xffffffffu, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < G_ITEMS; ++u) {
+        for (int u = 0; u < G; ++u) {
             const int32_t r00 = gt[u].x, steps = gt[u].y;
             const int32_t dx = steps & 1, dyw = (steps & 2) ? W : 0;
             const int32_t rows[4] = {r00, r00 + dx, r00 + dyw, r00 + dyw + dx};
@@ -160,7 +173,7 @@ struct Producer {
         kbase = k1;
         W = a.W1;
 #pragma unroll
-        for (int u = 0; u < G_ITEMS; ++u)
+        for (int u = 0; u < G; ++u)
             gt[u] = token_entry(a, cams, m0 + ((ptid + u * kProdThreads) >> 3), a.H1, a.W1,
                                 nullptr);
         set_items();
@@ -170,14 +183,14 @@ struct Producer {
     // map's channels not a multiple of 64, or the padding chunk) clamps the
     // address; commit() zeroes those values (zeroing here would make the
     // loads' registers wait).
-    __device__ __forceinline__ void gather_issue(Gq& gq, int kc) const {
+    __device__ __forceinline__ void gather_issue(Gq<G>& gq, int kc) const {
         const int kl = TwoMaps ? kc - kbase : kc;
         if constexpr (Off32) {
             if ((kl + 1) * 8 <= vpr) {
                 // buffer loads: map base in a resource, the chunk as the scalar
                 // offset, the item's 32-bit offset as is
 #pragma unroll
-                for (int u = 0; u < G_ITEMS; ++u)
+                for (int u = 0; u < G; ++u)
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
                         gq[u][k] = __builtin_bit_cast(
@@ -190,7 +203,7 @@ struct Producer {
                 const uint32_t kv16 = (uint32_t)min(kl * 8 + gv, vpr - 1) * 16u;
                 const uint32_t gv16 = (uint32_t)gv * 16u;
 #pragma unroll
-                for (int u = 0; u < G_ITEMS; ++u)
+                for (int u = 0; u < G; ++u)
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
                         gq[u][k] = *reinterpret_cast<const uint4*>(f + (off[u][k] - gv16 + kv16));
@@ -199,7 +212,7 @@ struct Producer {
         }
         const int kv = min(kl * 8 + gv, vpr - 1);
 #pragma unroll
-        for (int u = 0; u < G_ITEMS; ++u) {
+        for (int u = 0; u < G; ++u) {
             // the 32-bit row index stays live, not four hoisted 64-bit
             // addresses (those would not fit in the registers)
             int32_t r00 = gt[u].x, steps = gt[u].y;
@@ -214,11 +227,11 @@ struct Producer {
     // Blend the queued vectors of chunk kc (bilinear weights computed as in
     // the standalone sampler) and store the bf16 S chunk into sa; vectors
     // past the map's channels store zeros.
-    __device__ __forceinline__ void commit(const Gq& gq, int kc, uint4* __restrict__ sa) const {
+    __device__ __forceinline__ void commit(const Gq<G>& gq, int kc, uint4* __restrict__ sa) const {
         const int kl = TwoMaps ? kc - kbase : kc;
         const bool dead = kl * 8 + gv >= vpr;
 #pragma unroll
-        for (int u = 0; u < G_ITEMS; ++u) {
+        for (int u = 0; u < G; ++u) {
             const uint4 v = blend_bf16(gq[u], wt[u]);
             sa[slot((ptid + u * kProdThreads) >> 3, gv)] = dead ? make_uint4(0, 0, 0, 0) : v;
         }
@@ -230,10 +243,10 @@ struct Producer {
 // chunk k1 on), then this wave's W loads must have landed before the
 // barrier. The LDS stages are restrict parameters so that the compiler can
 // tell the direct W loads apart from the S stores.
-template <bool TwoMaps, bool Off32>
-__device__ __forceinline__ void produce(Producer<TwoMaps, Off32>& p, const ProjCondArgs& a,
+template <bool TwoMaps, bool Off32, int G>
+__device__ __forceinline__ void produce(Producer<TwoMaps, Off32, G>& p, const ProjCondArgs& a,
                                         const CamTable& cams, int64_t m0, int k1, int kc,
-                                        int nk2, Gq& gq, uint4* __restrict__ sa_n,
+                                        int nk2, Gq<G>& gq, uint4* __restrict__ sa_n,
                                         uint4* __restrict__ sw_n) {
     if (kc + 1 < nk2) {
         // Only this chunk's corners are in flight here: wait for them
@@ -248,7 +261,7 @@ __device__ __forceinline__ void produce(Producer<TwoMaps, Off32>& p, const ProjC
         }
         if (kc + 2 < nk2) {
             p.gather_issue(gq, kc + 2);
-            wait_vmcnt<G_ITEMS * 4>();               // the queued gather may stay in flight
+            wait_vmcnt<G * 4>();               // the queued gather may stay in flight
         } else {
             wait_vmcnt<0>();
         }
@@ -256,25 +269,27 @@ __device__ __forceinline__ void produce(Producer<TwoMaps, Off32>& p, const ProjC
     lds_barrier();
 }
 
-template <bool TwoMaps, bool Off32>
-__global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a, CamTable cams,
-                                                                  int32_t m_tiles,
-                                                                  int32_t n_tiles,
-                                                                  int32_t per_xcd,
-                                                                  int32_t null_tiles) {
-    __shared__ uint4 sW0[BN * 8], sW1[BN * 8];     // 2 x 64 KB
-    __shared__ uint4 sA0[BM * 8], sA1[BM * 8];     // 2 x 16 KB
-
+// One tile: 16 TIt tokens starting at token m0 (TIt = TI: a whole 128-token
+// tile; TIt = TI_TAIL: sub-tile `sub` of tile mt), features n0 .. n0 + 511.
+// The tile also writes its share of the null rows: rows m0 - 128 mt ..
+// m0 - 128 mt + 16 TIt - 1 of every 128-row null block q = mt, mt + m_tiles,
+// ..., for the same features.
+template <bool TwoMaps, bool Off32, int TIt>
+__device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& cams,
+                                         int32_t mt, int32_t nt, int sub, int32_t m_tiles,
+                                         int32_t null_tiles, uint4* __restrict__ sW0,
+                                         uint4* __restrict__ sW1, uint4* __restrict__ sA0,
+                                         uint4* __restrict__ sA1) {
+    constexpr int BMt = TIt * 16;
+    constexpr int G = g_items<TIt>();
+    constexpr int NULL_VEC = BMt * BN / 8;                // 16-byte vectors of a null share
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const bool producer = wave >= N_CONS;
 
-    const int32_t g = blockIdx.x;
-    const int32_t tile = (g & 7) * per_xcd + (g >> 3);
-    if (tile >= m_tiles * n_tiles) return;
-    const int32_t mt = tile / n_tiles, nt = tile - mt * n_tiles;
-    const int64_t m0 = (int64_t)mt * BM;
+    const int32_t r0 = sub * BMt;                          // first row within the 128-row tile
+    const int64_t m0 = (int64_t)mt * BM + r0;
     const int32_t n0 = nt * BN;
     const int nk = (a.C + a.C1 + BK - 1) / BK;
     const int k1 = a.C1 > 0 ? a.C / BK : 1 << 30;     // first chunk of map 1
@@ -284,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
 
     if (producer) {
         const int ptid = tid - N_CONS * 64;
-        Producer<TwoMaps, Off32> p;
+        Producer<TwoMaps, Off32, G> p;
         p.wl.init(a.weight, (a.C + a.C1) >> 3, a.D, n0,
                   __builtin_amdgcn_readfirstlane(wave - N_CONS), lane);
         // W of chunk 0 does not depend on the tokens: queue it before
@@ -295,8 +310,8 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
         // row steps to the right / lower corner, the two fractions) in sA1.
         // sA1 is next written after B_0, which every producer passes only
         // once its reads of this table have completed.
-        int4* s_tok = reinterpret_cast<int4*>(sA1);            // [BM]
-        if (ptid < BM) {
+        int4* s_tok = reinterpret_cast<int4*>(sA1);            // [BMt]
+        if (ptid < BMt) {
             const int64_t t = m0 + ptid;
             uint8_t mk = 0;
             s_tok[ptid] = token_entry(a, cams, t, a.H, a.W, &mk);
@@ -311,9 +326,9 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
         p.ptid = ptid;
         p.gv = ptid & 7;
 #pragma unroll
-        for (int u = 0; u < G_ITEMS; ++u) p.gt[u] = s_tok[(ptid + u * kProdThreads) >> 3];
+        for (int u = 0; u < G; ++u) p.gt[u] = s_tok[(ptid + u * kProdThreads) >> 3];
         p.set_items();
-        Gq gq;
+        Gq<G> gq;
         p.gather_issue(gq, 0);
         wait_vmcnt<0>();                                          // W and corners of chunk 0
         p.commit(gq, 0, sA0);
@@ -321,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
             if (k1 == 1) p.to_map1(a, cams, m0, k1);
         }
         p.gather_issue(gq, 1);
-        wait_vmcnt<G_ITEMS * 4>();
+        wait_vmcnt<G * 4>();
         lds_barrier();                                            // B_0
         for (int kc = 0; kc < nk2; kc += 2) {
             produce(p, a, cams, m0, k1, kc, nk2, gq, sA1, sW1);
@@ -329,12 +344,12 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
         }
         __syncthreads();                                          // consumers staged
 
-        // ---- null blocks of this workgroup: q = mt, mt + m_tiles, ...
+        // ---- this tile's share of the null blocks q = mt, mt + m_tiles, ...
         const uint4* bias4 = reinterpret_cast<const uint4*>(a.bias);
         for (int32_t q = mt; q < null_tiles; q += m_tiles) {
             for (int idx = ptid; idx < NULL_VEC; idx += kProdThreads) {
                 const int r = idx >> 6, cv = idx & 63;         // 64 vectors per 512-wide row
-                const int64_t row = a.n + (int64_t)q * BM + r;
+                const int64_t row = a.n + (int64_t)q * BM + r0 + r;
                 const int colv = (n0 >> 3) + cv;
                 if (row < a.n + a.n_null && colv < dv) {
                     const uint4 val = bias4 ? bias4[colv] : make_uint4(0, 0, 0, 0);
@@ -347,32 +362,92 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(ProjCondArgs a
 
     // ---------------------------------------------------------- consumers
     const int cw = wave;
-    f32x4_t acc[FJ][TI];
+    f32x4_t acc[FJ][TIt];
 #pragma unroll
     for (int j = 0; j < FJ; ++j)
 #pragma unroll
-        for (int i = 0; i < TI; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < TIt; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     lds_barrier();                                                // tokens parked
     lds_barrier();                                                // B_0
     for (int kc = 0; kc < nk2; kc += 2) {
-        consume(acc, lane, cw, sA0, sW0);
-        consume(acc, lane, cw, sA1, sW1);
+        consume<TIt>(acc, lane, cw, sA0, sW0);
+        consume<TIt>(acc, lane, cw, sA1, sW1);
     }
 
-    store_tile<false>(acc, lane, cw, n0, m0, a.n, a.D,
-                      reinterpret_cast<const uint16_t*>(a.bias), a.out, sW0, sW1);
+    store_tile<false, TIt>(acc, lane, cw, n0, m0, a.n, a.D,
+                           reinterpret_cast<const uint16_t*>(a.bias), a.out, sW0, sW1);
+}
+
+// Work of workgroup g, which runs on XCD x = g % 8 as its (g / 8)-th:
+// whole tiles x * big_per_xcd .. x * big_per_xcd + big_per_xcd - 1 (below
+// n_big), then tail sub-tiles x * small_per_xcd + ... (below n_small): tile
+// n_big + s / TAIL_SPLIT, part s % TAIL_SPLIT. Tiles are numbered token tile
+// major, N tile fastest.
+template <bool TwoMaps, bool Off32>
+__global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(
+    ProjCondArgs a, CamTable cams, int32_t m_tiles, int32_t n_tiles, int32_t n_big,
+    int32_t big_per_xcd, int32_t n_small, int32_t small_per_xcd, int32_t null_tiles) {
+    __shared__ uint4 sW0[BN * 8], sW1[BN * 8];     // 2 x 64 KB
+    __shared__ uint4 sA0[BM * 8], sA1[BM * 8];     // 2 x 16 KB
+
+    const int32_t g = blockIdx.x;
+    const int32_t x = g & 7, i = g >> 3;
+    if (i < big_per_xcd) {
+        const int32_t tile = x * big_per_xcd + i;
+        if (tile >= n_big) return;
+        const int32_t mt = tile / n_tiles;
+        run_tile<TwoMaps, Off32, TI>(a, cams, mt, tile - mt * n_tiles, 0, m_tiles, null_tiles,
+                                     sW0, sW1, sA0, sA1);
+    } else {
+        const int32_t st = x * small_per_xcd + (i - big_per_xcd);
+        if (st >= n_small) return;
+        const int32_t tile = n_big + st / TAIL_SPLIT;
+        const int32_t mt = tile / n_tiles;
+        run_tile<TwoMaps, Off32, TI_TAIL>(a, cams, mt, tile - mt * n_tiles, st % TAIL_SPLIT,
+                                          m_tiles, null_tiles, sW0, sW1, sA0, sA1);
+    }
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 }  // namespace
 
+// Tail split: one workgroup per CU, so T tiles take ceil(T / CUs) rounds and
+// the last round may leave most CUs idle. When the R tiles past the last
+// full round fit one round as 32-token sub-tiles (TAIL_SPLIT R <= CUs), they
+// run as sub-tiles instead: each moves the full W stream of its N tile and
+// a quarter of the gather, so it takes well under a whole tile's time.
 hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hipStream_t s) {
     int32_t m_tiles = (int32_t)((a.n + BM - 1) / BM);
     int32_t n_tiles = (a.D + BN - 1) / BN;
-    int32_t per_xcd = (int32_t)(((int64_t)m_tiles * n_tiles + 7) / 8);
+    const int32_t tiles = m_tiles * n_tiles;
+    const int32_t cus = device_cus();
+    const int32_t rem = tiles % cus;
+    const bool split = rem > 0 && (int64_t)rem * TAIL_SPLIT <= cus;
+    int32_t n_big = split ? tiles - rem : tiles;
+    int32_t n_small = split ? rem * TAIL_SPLIT : 0;
+    int32_t big_per_xcd = (n_big + 7) / 8;
+    int32_t small_per_xcd = (n_small + 7) / 8;
     int32_t null_tiles = (int32_t)((a.n_null + BM - 1) / BM);
     ProjCondArgs args = a;
     CamTable tab = cams;
-    void* params[] = {&args, &tab, &m_tiles, &n_tiles, &per_xcd, &null_tiles};
+    void* params[] = {&args,    &tab,        &m_tiles,       &n_tiles,   &n_big,
+                      &big_per_xcd, &n_small, &small_per_xcd, &null_tiles};
     // corner offsets fit 32 bits when every map is under 4 GiB
     const auto map_bytes = [&](int32_t H, int32_t W, int32_t C) {
         return (uint64_t)a.batch * (uint64_t)H * (uint64_t)W * (uint64_t)C * 2u;
@@ -384,8 +459,8 @@ hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hi
                           : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<true, false>))
                  : (off32 ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, true>)
                           : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, false>));
-    return hipLaunchKernel(fn,
-                           dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
+    return hipLaunchKernel(fn, dim3((unsigned)(big_per_xcd + small_per_xcd) * 8), dim3(kThreads),
+                           params, 0, s);
 }
 
 }  // namespace p3d

@@ -206,16 +206,18 @@ def test_proj_cond_extra_workloads(orc, name):
     say("  max|diff|/max|Y| %.3e corr %.8f" % st)
 
 
+@pytest.mark.parametrize("n", [1500, 9000], ids=["split_tiles", "whole_tiles"])
 @pytest.mark.parametrize("two_maps", [False, True], ids=["one_map", "two_maps"])
-def test_proj_cond_map_of_4gib(orc, two_maps):
+def test_proj_cond_map_of_4gib(orc, two_maps, n):
     """A bf16 map of exactly 4 GiB (1 x 1024 x 1024 x 2048): its corner
     offsets no longer fit 32 bits, so the fused kernel takes its 64-bit
     gather addressing (launches whose maps are all smaller take the 32-bit
-    one). Alone, or as map 1 behind a small seeded 32 x 32 x 64 map 0. The
-    large map is zero except around the pixels the tokens project to (chosen
-    by the oracle's projection), which hold seeded values; every row is
-    checked."""
-    B, H, W, C, D, R, n, n_null = 1, 1024, 1024, 2048, 264, 256, 1500, 7
+    one). Alone, or as map 1 behind a small seeded 32 x 32 x 64 map 0; 12
+    tiles of 128 tokens (run as 32-token parts) or 71 (run whole on 256
+    compute units). The large map is zero except around the pixels the
+    tokens project to (chosen by the oracle's projection), which hold seeded
+    values; every row is checked."""
+    B, H, W, C, D, R, n_null = 1, 1024, 1024, 2048, 264, 256, 7
     coords = synth.random_coords(R, B, n, seed=4242)
     fovs = [40.0]
     fo, do = oracle_cameras(orc, fovs, [None], W)

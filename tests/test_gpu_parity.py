@@ -267,6 +267,11 @@ SMALL = [
     # null rows far beyond the token rows, ragged, 25 vectors per row
     dict(name="bf16_null_heavy", bf16=True, R=16, B=1, n=130, H=8, W=8, C=64, D=200,
          bias=True, n_null=700),
+    # 300 tiles of 128 tokens: on 256 compute units the first 256 run whole
+    # and the 44 past the last full round as 32-token parts, one launch; the
+    # null blocks reach the split tiles too (block q goes with token tile q)
+    dict(name="bf16_whole_and_split_tiles", bf16=True, R=64, B=1, n=299 * 128 + 77, H=48,
+         W=40, C=136, D=264, bias=True, n_null=299 * 128 + 77),
 ]
 
 

@@ -3,19 +3,24 @@
 // cross-resolution agreement): coverage, per-map sums and sums of squares of
 // the samples, and the per-token cosine between two maps' samples.
 //
-// An HBM-bound gather with a reduction instead of a store. A wave takes TPW
-// tokens at a time: lanes 0..TPW-1 project one each, then the wave walks the
-// TPW tokens, broadcasting each token's corner metadata from its lane
-// (readlane) and gathering its corner rows with the lanes spread over the
-// channels (16-byte vectors, 64 lanes = 1 KB of a row per instruction), two
-// tokens at a time so that both tokens' loads are in flight together. Map 0
-// and map 1 vectors at the same channel offset sit in the same lane, so the
-// cosine's dot product and norms need no shuffles until the per-token wave
-// reduction. Samples are blended and rounded exactly as the fused kernel
-// feeds them to proj_linear; sums are binary64, reduced over the workgroup
-// in LDS and added to the result with one device atomic per figure per
-// workgroup (atomics on eight addresses serialise, so their count is kept to
-// a few thousand).
+// An HBM-bound gather with a reduction instead of a store. Tokens go to the
+// waves as quads of 4 consecutive tokens: each XCD owns a contiguous range,
+// and its waves take its quads round-robin, so that at any time an XCD's
+// waves sample one window of consecutive tokens, whose corner rows overlap,
+// in the same L2. Lanes project 16 quads at a time; then each 16-lane row of
+// the wave takes one token of a quad: the row's lanes walk that token's
+// channels 16 vectors (of 16 bytes) apart, map 0 and map 1 at the same
+// channel offset in the same lane, with the corner loads of several vectors
+// issued before any is blended. The cosine's dot product and norms stay
+// per-lane partial sums until one 16-lane reduction per token (four DPP
+// steps, no LDS). Samples are blended and rounded exactly as the fused
+// kernel feeds them to proj_linear. For bf16 maps a token's per-lane partial
+// sums are binary32 (at most 64 products of bf16-rounded values each) and
+// are carried in binary64 from there on; fp32 maps accumulate in binary64
+// throughout. Sums are reduced over the workgroup in LDS and added to the
+// result with one device atomic per figure per workgroup.
+#include <type_traits>
+
 #include "p3d_internal.h"
 
 namespace p3d {
@@ -23,11 +28,7 @@ namespace p3d {
 namespace {
 
 constexpr int kThreads = 256;
-// Tokens per wave and step. Each token keeps a whole wave's loads in flight
-// (16 per lane for two 1024-channel bf16 maps), so concurrency comes from the
-// number of waves: 16 tokens per wave gives 100k tokens ~6000 waves.
-constexpr int TPW = 16;
-constexpr int kMaxBlocks = 1024;   // 16 waves per CU; atomics: 8 per block
+constexpr int kWavesPerCU = 12;    // target residency (at most 168 registers per lane)
 
 // Corner metadata of token t on an H x W map (top-left row, 0/1 steps right
 // and down, fractions); the same construction as the fused kernel's.
@@ -47,54 +48,156 @@ __device__ __forceinline__ Meta meta_of(const Projected& p, int32_t H, int32_t W
     return m;
 }
 
-// The token's meta broadcast from lane j (uniform values).
-__device__ __forceinline__ Meta lane_meta(const Meta& m, int j) {
-    Meta r;
-    r.r00 = __builtin_amdgcn_readlane(m.r00, j);
-    r.steps = __builtin_amdgcn_readlane(m.steps, j);
-    r.tx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m.tx), j));
-    r.ty = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m.ty), j));
-    return r;
+// A token's four corner rows on one map (vector pointers) and bilinear
+// weights.
+struct Tok {
+    const uint4* row[4];
+    float w[4];
+};
+
+__device__ __forceinline__ Tok tok_of(const uint4* __restrict__ feat, int vpr, const Meta& m,
+                                      int W) {
+    const int32_t dx = m.steps & 1, dyw = (m.steps & 2) ? W : 0;
+    Tok t;
+    t.row[0] = feat + (int64_t)m.r00 * vpr;
+    t.row[1] = feat + (int64_t)(m.r00 + dx) * vpr;
+    t.row[2] = feat + (int64_t)(m.r00 + dyw) * vpr;
+    t.row[3] = feat + (int64_t)(m.r00 + dyw + dx) * vpr;
+    t.w[0] = (1.0f - m.tx) * (1.0f - m.ty);
+    t.w[1] = m.tx * (1.0f - m.ty);
+    t.w[2] = (1.0f - m.tx) * m.ty;
+    t.w[3] = m.tx * m.ty;
+    return t;
 }
 
-// Vector v of the blended sample of one token: 8 bf16 values (rounded to
-// bf16, as proj_linear receives them) or 4 binary32 values.
+__device__ __forceinline__ void load_corners(const Tok& t, int v, uint4 (&q)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = t.row[k][v];
+}
+
+// The blended sample of one 16-byte vector: 8 values rounded to bf16 (as
+// proj_linear receives them) or 4 binary32 values.
 template <bool Bf16>
-__device__ __forceinline__ void sample_vec(const uint4* __restrict__ feat, int vpr,
-                                           const Meta& m, int W, int v, float* out) {
-    const int32_t dx = m.steps & 1, dyw = (m.steps & 2) ? W : 0;
-    const uint4 a = feat[(int64_t)m.r00 * vpr + v];
-    const uint4 b = feat[(int64_t)(m.r00 + dx) * vpr + v];
-    const uint4 c = feat[(int64_t)(m.r00 + dyw) * vpr + v];
-    const uint4 d = feat[(int64_t)(m.r00 + dyw + dx) * vpr + v];
-    const float w0 = (1.0f - m.tx) * (1.0f - m.ty), w1 = m.tx * (1.0f - m.ty);
-    const float w2 = (1.0f - m.tx) * m.ty, w3 = m.tx * m.ty;
-    const uint32_t* pa = reinterpret_cast<const uint32_t*>(&a);
-    const uint32_t* pb = reinterpret_cast<const uint32_t*>(&b);
-    const uint32_t* pc = reinterpret_cast<const uint32_t*>(&c);
-    const uint32_t* pd = reinterpret_cast<const uint32_t*>(&d);
+__device__ __forceinline__ void blend(const uint4 (&q)[4], const Tok& t, float* out) {
+    const uint32_t* pa = reinterpret_cast<const uint32_t*>(&q[0]);
+    const uint32_t* pb = reinterpret_cast<const uint32_t*>(&q[1]);
+    const uint32_t* pc = reinterpret_cast<const uint32_t*>(&q[2]);
+    const uint32_t* pd = reinterpret_cast<const uint32_t*>(&q[3]);
     if constexpr (Bf16) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float lo = fmaf(w3, bf16lo(pd[e]), fmaf(w2, bf16lo(pc[e]),
-                                  fmaf(w1, bf16lo(pb[e]), w0 * bf16lo(pa[e]))));
-            const float hi = fmaf(w3, bf16hi(pd[e]), fmaf(w2, bf16hi(pc[e]),
-                                  fmaf(w1, bf16hi(pb[e]), w0 * bf16hi(pa[e]))));
-            const uint32_t q = pack_bf16x2(lo, hi);
-            out[2 * e] = bf16lo(q);
-            out[2 * e + 1] = bf16hi(q);
+            const float lo = fmaf(t.w[3], bf16lo(pd[e]), fmaf(t.w[2], bf16lo(pc[e]),
+                                  fmaf(t.w[1], bf16lo(pb[e]), t.w[0] * bf16lo(pa[e]))));
+            const float hi = fmaf(t.w[3], bf16hi(pd[e]), fmaf(t.w[2], bf16hi(pc[e]),
+                                  fmaf(t.w[1], bf16hi(pb[e]), t.w[0] * bf16hi(pa[e]))));
+            const uint32_t r = pack_bf16x2(lo, hi);
+            out[2 * e] = bf16lo(r);
+            out[2 * e + 1] = bf16hi(r);
         }
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            out[e] = fmaf(w3, __uint_as_float(pd[e]), fmaf(w2, __uint_as_float(pc[e]),
-                          fmaf(w1, __uint_as_float(pb[e]), w0 * __uint_as_float(pa[e]))));
+            out[e] = fmaf(t.w[3], __uint_as_float(pd[e]), fmaf(t.w[2], __uint_as_float(pc[e]),
+                          fmaf(t.w[1], __uint_as_float(pb[e]), t.w[0] * __uint_as_float(pa[e]))));
     }
 }
+
+// Per-lane partial sums of one token on one or two maps: the row's lanes
+// take vectors rl, rl + 16, ...; U vectors (of each map) are loaded before
+// any is blended, so that 4 U (one map) or 8 U (two maps) loads are in
+// flight; the last vectors of a ragged row go one at a time.
+template <bool Bf16, bool Two, typename Acc>
+struct Partial {
+    Acc su = 0, sw = 0, d = 0, x = 0, y = 0;
+    bool nz0 = false, nz1 = false;
+
+    __device__ __forceinline__ void add(const float* u, const float* w) {
+        constexpr int EPV = Bf16 ? 8 : 4;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const Acc uu = u[e];
+            nz0 |= u[e] != 0.0f;
+            su += uu;
+            x = fma(uu, uu, x);
+            if constexpr (Two) {
+                const Acc ww = w[e];
+                nz1 |= w[e] != 0.0f;
+                sw += ww;
+                d = fma(uu, ww, d);
+                y = fma(ww, ww, y);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void run(const Tok& ta, const Tok& tb, int rl, int vpr) {
+        constexpr int EPV = Bf16 ? 8 : 4;
+        constexpr int U = Two ? 2 : 4;
+        int v0 = rl;
+#pragma unroll 1
+        for (; v0 + 16 * (U - 1) < vpr; v0 += 16 * U) {
+            uint4 qa[U][4], qb[Two ? U : 1][4];
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                load_corners(ta, v0 + 16 * j, qa[j]);
+                if constexpr (Two) load_corners(tb, v0 + 16 * j, qb[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                float u[EPV], w[EPV];
+                blend<Bf16>(qa[j], ta, u);
+                if constexpr (Two) blend<Bf16>(qb[j], tb, w);
+                add(u, w);
+            }
+        }
+#pragma unroll 1
+        for (; v0 < vpr; v0 += 16) {
+            uint4 qa[4], qb[4];
+            float u[EPV], w[EPV];
+            load_corners(ta, v0, qa);
+            if constexpr (Two) load_corners(tb, v0, qb);
+            blend<Bf16>(qa, ta, u);
+            if constexpr (Two) blend<Bf16>(qb, tb, w);
+            add(u, w);
+        }
+    }
+};
 
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Lane value of a DPP permutation within each 16-lane row.
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
+}
+template <int Ctrl>
+__device__ __forceinline__ double dpp_d(double x) {
+    const int64_t v = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)v, Ctrl, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), Ctrl, 0xF, 0xF, false);
+    return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum over each 16-lane row, in every lane of the row: partners at xor 1 and
+// xor 2 (quad permutations), then the other quad of the half row (half
+// mirror), then the other half (mirror). Every lane adds the same pairs, so
+// all lanes of a row hold the same bits.
+template <typename T>
+__device__ __forceinline__ T row_sum(T x) {
+    if constexpr (std::is_same<T, float>::value) {
+        x += dpp_f<0xB1>(x);      // quad_perm [1, 0, 3, 2]
+        x += dpp_f<0x4E>(x);      // quad_perm [2, 3, 0, 1]
+        x += dpp_f<0x141>(x);     // row_half_mirror
+        x += dpp_f<0x140>(x);     // row_mirror
+    } else {
+        x += dpp_d<0xB1>(x);
+        x += dpp_d<0x4E>(x);
+        x += dpp_d<0x141>(x);
+        x += dpp_d<0x140>(x);
+    }
     return x;
 }
 
@@ -103,12 +206,32 @@ __global__ __launch_bounds__(64) void stats_zero_kernel(p3d_proj_stats* s) {
         reinterpret_cast<double*>(s)[threadIdx.x] = 0.0;
 }
 
+__device__ __forceinline__ Meta shfl_meta(const Meta& m, int src) {
+    Meta r;
+    r.r00 = __shfl(m.r00, src);
+    r.steps = __shfl(m.steps, src);
+    r.tx = __shfl(m.tx, src);
+    r.ty = __shfl(m.ty, src);
+    return r;
+}
+
+// Workgroup g runs on XCD g % 8 as that XCD's (g / 8)-th. XCD x owns the
+// tokens [x Wx per_wave, (x + 1) Wx per_wave), Wx = 4 per_xcd waves, as
+// quads of 4 consecutive tokens; the XCD's wave j takes quads j, j + Wx,
+// j + 2 Wx, ... (per_wave / 4 of them). The XCD's waves thus sweep one
+// window of consecutive tokens together, and neighbouring tokens, which
+// share corner rows, are sampled at about the same time in the same L2.
 template <bool Bf16>
-__global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a, CamTable cams) {
+__global__ __launch_bounds__(kThreads, kWavesPerCU / (kThreads / 64)) void stats_kernel(StatsArgs a, CamTable cams,
+                                                         int64_t per_wave, int64_t per_xcd) {
     constexpr int EPV = Bf16 ? 8 : 4;
+    using Acc = typename std::conditional<Bf16, float, double>::type;
     const int lane = threadIdx.x & 63;
-    const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
-    const int64_t waves = ((int64_t)gridDim.x * kThreads) >> 6;
+    const int row = lane >> 4, rl = lane & 15;
+    const int64_t wx = (int64_t)(blockIdx.x >> 3) * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t Wx = per_xcd * (kThreads / 64);
+    const int64_t xcd_t0 = (int64_t)(blockIdx.x & 7) * Wx * per_wave;
+    const int64_t quads = per_wave / 4;
     const uint4* __restrict__ f0 = reinterpret_cast<const uint4*>(a.feat0);
     const uint4* __restrict__ f1 = reinterpret_cast<const uint4*>(a.feat1);
     const int vpr0 = a.C0 / EPV, vpr1 = a.C1 / EPV;
@@ -116,14 +239,17 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a, CamTable c
     const bool cosine = two && a.C0 == a.C1;
 
     double s0 = 0.0, q0 = 0.0, s1 = 0.0, q1 = 0.0;   // per lane
-    double cos_sum = 0.0, cos_cnt = 0.0, inside = 0.0, tokens = 0.0;   // wave-uniform
+    double cos_sum = 0.0, cos_cnt = 0.0;             // per lane (row leaders add)
+    double inside = 0.0, tokens = 0.0;               // wave-uniform
 
-    for (int64_t base = wave * TPW; base < a.n; base += waves * TPW) {
-        // ---- lane j < TPW projects token base + j
-        const int64_t t = base + lane;
+    for (int64_t k0 = 0; k0 < quads; k0 += 16) {
+        // ---- lane l projects token l % 4 of this wave's quad k0 + l / 4
+        const int64_t k = k0 + (lane >> 2);
+        const int64_t t = xcd_t0 + 4 * (wx + k * Wx) + (lane & 3);
+        const bool valid = k < quads && t < a.n;
         Meta m0{0, 0, 0.0f, 0.0f}, m1{0, 0, 0.0f, 0.0f};
         int in = 0;
-        if (lane < TPW && t < a.n) {
+        if (valid) {
             int32_t b, x, y, z;
             token_cell(a.coords, t, a.R, b, x, y, z);
             const Projected p = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
@@ -131,126 +257,47 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a, CamTable c
             if (two) m1 = meta_of(p, a.H1, a.W1);
             in = p.mask;
         }
-        const int64_t cnt = a.n - base < TPW ? a.n - base : TPW;
+        const uint64_t vmask = __ballot(valid);
+        if (vmask == 0) break;                       // past the tokens: so are later quads
         inside += (double)__builtin_popcountll(__ballot(in));
-        tokens += (double)cnt;
-        // ---- the wave walks its tokens two at a time: both tokens' corner
-        // loads are in flight together and their reductions interleave
-        int j = 0;
-        for (; j + 1 < (int)cnt; j += 2) {
-            const Meta a0 = lane_meta(m0, j), b0 = lane_meta(m0, j + 1);
-            const Meta a1 = lane_meta(m1, j), b1 = lane_meta(m1, j + 1);
-            double dA = 0.0, xA = 0.0, yA = 0.0, dB = 0.0, xB = 0.0, yB = 0.0;
-            for (int v = lane; v < vpr0; v += 64) {
-                float pa[EPV], pb[EPV];
-                sample_vec<Bf16>(f0, vpr0, a0, a.W0, v, pa);
-                sample_vec<Bf16>(f0, vpr0, b0, a.W0, v, pb);
-                if (cosine) {
-                    float qa[EPV], qb[EPV];
-                    sample_vec<Bf16>(f1, vpr1, a1, a.W1, v, qa);
-                    sample_vec<Bf16>(f1, vpr1, b1, a.W1, v, qb);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) {
-                        const double u = pa[e], w = qa[e], u2 = pb[e], w2 = qb[e];
-                        s0 += u + u2;
-                        s1 += w + w2;
-                        dA = fma(u, w, dA);
-                        xA = fma(u, u, xA);
-                        yA = fma(w, w, yA);
-                        dB = fma(u2, w2, dB);
-                        xB = fma(u2, u2, xB);
-                        yB = fma(w2, w2, yB);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) {
-                        const double u = pa[e], u2 = pb[e];
-                        s0 += u + u2;
-                        q0 = fma(u, u, fma(u2, u2, q0));
-                    }
-                }
-            }
+        tokens += (double)__builtin_popcountll(vmask);
+        const int nq = quads - k0 < 16 ? (int)(quads - k0) : 16;
+        // ---- row r takes token r of each quad
+        for (int q = 0; q < nq; ++q) {
+            const int src = 4 * q + row;
+            const Meta a0 = shfl_meta(m0, src);
+            const Meta a1 = shfl_meta(m1, src);
+            const bool live = (vmask >> src) & 1;
+            const Tok ta = tok_of(f0, vpr0, a0, a.W0);
             if (cosine) {
-                q0 += xA + xB;
-                q1 += yA + yB;
-                dA = wave_sum(dA);
-                dB = wave_sum(dB);
-                xA = wave_sum(xA);
-                xB = wave_sum(xB);
-                yA = wave_sum(yA);
-                yB = wave_sum(yB);
-                if (xA > 0.0 && yA > 0.0) {
-                    cos_sum += dA / (sqrt(xA) * sqrt(yA));
+                // map 0 and map 1 at the same channels, in the same lanes
+                const Tok tb = tok_of(f1, vpr1, a1, a.W1);
+                Partial<Bf16, true, Acc> pt;
+                if (live) pt.run(ta, tb, rl, vpr0);
+                s0 += (double)pt.su;
+                s1 += (double)pt.sw;
+                q0 += (double)pt.x;
+                q1 += (double)pt.y;
+                const Acc dr = row_sum(pt.d), xr = row_sum(pt.x), yr = row_sum(pt.y);
+                // both samples non-zero somewhere in the row: exact, whatever
+                // the binary32 norms do
+                const uint64_t b0 = __ballot(pt.nz0), b1 = __ballot(pt.nz1);
+                const bool both = ((b0 >> (16 * row)) & 0xFFFF) && ((b1 >> (16 * row)) & 0xFFFF);
+                if (live && rl == 0 && both) {
+                    cos_sum += (double)dr / (sqrt((double)xr) * sqrt((double)yr));
                     cos_cnt += 1.0;
                 }
-                if (xB > 0.0 && yB > 0.0) {
-                    cos_sum += dB / (sqrt(xB) * sqrt(yB));
-                    cos_cnt += 1.0;
-                }
-            } else if (two) {
-                for (int v = lane; v < vpr1; v += 64) {
-                    float qa[EPV], qb[EPV];
-                    sample_vec<Bf16>(f1, vpr1, a1, a.W1, v, qa);
-                    sample_vec<Bf16>(f1, vpr1, b1, a.W1, v, qb);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) {
-                        const double w = qa[e], w2 = qb[e];
-                        s1 += w + w2;
-                        q1 = fma(w, w, fma(w2, w2, q1));
-                    }
-                }
-            }
-        }
-        // ---- an odd last token alone
-        if (j < (int)cnt) {
-            const Meta t0 = lane_meta(m0, j);
-            double dot = 0.0, n0 = 0.0, n1 = 0.0;
-            for (int v = lane; v < vpr0; v += 64) {
-                float x0[EPV];
-                sample_vec<Bf16>(f0, vpr0, t0, a.W0, v, x0);
-                if (cosine) {
-                    const Meta t1 = lane_meta(m1, j);
-                    float x1[EPV];
-                    sample_vec<Bf16>(f1, vpr1, t1, a.W1, v, x1);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) {
-                        const double u = x0[e], w = x1[e];
-                        s0 += u;
-                        s1 += w;
-                        dot = fma(u, w, dot);
-                        n0 = fma(u, u, n0);
-                        n1 = fma(w, w, n1);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) {
-                        const double u = x0[e];
-                        s0 += u;
-                        q0 = fma(u, u, q0);
-                    }
-                }
-            }
-            if (cosine) {
-                q0 += n0;
-                q1 += n1;
-                dot = wave_sum(dot);
-                n0 = wave_sum(n0);
-                n1 = wave_sum(n1);
-                if (n0 > 0.0 && n1 > 0.0) {
-                    cos_sum += dot / (sqrt(n0) * sqrt(n1));
-                    cos_cnt += 1.0;
-                }
-            } else if (two) {
-                const Meta t1 = lane_meta(m1, j);
-                for (int v = lane; v < vpr1; v += 64) {
-                    float x1[EPV];
-                    sample_vec<Bf16>(f1, vpr1, t1, a.W1, v, x1);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) {
-                        const double w = x1[e];
-                        s1 += w;
-                        q1 = fma(w, w, q1);
-                    }
+            } else if (live) {
+                Partial<Bf16, false, Acc> p0;
+                p0.run(ta, ta, rl, vpr0);
+                s0 += (double)p0.su;
+                q0 += (double)p0.x;
+                if (two) {
+                    const Tok tb = tok_of(f1, vpr1, a1, a.W1);
+                    Partial<Bf16, false, Acc> p1;
+                    p1.run(tb, tb, rl, vpr1);
+                    s1 += (double)p1.su;
+                    q1 += (double)p1.x;
                 }
             }
         }
@@ -258,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a, CamTable c
     // ---- workgroup reduction, then one atomic per figure
     __shared__ double part[kThreads / 64][8];
     const double fig[8] = {tokens, inside, wave_sum(s0), wave_sum(s1), wave_sum(q0),
-                           wave_sum(q1), cos_sum, cos_cnt};
+                           wave_sum(q1), wave_sum(cos_sum), wave_sum(cos_cnt)};
     if (lane == 0)
 #pragma unroll
         for (int k = 0; k < 8; ++k) part[threadIdx.x >> 6][k] = fig[k];
@@ -272,6 +319,16 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a, CamTable c
     }
 }
 
+// Compute units of the current device.
+int stats_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return 256;
+    return cus;
+}
+
 }  // namespace
 
 hipError_t launch_stats(const StatsArgs& a, bool bf16, const CamTable& cams, hipStream_t s) {
@@ -283,13 +340,16 @@ hipError_t launch_stats(const StatsArgs& a, bool bf16, const CamTable& cams, hip
                                        dim3(64), params, 0, s);
         if (e != hipSuccess || a.n == 0) return e;
     }
-    // one step of TPW tokens per wave where the grid allows; larger inputs
-    // loop (grid-stride)
-    const int64_t per_block = (int64_t)TPW * (kThreads / 64);
-    const int64_t blocks_needed = (a.n + per_block - 1) / per_block;
-    int64_t blocks = blocks_needed < kMaxBlocks ? blocks_needed : kMaxBlocks;
+    // an equal share of the tokens per wave, for a full residency of waves
+    const int64_t max_waves = (int64_t)stats_cus() * kWavesPerCU;
+    int64_t per_wave = (a.n + max_waves - 1) / max_waves;
+    per_wave = (per_wave + 3) & ~(int64_t)3;
+    const int64_t waves = (a.n + per_wave - 1) / per_wave;
+    const int64_t blocks_needed = (waves + kThreads / 64 - 1) / (kThreads / 64);
+    int64_t per_xcd = (blocks_needed + 7) / 8;
+    const int64_t blocks = per_xcd * 8;             // the last XCD's tail runs empty
     CamTable tab = cams;
-    void* params[] = {&args, &tab};
+    void* params[] = {&args, &tab, &per_wave, &per_xcd};
     const void* fn = bf16 ? reinterpret_cast<const void*>(&stats_kernel<true>)
                           : reinterpret_cast<const void*>(&stats_kernel<false>);
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), params, 0, s);

@@ -116,8 +116,10 @@ struct WLoader {
 };
 
 // Consumer: the chunk's 2 x TIt x 4 MFMAs over the first 16 TIt tokens of
-// the stage (TIt = TI for a full tile). The other consumer wave on the SIMD
-// covers the LDS latency of the fragment reads.
+// the stage (TIt = TI for a full tile). The S fragment of token block i + 1
+// is read before the MFMAs of block i are issued (the scheduling barriers
+// keep that order), so its LDS latency runs under them; the other consumer
+// wave on the SIMD covers the rest.
 template <int TIt = TI>
 __device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TIt], int lane, int cw,
                                         const uint4* __restrict__ sa,
@@ -130,12 +132,17 @@ __device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TIt], int lane, int c
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
             wf[j] = __builtin_bit_cast(bf16x8_t, sw[slot(cw * WN + j * 16 + n, v)]);
+        bf16x8_t sf = __builtin_bit_cast(bf16x8_t, sa[slot(n, v)]);
 #pragma unroll
         for (int i = 0; i < TIt; ++i) {
-            const bf16x8_t sf = __builtin_bit_cast(bf16x8_t, sa[slot(i * 16 + n, v)]);
+            bf16x8_t nxt = sf;
+            if (i + 1 < TIt) nxt = __builtin_bit_cast(bf16x8_t, sa[slot((i + 1) * 16 + n, v)]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < FJ; ++j)
                 acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], sf, acc[j][i], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            sf = nxt;
         }
     }
     lds_barrier();

@@ -75,62 +75,103 @@ __device__ __forceinline__ void load_corners(const Tok& t, int v, uint4 (&q)[4])
     for (int k = 0; k < 4; ++k) q[k] = t.row[k][v];
 }
 
-// The blended sample of one 16-byte vector: 8 values rounded to bf16 (as
-// proj_linear receives them) or 4 binary32 values.
-template <bool Bf16>
-__device__ __forceinline__ void blend(const uint4 (&q)[4], const Tok& t, float* out) {
+// The blended samples of one 16-byte vector of a bf16 map: 8 values rounded
+// to bf16 (as proj_linear receives them), as 4 packed pairs.
+__device__ __forceinline__ void blend_bf16(const uint4 (&q)[4], const Tok& t, uint32_t (&r)[4]) {
     const uint32_t* pa = reinterpret_cast<const uint32_t*>(&q[0]);
     const uint32_t* pb = reinterpret_cast<const uint32_t*>(&q[1]);
     const uint32_t* pc = reinterpret_cast<const uint32_t*>(&q[2]);
     const uint32_t* pd = reinterpret_cast<const uint32_t*>(&q[3]);
-    if constexpr (Bf16) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float lo = fmaf(t.w[3], bf16lo(pd[e]), fmaf(t.w[2], bf16lo(pc[e]),
-                                  fmaf(t.w[1], bf16lo(pb[e]), t.w[0] * bf16lo(pa[e]))));
-            const float hi = fmaf(t.w[3], bf16hi(pd[e]), fmaf(t.w[2], bf16hi(pc[e]),
-                                  fmaf(t.w[1], bf16hi(pb[e]), t.w[0] * bf16hi(pa[e]))));
-            const uint32_t r = pack_bf16x2(lo, hi);
-            out[2 * e] = bf16lo(r);
-            out[2 * e + 1] = bf16hi(r);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            out[e] = fmaf(t.w[3], __uint_as_float(pd[e]), fmaf(t.w[2], __uint_as_float(pc[e]),
-                          fmaf(t.w[1], __uint_as_float(pb[e]), t.w[0] * __uint_as_float(pa[e]))));
+    for (int e = 0; e < 4; ++e) {
+        const float lo = fmaf(t.w[3], bf16lo(pd[e]), fmaf(t.w[2], bf16lo(pc[e]),
+                              fmaf(t.w[1], bf16lo(pb[e]), t.w[0] * bf16lo(pa[e]))));
+        const float hi = fmaf(t.w[3], bf16hi(pd[e]), fmaf(t.w[2], bf16hi(pc[e]),
+                              fmaf(t.w[1], bf16hi(pb[e]), t.w[0] * bf16hi(pa[e]))));
+        r[e] = pack_bf16x2(lo, hi);
     }
 }
+
+// The blended samples of one 16-byte vector of an fp32 map: 4 values.
+__device__ __forceinline__ void blend_f32(const uint4 (&q)[4], const Tok& t, float (&o)[4]) {
+    const uint32_t* pa = reinterpret_cast<const uint32_t*>(&q[0]);
+    const uint32_t* pb = reinterpret_cast<const uint32_t*>(&q[1]);
+    const uint32_t* pc = reinterpret_cast<const uint32_t*>(&q[2]);
+    const uint32_t* pd = reinterpret_cast<const uint32_t*>(&q[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = fmaf(t.w[3], __uint_as_float(pd[e]), fmaf(t.w[2], __uint_as_float(pc[e]),
+                    fmaf(t.w[1], __uint_as_float(pb[e]), t.w[0] * __uint_as_float(pa[e]))));
+}
+
+// a.lo * b.lo + a.hi * b.hi + c for packed bf16 pairs (each product is exact
+// in binary32; the sums round as binary32 additions do).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+constexpr uint32_t kOnePair = 0x3F803F80u;   // (1.0, 1.0) in bf16
 
 // Per-lane partial sums of one token on one or two maps: the row's lanes
 // take vectors rl, rl + 16, ...; U vectors (of each map) are loaded before
 // any is blended, so that 4 U (one map) or 8 U (two maps) loads are in
-// flight; the last vectors of a ragged row go one at a time.
+// flight; the last vectors of a ragged row go one at a time. bf16 samples
+// are summed as packed pairs (sum: dot with (1, 1); squares and the two-map
+// dot product: dot of the pairs); a sample is non-zero when its magnitude
+// bits are.
 template <bool Bf16, bool Two, typename Acc>
 struct Partial {
     Acc su = 0, sw = 0, d = 0, x = 0, y = 0;
-    bool nz0 = false, nz1 = false;
+    uint32_t or0 = 0, or1 = 0;         // bf16: OR of the packed samples
+    bool nz0 = false, nz1 = false;     // fp32
 
-    __device__ __forceinline__ void add(const float* u, const float* w) {
-        constexpr int EPV = Bf16 ? 8 : 4;
+    __device__ __forceinline__ void step(const uint4 (&qa)[4], const uint4 (&qb)[4],
+                                         const Tok& ta, const Tok& tb) {
+        if constexpr (Bf16) {
+            uint32_t ru[4], rw[4];
+            blend_bf16(qa, ta, ru);
+            if constexpr (Two) blend_bf16(qb, tb, rw);
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            const Acc uu = u[e];
-            nz0 |= u[e] != 0.0f;
-            su += uu;
-            x = fma(uu, uu, x);
-            if constexpr (Two) {
-                const Acc ww = w[e];
-                nz1 |= w[e] != 0.0f;
-                sw += ww;
-                d = fma(uu, ww, d);
-                y = fma(ww, ww, y);
+            for (int e = 0; e < 4; ++e) {
+                su = dot2(ru[e], kOnePair, su);
+                x = dot2(ru[e], ru[e], x);
+                or0 |= ru[e];
+                if constexpr (Two) {
+                    sw = dot2(rw[e], kOnePair, sw);
+                    y = dot2(rw[e], rw[e], y);
+                    d = dot2(ru[e], rw[e], d);
+                    or1 |= rw[e];
+                }
+            }
+        } else {
+            float u[4], w[4];
+            blend_f32(qa, ta, u);
+            if constexpr (Two) blend_f32(qb, tb, w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const Acc uu = u[e];
+                nz0 |= u[e] != 0.0f;
+                su += uu;
+                x = fma(uu, uu, x);
+                if constexpr (Two) {
+                    const Acc ww = w[e];
+                    nz1 |= w[e] != 0.0f;
+                    sw += ww;
+                    d = fma(uu, ww, d);
+                    y = fma(ww, ww, y);
+                }
             }
         }
     }
 
+    __device__ __forceinline__ bool nonzero0() const {
+        return Bf16 ? (or0 & 0x7FFF7FFFu) != 0 : nz0;
+    }
+    __device__ __forceinline__ bool nonzero1() const {
+        return Bf16 ? (or1 & 0x7FFF7FFFu) != 0 : nz1;
+    }
+
     __device__ __forceinline__ void run(const Tok& ta, const Tok& tb, int rl, int vpr) {
-        constexpr int EPV = Bf16 ? 8 : 4;
         constexpr int U = Two ? 2 : 4;
         int v0 = rl;
 #pragma unroll 1
@@ -142,22 +183,14 @@ struct Partial {
                 if constexpr (Two) load_corners(tb, v0 + 16 * j, qb[j]);
             }
 #pragma unroll
-            for (int j = 0; j < U; ++j) {
-                float u[EPV], w[EPV];
-                blend<Bf16>(qa[j], ta, u);
-                if constexpr (Two) blend<Bf16>(qb[j], tb, w);
-                add(u, w);
-            }
+            for (int j = 0; j < U; ++j) step(qa[j], qb[Two ? j : 0], ta, tb);
         }
 #pragma unroll 1
         for (; v0 < vpr; v0 += 16) {
             uint4 qa[4], qb[4];
-            float u[EPV], w[EPV];
             load_corners(ta, v0, qa);
             if constexpr (Two) load_corners(tb, v0, qb);
-            blend<Bf16>(qa, ta, u);
-            if constexpr (Two) blend<Bf16>(qb, tb, w);
-            add(u, w);
+            step(qa, qb, ta, tb);
         }
     }
 };
@@ -281,7 +314,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerCU / (kThreads / 64)) void stats
                 const Acc dr = row_sum(pt.d), xr = row_sum(pt.x), yr = row_sum(pt.y);
                 // both samples non-zero somewhere in the row: exact, whatever
                 // the binary32 norms do
-                const uint64_t b0 = __ballot(pt.nz0), b1 = __ballot(pt.nz1);
+                const uint64_t b0 = __ballot(pt.nonzero0()), b1 = __ballot(pt.nonzero1());
                 const bool both = ((b0 >> (16 * row)) & 0xFFFF) && ((b1 >> (16 * row)) & 0xFFFF);
                 if (live && rl == 0 && both) {
                     cos_sum += (double)dr / (sqrt((double)xr) * sqrt((double)yr));

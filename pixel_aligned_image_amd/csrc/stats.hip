@@ -28,7 +28,7 @@ namespace p3d {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWavesPerCU = 12;    // target residency (at most 168 registers per lane)
+constexpr int kWavesPerCU = 8;     // target residency (at most 256 registers per lane)
 
 // Corner metadata of token t on an H x W map (top-left row, 0/1 steps right
 // and down, fractions); the same construction as the fused kernel's.
@@ -172,7 +172,7 @@ struct Partial {
     }
 
     __device__ __forceinline__ void run(const Tok& ta, const Tok& tb, int rl, int vpr) {
-        constexpr int U = Two ? 2 : 4;
+        constexpr int U = Two ? 4 : 8;
         int v0 = rl;
 #pragma unroll 1
         for (; v0 + 16 * (U - 1) < vpr; v0 += 16 * U) {

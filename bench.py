@@ -153,8 +153,11 @@ def cpu_baseline(inp, cams_o, target_s=12.0):
 
 def run_extra(p3d, synth, stream, reps, lead_step):
     """Adjacent parts on their own workloads: requantization of a res-512
-    shell onto the 64-node grid, the fused kernel on those grid nodes, and
-    the fused kernel over the two-map texture-stage workload."""
+    shell onto the 64-node grid, the fused kernel on those grid nodes, the
+    fused kernel over the two-map texture-stage workload, its diagnostics,
+    the gather-once samples and the per-block linears; and, as a reference,
+    one block of the plain product through the tile and through a library
+    GEMM."""
     import numpy as np
     import torch
 
@@ -278,7 +281,30 @@ def run_extra(p3d, synth, stream, reps, lead_step):
         "achieved": gflops / (grp_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s", "frac": gflops / (grp_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "note": "residual add: every block's output is read and rewritten (S 2048 -> 1536)"}
-    del maps, weight, y, coords, S, Wg, outs
+    # ---- the same product, one block without the residual, through the tile
+    # and through a library GEMM (torch.matmul, ROCm's BLAS): a reference for
+    # what a plain bf16 GEMM of this shape reaches on this device
+    y1 = torch.empty((n, w.out_dim), dtype=torch.bfloat16, device="cuda")
+    wt = Wg[0].t().contiguous()
+    one = lambda: p3d.p3d_proj_linear_grouped(S, Wg[:1], [y1])
+    lib_mm = lambda: torch.matmul(S, wt, out=y1)
+    for f in (one, lib_mm):
+        for _ in range(3):
+            f()
+    # alternating blocks, medians: the two are compared under the same clocks
+    t_one, t_lib = [], []
+    for _ in range(5):
+        t_one.append(time_events(one, reps, stream))
+        t_lib.append(time_events(lib_mm, reps, stream))
+    one_ms, lib_ms = float(np.median(t_one)), float(np.median(t_lib))
+    f1 = 2.0 * n * K * w.out_dim
+    out["gemm_reference"] = {
+        "shape": "[%d, %d] x [%d, %d] bf16" % (n, K, K, w.out_dim),
+        "grouped_kernel_one_block_ms": one_ms,
+        "grouped_kernel_frac": f1 / (one_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "library_gemm": "torch.matmul (ROCm BLAS)", "library_gemm_ms": lib_ms,
+        "library_gemm_frac": f1 / (lib_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    del maps, weight, y, coords, S, Wg, outs, y1, wt
     torch.cuda.empty_cache()
     return out
 

@@ -20,7 +20,8 @@
 //   4 producer waves (one per SIMD) do everything else: project the tokens,
 //     keep the corner-row gather a chunk ahead in registers, blend and
 //     round the samples into the LDS S tile, stream W through LDS with
-//     direct loads, and write the null rows at the end.
+//     direct loads, and write the tile's share of the null rows, one
+//     16-byte store per lane per K chunk.
 // A wave issuing MFMAs is held at each one until the matrix core takes it,
 // so a wave's own VALU work does not overlap its MFMAs; a producer on the
 // same SIMD fills those issue slots instead.
@@ -238,22 +239,49 @@ struct Producer {
     }
 };
 
+// A producer lane's share of its tile's null rows, written a few vectors per
+// K chunk (the bias rows would otherwise all go out at the tile's end, when
+// the consumers store the tile's output through the same load/store path).
+// The lane owns column vector colv (fixed for the tile) of rows
+// row0 + 4 i (i < ipt) of every null block q = mt, mt + m_tiles, ...; item
+// j is block j / ipt, row i = j % ipt. Everything but colv and the bias
+// value is uniform over the wave.
+struct NullWriter {
+    uint4* out4;
+    int64_t row0;                    // first row of this wave's share of block mt
+    int64_t q_rows;                  // rows between blocks q and q + m_tiles
+    int64_t n_end;                   // n + n_null
+    int dv, colv, ipt;
+    int j, total, per;               // next item, items, items per chunk
+    uint4 val;                       // bias vector colv (or zeros)
+
+    __device__ __forceinline__ void issue() {
+        for (int s = 0; s < per && j < total; ++s, ++j) {
+            const int qi = j / ipt, i = j - qi * ipt;
+            const int64_t row = row0 + qi * q_rows + 4 * i;
+            if (row < n_end && colv < dv) store_nt16(out4 + row * dv + colv, val);
+        }
+    }
+};
+
 // One producer iteration: W of chunk kc+1, S of chunk kc+1 (its corner rows
 // were queued one chunk ago), corner rows of chunk kc+2 (from map 1 from
 // chunk k1 on), then this wave's W loads must have landed before the
 // barrier. The LDS stages are restrict parameters so that the compiler can
 // tell the direct W loads apart from the S stores.
 template <bool TwoMaps, bool Off32, int G>
-__device__ __forceinline__ void produce(Producer<TwoMaps, Off32, G>& p, const ProjCondArgs& a,
-                                        const CamTable& cams, int64_t m0, int k1, int kc,
-                                        int nk2, Gq<G>& gq, uint4* __restrict__ sa_n,
-                                        uint4* __restrict__ sw_n) {
+__device__ __forceinline__ void produce(Producer<TwoMaps, Off32, G>& p, NullWriter& nw,
+                                        const ProjCondArgs& a, const CamTable& cams, int64_t m0,
+                                        int k1, int kc, int nk2, Gq<G>& gq,
+                                        uint4* __restrict__ sa_n, uint4* __restrict__ sw_n) {
     if (kc + 1 < nk2) {
         // Only this chunk's corners are in flight here: wait for them
         // explicitly, then queue W, then blend. Without the explicit wait the
         // compiler waits before the blend, for the W loads queued just before
-        // it as well.
+        // it as well. This chunk's null-row stores go first: they are older
+        // than the W loads, so the wait for W covers them too.
         wait_vmcnt<0>();
+        nw.issue();
         p.wl.issue(sw_n, kc + 1);
         p.commit(gq, kc + 1, sa_n);
         if constexpr (TwoMaps) {
@@ -299,6 +327,23 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
 
     if (producer) {
         const int ptid = tid - N_CONS * 64;
+        // ---- this tile's share of the null blocks q = mt, mt + m_tiles, ...
+        // (written inside the K loop); the lane's bias vector first, so that
+        // its load has landed long before the first store
+        NullWriter nw;
+        nw.out4 = out4;
+        nw.dv = dv;
+        nw.colv = (n0 >> 3) + (ptid & 63);                    // 64 vectors per 512-wide row
+        nw.ipt = NULL_VEC / kProdThreads;
+        nw.row0 = a.n + (int64_t)mt * BM + r0 + (ptid >> 6);
+        nw.q_rows = (int64_t)m_tiles * BM;
+        nw.n_end = a.n + a.n_null;
+        nw.j = 0;
+        nw.total = mt < null_tiles ? ((null_tiles - 1 - mt) / m_tiles + 1) * nw.ipt : 0;
+        nw.per = (nw.total + nk2 - 2) / (nk2 - 1);             // over the nk2 - 1 loaded chunks
+        nw.val = make_uint4(0, 0, 0, 0);
+        if (a.bias && nw.total > 0 && nw.colv < dv)
+            nw.val = reinterpret_cast<const uint4*>(a.bias)[nw.colv];
         Producer<TwoMaps, Off32, G> p;
         p.wl.init(a.weight, (a.C + a.C1) >> 3, a.D, n0,
                   __builtin_amdgcn_readfirstlane(wave - N_CONS), lane);
@@ -339,24 +384,10 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
         wait_vmcnt<G * 4>();
         lds_barrier();                                            // B_0
         for (int kc = 0; kc < nk2; kc += 2) {
-            produce(p, a, cams, m0, k1, kc, nk2, gq, sA1, sW1);
-            produce(p, a, cams, m0, k1, kc + 1, nk2, gq, sA0, sW0);
+            produce(p, nw, a, cams, m0, k1, kc, nk2, gq, sA1, sW1);
+            produce(p, nw, a, cams, m0, k1, kc + 1, nk2, gq, sA0, sW0);
         }
         __syncthreads();                                          // consumers staged
-
-        // ---- this tile's share of the null blocks q = mt, mt + m_tiles, ...
-        const uint4* bias4 = reinterpret_cast<const uint4*>(a.bias);
-        for (int32_t q = mt; q < null_tiles; q += m_tiles) {
-            for (int idx = ptid; idx < NULL_VEC; idx += kProdThreads) {
-                const int r = idx >> 6, cv = idx & 63;         // 64 vectors per 512-wide row
-                const int64_t row = a.n + (int64_t)q * BM + r0 + r;
-                const int colv = (n0 >> 3) + cv;
-                if (row < a.n + a.n_null && colv < dv) {
-                    const uint4 val = bias4 ? bias4[colv] : make_uint4(0, 0, 0, 0);
-                    store_nt16(out4 + row * dv + colv, val);
-                }
-            }
-        }
         return;
     }
 

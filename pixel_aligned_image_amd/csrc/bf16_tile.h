@@ -101,11 +101,16 @@ struct WLoader {
                     (lds_void*)(dst + q * 64), 16, 0, 0);
             }
         } else {
-            const int wv_even = (lane & 7) ^ ((lane >> 4) & 7);
-            const int wv_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
+            // the lane index is opaque here, so that the clamped row
+            // addresses are formed per load rather than hoisted out of the K
+            // loop (where they would take registers the producers need)
+            int l = lane;
+            asm volatile("" : "+v"(l));
+            const int wv_even = (l & 7) ^ ((l >> 4) & 7);
+            const int wv_odd = (l & 7) ^ ((4 + (l >> 4)) & 7);
 #pragma unroll
             for (int q = 0; q < W_INSTR; ++q) {
-                const int col = min(row0 + q * 8 + (lane >> 3), D - 1);
+                const int col = min(row0 + q * 8 + (l >> 3), D - 1);
                 const int kv = min(kc * 8 + ((q & 1) ? wv_odd : wv_even), vprw - 1);
                 __builtin_amdgcn_global_load_lds(
                     reinterpret_cast<const void*>(wgt + (int64_t)col * vprw + kv),

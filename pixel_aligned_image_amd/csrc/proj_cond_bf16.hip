@@ -33,6 +33,10 @@
 //     k+1 into S stage (k+1)%2, queue the corner rows of chunk k+2, then wait
 //     for their own W loads;
 //   B_{k+1}.
+// Tile start: the producers queue W of chunk 0, project the tokens into LDS,
+// then queue the corner rows of chunk 1; meanwhile the consumers, whose
+// accumulators are not live yet, gather and blend chunk 0 into S stage 0,
+// so the first two round trips to memory overlap; B_0.
 // Per tile, each producer item keeps its corner rows' offsets and its
 // bilinear weights (Producer), so a chunk's gather and W loads need no
 // vector address arithmetic.
@@ -133,13 +137,16 @@ struct Producer {
     int vpr;                         // 16-byte vectors per row of that map
     int kbase;                       // first K chunk of that map
     int W;                           // that map's width (row step between image rows)
-    int ptid;
+    int vfirst, vstride;             // item u is vector vfirst + u vstride of a chunk
     int gv;                          // vector of each gathered 128-byte segment
     int4 gt[G];                // token_entry of each item (used without Off32)
     uint32_t off[G][4];        // corner rows' byte offsets + 16 gv (Off32)
     __amdgpu_buffer_rsrc_t rsrc;     // the map as a buffer resource (Off32)
     float wt[G][4];            // bilinear weights, 0 for a padding token
     WLoader wl;
+
+    // Tile row (token) of item u.
+    __device__ __forceinline__ int row(int u) const { return (vfirst + u * vstride) >> 3; }
 
     // Offsets and weights of the items from their corner metadata gt.
     __device__ __forceinline__ void set_items() {
@@ -175,8 +182,7 @@ struct Producer {
         W = a.W1;
 #pragma unroll
         for (int u = 0; u < G; ++u)
-            gt[u] = token_entry(a, cams, m0 + ((ptid + u * kProdThreads) >> 3), a.H1, a.W1,
-                                nullptr);
+            gt[u] = token_entry(a, cams, m0 + row(u), a.H1, a.W1, nullptr);
         set_items();
     }
 
@@ -234,7 +240,7 @@ struct Producer {
 #pragma unroll
         for (int u = 0; u < G; ++u) {
             const uint4 v = blend_bf16(gq[u], wt[u]);
-            sa[slot((ptid + u * kProdThreads) >> 3, gv)] = dead ? make_uint4(0, 0, 0, 0) : v;
+            sa[slot(row(u), gv)] = dead ? make_uint4(0, 0, 0, 0) : v;
         }
     }
 };
@@ -368,20 +374,20 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
         p.vpr = a.C >> 3;
         p.kbase = 0;
         p.W = a.W;
-        p.ptid = ptid;
+        p.vfirst = ptid;
+        p.vstride = kProdThreads;
         p.gv = ptid & 7;
 #pragma unroll
-        for (int u = 0; u < G; ++u) p.gt[u] = s_tok[(ptid + u * kProdThreads) >> 3];
+        for (int u = 0; u < G; ++u) p.gt[u] = s_tok[p.row(u)];
         p.set_items();
+        // chunk 0 is gathered and blended by the consumers (below); the
+        // producers queue chunk 1 at once, so the two round trips overlap
         Gq<G> gq;
-        p.gather_issue(gq, 0);
-        wait_vmcnt<0>();                                          // W and corners of chunk 0
-        p.commit(gq, 0, sA0);
         if constexpr (TwoMaps) {
             if (k1 == 1) p.to_map1(a, cams, m0, k1);
         }
         p.gather_issue(gq, 1);
-        wait_vmcnt<G * 4>();
+        wait_vmcnt<G * 4>();                                      // W of chunk 0 (older)
         lds_barrier();                                            // B_0
         for (int kc = 0; kc < nk2; kc += 2) {
             produce(p, nw, a, cams, m0, k1, kc, nk2, gq, sA1, sW1);
@@ -393,12 +399,40 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
 
     // ---------------------------------------------------------- consumers
     const int cw = wave;
+    lds_barrier();                                                // tokens parked
+    {
+        // chunk 0's samples: gathered and blended here (the accumulators are
+        // not live yet), while the producers queue chunk 1. Vector v of the
+        // chunk goes to consumer thread v % 512; a 32-token part has 256
+        // vectors, so only the first four waves take one.
+        constexpr int NV = TIt * 16 * (BK / 8);
+        constexpr int CT = N_CONS * 64;
+        constexpr int GC = (NV + CT - 1) / CT;
+        static_assert(NV % 64 == 0, "whole waves");
+        if (NV >= CT || tid < NV) {
+            const int4* s_tok = reinterpret_cast<const int4*>(sA1);
+            Producer<TwoMaps, Off32, GC> c;
+            c.feat = reinterpret_cast<const uint4*>(a.feat);
+            c.vpr = a.C >> 3;
+            c.kbase = 0;
+            c.W = a.W;
+            c.vfirst = tid;
+            c.vstride = CT;
+            c.gv = tid & 7;
+#pragma unroll
+            for (int u = 0; u < GC; ++u) c.gt[u] = s_tok[c.row(u)];
+            c.set_items();
+            Gq<GC> gq;
+            c.gather_issue(gq, 0);
+            wait_vmcnt<0>();
+            c.commit(gq, 0, sA0);
+        }
+    }
     f32x4_t acc[FJ][TIt];
 #pragma unroll
     for (int j = 0; j < FJ; ++j)
 #pragma unroll
         for (int i = 0; i < TIt; ++i) acc[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    lds_barrier();                                                // tokens parked
     lds_barrier();                                                // B_0
     for (int kc = 0; kc < nk2; kc += 2) {
         consume<TIt>(acc, lane, cw, sA0, sW0);

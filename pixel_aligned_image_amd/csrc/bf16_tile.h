@@ -224,7 +224,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TIt], int la
         const int t = q >> 3, cv = q & 7;
         const int64_t tok = m0 + t;
         const int colv = (fbase >> 3) + cv;
-        if (tok < n && colv < dv) out4[tok * dv + colv] = stage4[slot(t, cv)];
+        if (tok < n && colv < dv) store_nt16(out4 + tok * dv + colv, stage4[slot(t, cv)]);
     }
 }
 

@@ -156,7 +156,8 @@ __device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TIt], int lane, int c
 // Epilogue: + bias (bf16 parameters), optionally + the value already in
 // `out` (Accumulate: a residual add, rounded once), round to bf16, stage the
 // wave's 16 TIt x 64 block in the free W stages (token-major 128-byte rows,
-// the same slot swizzle) and write 16-byte row pieces. Lane l of block (j, i)
+// the same slot swizzle) and write 16-byte row pieces with non-temporal
+// stores (the output is not read back here). Lane l of block (j, i)
 // holds features 4*(l/16) + r of token l % 16. out is [n, D] bf16; rows at or
 // past n are not touched.
 constexpr int OLD_BATCH = 4;        // residual loads in flight together (registers)

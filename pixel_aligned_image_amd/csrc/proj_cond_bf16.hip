@@ -123,7 +123,8 @@ __device__ __forceinline__ int4 token_entry(const ProjCondArgs& a, const CamTabl
     return e;
 }
 
-// Producer state: one thread of the four producer waves. TwoMaps: the gather
+// Gather state of one thread: a producer's items of every chunk past the
+// first, or a consumer's items of chunk 0. TwoMaps: the gather
 // switches to map 1 part-way through K (kbase, vpr, W and the metadata
 // change); with one map they are constants of the launch. Off32: every map
 // is under 4 GiB, so a corner vector's byte offset in its map fits 32 bits.
@@ -139,10 +140,10 @@ struct Producer {
     int W;                           // that map's width (row step between image rows)
     int vfirst, vstride;             // item u is vector vfirst + u vstride of a chunk
     int gv;                          // vector of each gathered 128-byte segment
-    int4 gt[G];                // token_entry of each item (used without Off32)
-    uint32_t off[G][4];        // corner rows' byte offsets + 16 gv (Off32)
+    int4 gt[G];                      // token_entry of each item (used without Off32)
+    uint32_t off[G][4];              // corner rows' byte offsets + 16 gv (Off32)
     __amdgpu_buffer_rsrc_t rsrc;     // the map as a buffer resource (Off32)
-    float wt[G][4];            // bilinear weights, 0 for a padding token
+    float wt[G][4];                  // bilinear weights, 0 for a padding token
     WLoader wl;
 
     // Tile row (token) of item u.
@@ -284,8 +285,9 @@ __device__ __forceinline__ void produce(Producer<TwoMaps, Off32, G>& p, NullWrit
         // Only this chunk's corners are in flight here: wait for them
         // explicitly, then queue W, then blend. Without the explicit wait the
         // compiler waits before the blend, for the W loads queued just before
-        // it as well. This chunk's null-row stores go first: they are older
-        // than the W loads, so the wait for W covers them too.
+        // it as well. This chunk's null-row stores go first, so that they
+        // have the whole chunk to complete before the next chunk's wait for
+        // everything in flight.
         wait_vmcnt<0>();
         nw.issue();
         p.wl.issue(sw_n, kc + 1);
@@ -359,8 +361,9 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
         p.wl.issue(sW0, 0);
         // ---- project the tile's tokens; per token park (top-left row, the
         // row steps to the right / lower corner, the two fractions) in sA1.
-        // sA1 is next written after B_0, which every producer passes only
-        // once its reads of this table have completed.
+        // sA1 is next written after B_0, which every wave (producers and the
+        // consumers gathering chunk 0) passes only once its reads of this
+        // table have completed.
         int4* s_tok = reinterpret_cast<int4*>(sA1);            // [BMt]
         if (ptid < BMt) {
             const int64_t t = m0 + ptid;

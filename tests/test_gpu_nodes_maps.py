@@ -164,6 +164,11 @@ CASES = [
          maps=[(16, 16, 128), (64, 48, 192)], D=136, bias=True, n_null=5, points="grid_nodes"),
     dict(name="f32_two_maps", bf16=False, R=24, B=2, n=270, maps=[(6, 6, 64), (31, 29, 36)],
          D=100, bias=True, n_null=7, points="cell_centres"),
+    # 70 whole tiles; map 0 is one K chunk, so the switch to map 1 comes
+    # right after the consumers' chunk 0
+    dict(name="bf16_two_maps_whole_tiles", bf16=True, R=48, B=2, n=70 * 128 - 3,
+         maps=[(16, 16, 64), (40, 24, 72)], D=136, bias=True, n_null=200,
+         points="cell_centres"),
 ]
 
 

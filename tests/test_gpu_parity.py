@@ -272,6 +272,10 @@ SMALL = [
     # null blocks reach the split tiles too (block q goes with token tile q)
     dict(name="bf16_whole_and_split_tiles", bf16=True, R=64, B=1, n=299 * 128 + 77, H=48,
          W=40, C=136, D=264, bias=True, n_null=299 * 128 + 77),
+    # 70 whole tiles (too many past a round to split), each writing two or
+    # three null blocks inside a three-chunk K loop
+    dict(name="bf16_whole_tiles_null_blocks", bf16=True, R=48, B=2, n=70 * 128 - 5, H=32,
+         W=36, C=136, D=264, bias=True, n_null=25000),
 ]
 
 

@@ -323,8 +323,8 @@ p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution
  *   cosine   = cos_sum / cos_count
  * Sums are carried in binary64 and accumulated with device atomics (their
  * order, and so the last bits, varies between runs). For BF16 maps each
- * token's partial sums over a lane's share of its channels (at most 64
- * products of bf16 samples) are binary32 first; FP32 maps are binary64
+ * token's partial sums over a lane's share of its channels (C / 16 products
+ * of bf16 samples per map) are binary32 first; FP32 maps are binary64
  * throughout. The non-zero test of the cosine is exact. With one map, or two
  * of unequal channels, cos_sum = cos_count = 0.
  *

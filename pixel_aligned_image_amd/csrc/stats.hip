@@ -15,9 +15,9 @@
 // per-lane partial sums until one 16-lane reduction per token (four DPP
 // steps, no LDS). Samples are blended and rounded exactly as the fused
 // kernel feeds them to proj_linear. For bf16 maps a token's per-lane partial
-// sums are binary32 (at most 64 products of bf16-rounded values each) and
-// are carried in binary64 from there on; fp32 maps accumulate in binary64
-// throughout. Sums are reduced over the workgroup in LDS and added to the
+// sums are binary32 (C / 16 products of bf16-rounded values each: 64 for 1024
+// channels, 128 for 2048) and are carried in binary64 from there on; fp32
+// maps accumulate in binary64 throughout. Sums are reduced over the workgroup in LDS and added to the
 // result with one device atomic per figure per workgroup.
 #include <type_traits>
 

@@ -91,3 +91,41 @@ def check_bf16_linear(Y_gpu_bits, Y_orc, tol=2e-2):
     assert err.max() <= tol * scale, "bf16 proj_linear: max|diff| %.3e vs max|Y| %.3e" % (
         err.max(), scale)
     return err.max() / max(scale, 1e-30), np.corrcoef(Yg.ravel(), Y_orc.ravel())[0, 1]
+
+
+def run_fused(p3d, o, coords, n, R, fovs, dists, maps_np, W_np, b_np, n_null, bf16, rows,
+              points, image_size):
+    """One p3d_proj_cond call (one map, or a list of two) on the GPU against the
+    oracle's rows `rows`: every checked row must have been written (out starts
+    as NaN), masks bit-exact, null rows equal to the bias bit for bit, token
+    rows within the bf16 / fp32 tolerances. Returns the bf16 statistics."""
+    D = W_np.shape[0]
+    cp = product_cameras(p3d, fovs, dists, image_size)
+    fo, do = oracle_cameras(o, fovs, dists, image_size)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    out = torch.full((n + n_null, D), float("nan"), dtype=dt, device="cuda")
+    mask = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+    feats = [to_dev(m, bf16) for m in maps_np]
+    p3d.p3d_proj_cond(to_dev(coords), n, R, cp, feats if len(feats) > 1 else feats[0],
+                      to_dev(W_np, bf16), out, bias=to_dev(b_np, bf16), n_null=n_null,
+                      mask=mask, points=points)
+    torch.cuda.synchronize()
+    Yref, mref = o.proj_cond_rows(coords, n, R, fo, do, list(maps_np), W_np, b_np, n_null, rows,
+                                  points=points)
+    got = to_host(out[torch.from_numpy(rows).cuda()])
+    tok = rows < n
+    assert np.array_equal(to_host(mask)[rows[tok]], mref[tok]), "mask differs"
+    null = ~tok
+    if null.any():
+        want = b_np if b_np is not None else np.zeros(D, W_np.dtype)
+        assert np.array_equal(got[null], np.broadcast_to(want, (null.sum(), D))), "null rows"
+    if not tok.any():
+        return None
+    if bf16:
+        return check_bf16_linear(got[tok], Yref[tok])
+    absmaps = [np.abs(m) for m in maps_np]
+    S = o.proj_cond_rows(coords, n, R, fo, do, absmaps, np.abs(W_np),
+                         None if b_np is None else np.abs(b_np), n_null, rows[tok],
+                         points=points)[0]
+    check_fp32_linear(got[tok], Yref[tok], S)
+    return None

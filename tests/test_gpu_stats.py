@@ -15,7 +15,7 @@ import torch
 import oracle
 import p3d_synth as synth
 import pixel_aligned_image_amd as p3d
-from parity_util import oracle_cameras, product_cameras, to_dev
+from parity_util import run_stats
 
 pytestmark = pytest.mark.gpu
 
@@ -33,30 +33,7 @@ def orc():
 
 
 def _check(o, coords, n, R, fovs, dists, maps_np, bf16, points, image_size):
-    cp = product_cameras(p3d, fovs, dists, image_size)
-    fo, do = oracle_cameras(o, fovs, dists, image_size)
-    stats = torch.full((8,), float("nan"), dtype=torch.float64, device="cuda")
-    feats = [to_dev(m, bf16) for m in maps_np]
-    p3d.p3d_projection_stats(to_dev(coords), n, R, cp, feats, stats, points=points)
-    torch.cuda.synchronize()
-    got = dict(zip(p3d.STAT_FIELDS, stats.cpu().numpy().tolist()))
-    want = o.projection_stats(coords, n, R, fo, do, list(maps_np), points=points)
-    assert got["tokens"] == want["tokens"] == n
-    assert got["inside"] == want["inside"]
-    tol = 2.0 ** -8 if bf16 else 1e-5
-    for h in range(len(maps_np)):
-        c = maps_np[h].shape[3]
-        mag = np.sqrt(n * c * want["sum_sq%d" % h])        # >= sum |S|
-        assert abs(got["sum%d" % h] - want["sum%d" % h]) <= tol * mag + 1e-300, h
-        assert abs(got["sum_sq%d" % h] - want["sum_sq%d" % h]) <= 2 * tol * want["sum_sq%d" % h] \
-            + 1e-300, h
-    assert got["cos_count"] == want["cos_count"]
-    if want["cos_count"]:
-        dc = abs(got["cos_sum"] - want["cos_sum"]) / want["cos_count"]
-        assert dc <= (1e-3 if bf16 else 1e-6), dc
-    else:
-        assert got["cos_sum"] == 0.0
-    return got, want
+    return run_stats(p3d, o, coords, n, R, fovs, dists, maps_np, bf16, points, image_size)
 
 
 CASES = [

@@ -8,6 +8,8 @@ bf16: that plus one bf16 ulp, since both sides round); masks bit-exact; one-map 
 bit-identical to p3d_bilinear_sample at the same projected points (the same
 arithmetic); per-block outputs within the bf16 proj_linear tolerance (2e-2
 of |Y| + rms(row) per element, 2e-2 of max |Y| overall), residual included.
+Besides the fixed cases, a seeded sweep draws token counts, ragged K and D,
+the number of blocks, the residual add and the bias, and checks every row.
 """
 import os
 import sys
@@ -145,6 +147,34 @@ def test_grouped_small(orc, case):
     S_np = synth.bf16_bits(rng.standard_normal((n, K)).astype(np.float32))
     _grouped(orc, S_np, n, K, case["D"], case["G"], case["acc"], case["bias"], np.arange(n),
              len(case["name"]) + 1)
+
+
+def _draw_grouped(i):
+    rng = np.random.default_rng(4300 + i)
+    n = [1, 127, 128, 129][i] if i < 4 else int(rng.integers(2, 20000))
+    K = 8 * int(rng.integers(1, 66))                          # 8 .. 520
+    D = 8 * int(rng.integers(1, 138))                         # 8 .. 1096
+    G = int(rng.integers(1, 9))
+    while n * K * D * G > 2.5e9:                              # keep the oracle quick
+        n //= 2
+    return dict(i=i, n=max(n, 1), K=K, D=D, G=G, acc=bool(rng.random() < 0.5),
+                bias=bool(rng.random() < 0.5))
+
+
+SWEEP = [_draw_grouped(i) for i in range(20)]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=["%d_n%d_K%d_D%d_G%d" % (c["i"], c["n"], c["K"], c["D"],
+                                                                   c["G"]) for c in SWEEP])
+def test_grouped_random_shape(orc, case):
+    """A seeded sweep of shapes: ragged K and D, 1 to 8 blocks, with and
+    without the residual add and the bias, every row."""
+    say(case)
+    rng = np.random.default_rng(4400 + case["i"])
+    n, K = case["n"], case["K"]
+    S_np = synth.bf16_bits(rng.standard_normal((n, K)).astype(np.float32))
+    _grouped(orc, S_np, n, K, case["D"], case["G"], case["acc"], case["bias"], np.arange(n),
+             4500 + case["i"])
 
 
 def test_gather_once_then_blocks_full_size(orc):

@@ -108,6 +108,17 @@ def unique_corner_rows(pixel, bidx, H, W):
     return int(np.unique(rows).size)
 
 
+def bf16_kernel_name(two_maps, n, D):
+    """The fused bf16 kernel instantiation a launch of n tokens and D features
+    runs: the last template argument is its tail part size in 16-token blocks
+    (4 when the tiles past the last full round run as 64-token parts, else 2)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rem = (-(-n // 128) * -(-D // 512)) % cus
+    tip = 4 if rem and 4 * rem > cus and 2 * rem <= cus else 2
+    return "proj_cond_bf16_kernel<%s, true, %d>" % ("true" if two_maps else "false", tip)
+
+
 def time_events(fn, reps, stream, lead=None):
     """Mean duration (ms) of fn() over reps launches, HIP events on stream.
     lead(), enqueued first and not timed, keeps the GPU busy while the host
@@ -198,7 +209,7 @@ def run_extra(p3d, synth, stream, reps, lead_step):
         "frac": rq_bytes / (rq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "note": "100k tokens = 3.2 MB: launch-latency bound, far from the HBM roofline"}
     out["grid_nodes"] = {
-        "workload": w.name, "kernel": "proj_cond_bf16_kernel<false, true>", "tokens": n,
+        "workload": w.name, "kernel": bf16_kernel_name(False, n, w.out_dim), "tokens": n,
         "mean_ms": nodes_ms, "bound": "mfma", "flops_per_launch": flops,
         "achieved": flops / (nodes_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s", "frac": flops / (nodes_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
@@ -222,7 +233,7 @@ def run_extra(p3d, synth, stream, reps, lead_step):
     two_ms = time_events(two, reps, stream)
     flops = 2.0 * n * w.k_total * w.out_dim
     out["two_maps"] = {
-        "workload": w.name, "kernel": "proj_cond_bf16_kernel<true, true>", "tokens": n,
+        "workload": w.name, "kernel": bf16_kernel_name(True, n, w.out_dim), "tokens": n,
         "null_rows": nn, "maps": ["%dx%dx%dx%d" % tuple(m.shape) for m in maps],
         "mean_ms": two_ms, "tokens_per_s": n / (two_ms * 1e-3), "bound": "mfma",
         "flops_per_launch": flops, "achieved": flops / (two_ms * 1e-3) / 1e12,

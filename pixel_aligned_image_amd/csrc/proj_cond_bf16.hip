@@ -61,9 +61,11 @@
 // Tail: with one workgroup per CU the tiles run in rounds of one per CU.
 // When the tiles past the last full round fit one round four times over,
 // each of them runs as four 32-token parts (the same code with two token
-// blocks per consumer and one gathered vector per producer thread), queued
-// after every whole tile.
+// blocks per consumer and one gathered vector per producer thread), else,
+// when they fit twice over, as two 64-token parts (four token blocks, two
+// vectors); the parts are queued after every whole tile.
 #include <atomic>
+#include <type_traits>
 
 #include "bf16_tile.h"
 
@@ -73,9 +75,10 @@ namespace {
 
 using namespace tile;
 
-// Tail sub-tiles: 32 tokens (TI_TAIL token blocks) of a 128-token tile.
-constexpr int TI_TAIL = 2;
-constexpr int TAIL_SPLIT = TI / TI_TAIL;                // sub-tiles per tile
+// Tail sub-tiles: 32 tokens (TI_QUARTER token blocks) or 64 tokens
+// (TI_HALF) of a 128-token tile.
+constexpr int TI_QUARTER = 2;
+constexpr int TI_HALF = 4;
 
 // Gathered vectors per producer thread for a tile of TIt token blocks.
 template <int TIt>
@@ -306,11 +309,16 @@ __device__ __forceinline__ void produce(Producer<TwoMaps, Off32, G>& p, NullWrit
 }
 
 // One tile: 16 TIt tokens starting at token m0 (TIt = TI: a whole 128-token
-// tile; TIt = TI_TAIL: sub-tile `sub` of tile mt), features n0 .. n0 + 511.
+// tile; TIt = TI_QUARTER or TI_HALF: sub-tile `sub` of tile mt), features
+// n0 .. n0 + 511.
 // The tile also writes its share of the null rows: rows m0 - 128 mt ..
 // m0 - 128 mt + 16 TIt - 1 of every 128-row null block q = mt, mt + m_tiles,
 // ..., for the same features.
-template <bool TwoMaps, bool Off32, int TIt>
+//
+// Kernel tags the instantiation with the kernel's part size: two kernels that
+// inline one shared instantiation of the whole tile both spill registers to
+// scratch (hipcc of ROCm 7.2), while a copy per kernel does not.
+template <bool TwoMaps, bool Off32, int TIt, int Kernel>
 __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& cams,
                                          int32_t mt, int32_t nt, int sub, int32_t m_tiles,
                                          int32_t null_tiles, uint4* __restrict__ sW0,
@@ -407,7 +415,8 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
         // chunk 0's samples: gathered and blended here (the accumulators are
         // not live yet), while the producers queue chunk 1. Vector v of the
         // chunk goes to consumer thread v % 512; a 32-token part has 256
-        // vectors, so only the first four waves take one.
+        // vectors, so only the first four waves take one, a 64-token part
+        // one per thread.
         constexpr int NV = TIt * 16 * (BK / 8);
         constexpr int CT = N_CONS * 64;
         constexpr int GC = (NV + CT - 1) / CT;
@@ -449,12 +458,15 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
 // Work of workgroup g, which runs on XCD x = g % 8 as its (g / 8)-th:
 // whole tiles x * big_per_xcd .. x * big_per_xcd + big_per_xcd - 1 (below
 // n_big), then tail sub-tiles x * small_per_xcd + ... (below n_small): tile
-// n_big + s / TAIL_SPLIT, part s % TAIL_SPLIT. Tiles are numbered token tile
-// major, N tile fastest.
-template <bool TwoMaps, bool Off32>
+// n_big + s / split, part s % split, of 16 TIp tokens (split = TI / TIp).
+// Tiles are numbered token tile major, N tile fastest. The part size is a
+// template parameter, so that each kernel holds only two tile shapes (a
+// third would raise its register pressure).
+template <bool TwoMaps, bool Off32, int TIp>
 __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(
     ProjCondArgs a, CamTable cams, int32_t m_tiles, int32_t n_tiles, int32_t n_big,
     int32_t big_per_xcd, int32_t n_small, int32_t small_per_xcd, int32_t null_tiles) {
+    constexpr int split = TI / TIp;
     __shared__ uint4 sW0[BN * 8], sW1[BN * 8];     // 2 x 64 KB
     __shared__ uint4 sA0[BM * 8], sA1[BM * 8];     // 2 x 16 KB
 
@@ -464,15 +476,15 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(
         const int32_t tile = x * big_per_xcd + i;
         if (tile >= n_big) return;
         const int32_t mt = tile / n_tiles;
-        run_tile<TwoMaps, Off32, TI>(a, cams, mt, tile - mt * n_tiles, 0, m_tiles, null_tiles,
-                                     sW0, sW1, sA0, sA1);
+        run_tile<TwoMaps, Off32, TI, TIp>(a, cams, mt, tile - mt * n_tiles, 0, m_tiles,
+                                          null_tiles, sW0, sW1, sA0, sA1);
     } else {
         const int32_t st = x * small_per_xcd + (i - big_per_xcd);
         if (st >= n_small) return;
-        const int32_t tile = n_big + st / TAIL_SPLIT;
+        const int32_t tile = n_big + st / split;
         const int32_t mt = tile / n_tiles;
-        run_tile<TwoMaps, Off32, TI_TAIL>(a, cams, mt, tile - mt * n_tiles, st % TAIL_SPLIT,
-                                          m_tiles, null_tiles, sW0, sW1, sA0, sA1);
+        run_tile<TwoMaps, Off32, TIp, TIp>(a, cams, mt, tile - mt * n_tiles, st % split,
+                                           m_tiles, null_tiles, sW0, sW1, sA0, sA1);
     }
 }
 
@@ -497,18 +509,21 @@ int device_cus() {
 
 // Tail split: one workgroup per CU, so T tiles take ceil(T / CUs) rounds and
 // the last round may leave most CUs idle. When the R tiles past the last
-// full round fit one round as 32-token sub-tiles (TAIL_SPLIT R <= CUs), they
-// run as sub-tiles instead: each moves the full W stream of its N tile and
-// a quarter of the gather, so it takes well under a whole tile's time.
+// full round fit one round as 32-token sub-tiles (4 R <= CUs), or else as
+// 64-token sub-tiles (2 R <= CUs), they run as sub-tiles instead: each
+// moves the full W stream of its N tile and a quarter or half of the
+// gather, so it takes well under a whole tile's time.
 hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hipStream_t s) {
     int32_t m_tiles = (int32_t)((a.n + BM - 1) / BM);
     int32_t n_tiles = (a.D + BN - 1) / BN;
     const int32_t tiles = m_tiles * n_tiles;
     const int32_t cus = device_cus();
     const int32_t rem = tiles % cus;
-    const bool split = rem > 0 && (int64_t)rem * TAIL_SPLIT <= cus;
+    int32_t split = 0;
+    if (rem > 0 && rem * (TI / TI_QUARTER) <= cus) split = TI / TI_QUARTER;
+    else if (rem > 0 && rem * (TI / TI_HALF) <= cus) split = TI / TI_HALF;
     int32_t n_big = split ? tiles - rem : tiles;
-    int32_t n_small = split ? rem * TAIL_SPLIT : 0;
+    int32_t n_small = split ? rem * split : 0;
     int32_t big_per_xcd = (n_big + 7) / 8;
     int32_t small_per_xcd = (n_small + 7) / 8;
     int32_t null_tiles = (int32_t)((a.n_null + BM - 1) / BM);
@@ -522,11 +537,16 @@ hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hi
     };
     const bool off32 = map_bytes(a.H, a.W, a.C) < ((uint64_t)1 << 32) &&
                        (a.C1 == 0 || map_bytes(a.H1, a.W1, a.C1) < ((uint64_t)1 << 32));
-    const void* fn =
-        a.C1 > 0 ? (off32 ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<true, true>)
-                          : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<true, false>))
-                 : (off32 ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, true>)
-                          : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<false, false>));
+    const bool half = split == TI / TI_HALF;
+    const auto pick = [&](auto two_maps, auto o32) -> const void* {
+        constexpr bool T = decltype(two_maps)::value, O = decltype(o32)::value;
+        return half ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<T, O, TI_HALF>)
+                    : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<T, O, TI_QUARTER>);
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    const void* fn = a.C1 > 0 ? (off32 ? pick(yes{}, yes{}) : pick(yes{}, no{}))
+                              : (off32 ? pick(no{}, yes{}) : pick(no{}, no{}));
     return hipLaunchKernel(fn, dim3((unsigned)(big_per_xcd + small_per_xcd) * 8), dim3(kThreads),
                            params, 0, s);
 }

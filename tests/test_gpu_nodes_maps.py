@@ -136,9 +136,13 @@ CASES = [
          maps=[(16, 16, 128), (64, 48, 192)], D=136, bias=True, n_null=5, points="grid_nodes"),
     dict(name="f32_two_maps", bf16=False, R=24, B=2, n=270, maps=[(6, 6, 64), (31, 29, 36)],
          D=100, bias=True, n_null=7, points="cell_centres"),
-    # 70 whole tiles; map 0 is one K chunk, so the switch to map 1 comes
-    # right after the consumers' chunk 0
-    dict(name="bf16_two_maps_whole_tiles", bf16=True, R=48, B=2, n=70 * 128 - 3,
+    # 140 whole tiles on 256 compute units; map 0 is one K chunk, so the
+    # switch to map 1 comes right after the consumers' chunk 0
+    dict(name="bf16_two_maps_whole_tiles", bf16=True, R=48, B=2, n=140 * 128 - 3,
+         maps=[(16, 16, 64), (40, 24, 72)], D=136, bias=True, n_null=200,
+         points="cell_centres"),
+    # 70 tiles, run as 140 64-token parts, the same switch
+    dict(name="bf16_two_maps_half_parts", bf16=True, R=48, B=2, n=70 * 128 - 3,
          maps=[(16, 16, 64), (40, 24, 72)], D=136, bias=True, n_null=200,
          points="cell_centres"),
 ]
@@ -183,15 +187,17 @@ def test_proj_cond_extra_workloads(orc, name):
     say("  max|diff|/max|Y| %.3e corr %.8f" % st)
 
 
-@pytest.mark.parametrize("n", [1500, 9000], ids=["split_tiles", "whole_tiles"])
+@pytest.mark.parametrize("n", [1500, 9000, 20000],
+                         ids=["quarter_parts", "half_parts", "whole_tiles"])
 @pytest.mark.parametrize("two_maps", [False, True], ids=["one_map", "two_maps"])
 def test_proj_cond_map_of_4gib(orc, two_maps, n):
     """A bf16 map of exactly 4 GiB (1 x 1024 x 1024 x 2048): its corner
     offsets no longer fit 32 bits, so the fused kernel takes its 64-bit
     gather addressing (launches whose maps are all smaller take the 32-bit
     one). Alone, or as map 1 behind a small seeded 32 x 32 x 64 map 0; 12
-    tiles of 128 tokens (run as 32-token parts) or 71 (run whole on 256
-    compute units). The large map is zero except around the pixels the
+    tiles of 128 tokens (run as 32-token parts), 71 (as 64-token parts) or
+    157 (run whole on 256 compute units). The large map is zero except
+    around the pixels the
     tokens project to (chosen by the oracle's projection), which hold seeded
     values; every row is checked."""
     B, H, W, C, D, R, n_null = 1, 1024, 1024, 2048, 264, 256, 7

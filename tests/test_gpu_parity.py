@@ -272,9 +272,17 @@ SMALL = [
     # null blocks reach the split tiles too (block q goes with token tile q)
     dict(name="bf16_whole_and_split_tiles", bf16=True, R=64, B=1, n=299 * 128 + 77, H=48,
          W=40, C=136, D=264, bias=True, n_null=299 * 128 + 77),
-    # 70 whole tiles (too many past a round to split), each writing two or
+    # 357 tiles: 256 run whole and the 101 past the last full round (too
+    # many for 32-token parts) as 64-token parts, null blocks included
+    dict(name="bf16_whole_and_half_tiles", bf16=True, R=64, B=1, n=356 * 128 + 45, H=48,
+         W=40, C=136, D=264, bias=True, n_null=200 * 128 + 3),
+    # 140 whole tiles (too many past a round to split), each writing two or
     # three null blocks inside a three-chunk K loop
-    dict(name="bf16_whole_tiles_null_blocks", bf16=True, R=48, B=2, n=70 * 128 - 5, H=32,
+    dict(name="bf16_whole_tiles_null_blocks", bf16=True, R=48, B=2, n=140 * 128 - 5, H=32,
+         W=36, C=136, D=264, bias=True, n_null=50000),
+    # 70 tiles as 140 64-token parts, each writing its half of two or three
+    # null blocks
+    dict(name="bf16_half_parts_null_blocks", bf16=True, R=48, B=2, n=70 * 128 - 5, H=32,
          W=36, C=136, D=264, bias=True, n_null=25000),
 ]
 

@@ -6,8 +6,10 @@ counts (ragged K tails; map 0 a multiple of 64 when there are two), map
 sizes, feature width D (not a multiple of 512, up to three 512-wide tiles),
 bias or none, cell centres or grid nodes, and a token count picked so that
 the launch runs as 32-token parts only, as whole tiles only, or as whole
-tiles plus parts; null rows range from none to several 128-row blocks per
-tile. Bar as in the other fused tests: masks bit-exact, null rows equal to
+tiles plus parts; a further set draws 65 to 128 tiles past a full round, so
+that the leftover tiles run as 64-token parts. Each case is named by the
+regime its tile count takes on 256 compute units. Null rows range from none
+to several 128-row blocks per tile. Bar as in the other fused tests: masks bit-exact, null rows equal to
 the bias bit for bit, token rows within 2e-2 (bf16) / 1e-5 (fp32), and
 every checked row written (the output starts as NaN).
 """
@@ -71,10 +73,30 @@ def _draw(i):
                 points="grid_nodes" if rng.random() < 0.3 else "cell_centres")
 
 
-CASES = [_draw(i) for i in range(40)]
+def _draw_half(i):
+    """Whole tiles plus 65 to 128 leftover tiles, or 65 to 128 tiles alone."""
+    c = _draw(i)
+    rng = np.random.default_rng(9500 + i)
+    D = int(rng.integers(1, 64)) * 8
+    T = (CUS if i % 2 else 0) + int(rng.integers(65, 129))
+    n = (T - 1) * 128 + int(rng.integers(1, 129))
+    c.update(i=i, D=D, T=T, n=n, n_null=[0, int(rng.integers(1, 300)), n][i % 3],
+             R=int(max(8, np.ceil((n / c["B"]) ** (1 / 3))) + rng.integers(0, 16)))
+    return c
 
 
-@pytest.mark.parametrize("case", CASES, ids=["%d_%s_T%d" % (c["i"], c["regime"], c["T"])
+def _regime(T):
+    """How a launch of T tiles runs on CUS compute units."""
+    rem = T % CUS
+    tail = "quarters" if rem and 4 * rem <= CUS else "halves" if rem and 2 * rem <= CUS else ""
+    whole = T - rem if tail else T
+    return "+".join(x for x in (["whole"] if whole else []) + ([tail] if tail else []))
+
+
+CASES = [_draw(i) for i in range(40)] + [_draw_half(i) for i in range(40, 52)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["%d_%s_T%d" % (c["i"], _regime(c["T"]), c["T"])
                                               for c in CASES])
 def test_proj_cond_random_shape(orc, case):
     say(case)

@@ -159,3 +159,29 @@ def run_stats(p3d, o, coords, n, R, fovs, dists, maps_np, bf16, points, image_si
     else:
         assert got["cos_sum"] == 0.0
     return got, want
+
+
+def run_sample(p3d, o, feat_np, grid_np, bidx_np, bf16_in, out_bf16):
+    """p3d_bilinear_sample of feat_np at grid_np (batch indices bidx_np or
+    None) against the oracle: every value within 1e-5 of sum_k w_k |F_k|,
+    plus one bf16 rounding (2^-8 |ref|) for bf16 output. Returns the largest
+    error and the correlation."""
+    n = len(grid_np)
+    feat = to_dev(feat_np, bf16=bf16_in)
+    grid = to_dev(grid_np.astype(np.float32))
+    bidx = to_dev(bidx_np) if bidx_np is not None else None
+    C = feat_np.shape[-1]
+    out = torch.empty((n, C), dtype=torch.bfloat16 if out_bf16 else torch.float32,
+                      device="cuda")
+    p3d.p3d_bilinear_sample(feat, grid, out, batch_index=bidx)
+    torch.cuda.synchronize()
+    got = to_host(out)
+    ref = o.sample(feat_np, grid_np, bidx_np)
+    absf = np.abs(bf16_to_f64(feat_np) if bf16_in else feat_np.astype(np.float64))
+    mag = o.sample(absf.astype(np.float32), grid_np, bidx_np)      # sum_k w_k |F_k|
+    g = bf16_to_f64(got) if out_bf16 else got.astype(np.float64)
+    err = np.abs(g - ref)
+    bound = 1e-5 * mag + (2.0 ** -8 * np.abs(ref) if out_bf16 else 0.0) + 1e-30
+    assert np.all(err <= bound), "sample: %d off, worst %.3e" % ((err > bound).sum(),
+                                                                (err / bound).max())
+    return np.max(err), np.corrcoef(g.ravel(), ref.ravel())[0, 1] if g.size > 1 else 1.0

@@ -58,6 +58,7 @@
 #ifndef P3D_H
 #define P3D_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -299,6 +300,43 @@ p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution
                             const void* weight, int32_t out_dim, int32_t weight_in,
                             const void* bias, int64_t n_null,
                             void* out, uint8_t* mask, void* stream);
+
+/* ------------------------------------------------------------------------
+ * p3d_proj_cond_ws -- p3d_proj_cond_ex with the tokens taken in image-space
+ * order, through a caller-owned workspace. Same arguments, results and
+ * errors as p3d_proj_cond_ex, plus:
+ *
+ *   workspace        DEVICE buffer of at least workspace_bytes, 256-byte
+ *                    aligned, owned by the caller; its contents on entry do
+ *                    not matter and on return are undefined. Calls that
+ *                    share one workspace must not overlap (they would race
+ *                    on it); the library keeps no pointer to it.
+ *   workspace_bytes  >= p3d_proj_cond_workspace_size(n, batch, maps, n_maps),
+ *                    else P3D_ERR_INVALID_ARG with both sizes.
+ *
+ * For BF16 and n > 0 the call first sorts the tokens by the texel block
+ * their top-left bilinear corner falls in (batch item, then the Morton index
+ * of 16 x 16-texel blocks on the map with the most texels) with a counting
+ * sort in the workspace, then runs p3d_proj_cond_ex's fused kernel over the
+ * tokens in that order, writing each token's row and mask byte at the
+ * token's own index. Tokens that share corner rows are then processed
+ * together, so the rows are fetched fewer times. Each output row depends on
+ * its own token only, and the arithmetic per row is unchanged, so `out` and
+ * `mask` are identical bit for bit to p3d_proj_cond_ex's (pixel-aligned
+ * head commit of pixal3d_mrp_mlx; FlowCond commit of trellis.cpp PR #38).
+ * F32 calls and null-only calls run p3d_proj_cond_ex unchanged and do not
+ * touch the workspace.
+ * --------------------------------------------------------------------- */
+size_t p3d_proj_cond_workspace_size(int64_t n, int32_t batch, const p3d_map* maps,
+                                    int32_t n_maps);
+                                    /* 0 on invalid sizes (p3d_last_error says why) */
+p3d_status p3d_proj_cond_ws(const int32_t* coords, int64_t n, int32_t resolution,
+                            p3d_points points, const p3d_camera* cams, int32_t batch,
+                            p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                            const void* weight, int32_t out_dim, int32_t weight_in,
+                            const void* bias, int64_t n_null,
+                            void* out, uint8_t* mask,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * p3d_projection_stats -- projection diagnostics (PR #38, commits adding the

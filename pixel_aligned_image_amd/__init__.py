@@ -21,6 +21,7 @@ __all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_versi
            "p3d_project_points", "p3d_bilinear_sample", "p3d_proj_cond",
            "p3d_requantize_coords", "p3d_projection_stats", "stats_summary",
            "p3d_proj_sample", "p3d_proj_linear_grouped", "P3D_MAX_GROUPS",
+           "p3d_proj_cond_workspace_size", "proj_cond_workspace",
            "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libp3d.so")
@@ -95,6 +96,12 @@ def _load():
     L.p3d_proj_cond_ex.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
                                    ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp, vp,
                                    vp]
+    L.p3d_proj_cond_workspace_size.restype = ctypes.c_size_t
+    L.p3d_proj_cond_workspace_size.argtypes = [i64, i32, ctypes.POINTER(p3d_map), i32]
+    L.p3d_proj_cond_ws.restype = ctypes.c_int
+    L.p3d_proj_cond_ws.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
+                                   ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp, vp,
+                                   vp, ctypes.c_size_t, vp]
     return L
 
 
@@ -228,14 +235,43 @@ def p3d_bilinear_sample(feat, grid, out, batch_index=None, stream=None):
         _dev(out, "out", None, (n, C)), odt, _stream(stream)))
 
 
+def _map_array(feats):
+    maps = (p3d_map * len(feats))()
+    for i, f in enumerate(feats):
+        maps[i].feat = _dev(f, "feat[%d]" % i) if isinstance(f, torch.Tensor) else None
+        maps[i].height, maps[i].width, maps[i].channels = f.shape[1], f.shape[2], f.shape[3]
+    return maps
+
+
+def p3d_proj_cond_workspace_size(n, batch, feat):
+    """Bytes of device workspace p3d_proj_cond_ws needs; feat: one map or a
+    list of two (tensors, or anything with a 4-entry .shape)."""
+    feats = list(feat) if isinstance(feat, (list, tuple)) else [feat]
+    maps = (p3d_map * len(feats))()
+    for i, f in enumerate(feats):
+        maps[i].height, maps[i].width, maps[i].channels = f.shape[1], f.shape[2], f.shape[3]
+    size = lib.p3d_proj_cond_workspace_size(int(n), int(batch), maps, len(feats))
+    if size == 0:
+        raise P3DError(P3D_ERR_INVALID_ARG, lib.p3d_last_error().decode())
+    return int(size)
+
+
+def proj_cond_workspace(n, batch, feat, device="cuda"):
+    """A fresh uint8 device tensor large enough for p3d_proj_cond_ws."""
+    return torch.empty(p3d_proj_cond_workspace_size(n, batch, feat), dtype=torch.uint8,
+                       device=device)
+
+
 def p3d_proj_cond(coords, n, resolution, cams, feat, weight, out, bias=None, n_null=0,
-                  mask=None, stream=None, points="cell_centres"):
-    """Enqueue p3d_proj_cond (one map, cell centres) or p3d_proj_cond_ex.
-    feat: [B, H, W, C], or a list of two such maps (own H, W, C; samples
-    concatenated, map 0 first); weight: [D, C_w] (torch Linear layout; C_w is
-    checked against the summed C by the library); bias: [D] or None; out:
-    [n + n_null, D]; all of one dtype (float32 or bfloat16); mask: uint8 [n]
-    or None; points: "cell_centres" or "grid_nodes"."""
+                  mask=None, stream=None, points="cell_centres", workspace=None):
+    """Enqueue p3d_proj_cond (one map, cell centres), p3d_proj_cond_ex, or
+    p3d_proj_cond_ws when `workspace` (a uint8 device tensor, e.g. from
+    proj_cond_workspace) is given. feat: [B, H, W, C], or a list of two such
+    maps (own H, W, C; samples concatenated, map 0 first); weight: [D, C_w]
+    (torch Linear layout; C_w is checked against the summed C by the
+    library); bias: [D] or None; out: [n + n_null, D]; all of one dtype
+    (float32 or bfloat16); mask: uint8 [n] or None; points: "cell_centres" or
+    "grid_nodes"."""
     camarr, batch = _cams(cams)
     feats = list(feat) if isinstance(feat, (list, tuple)) else [feat]
     for f in feats:
@@ -258,6 +294,12 @@ def p3d_proj_cond(coords, n, resolution, cams, feat, weight, out, bias=None, n_n
               _dev(out, "out", dtype, (n + n_null, D)), _dev(mask, "mask", torch.uint8, (n,)),
               _stream(stream))
     c = _dev(coords, "coords", torch.int32, (n, 4))
+    if workspace is not None:
+        ws = _dev(workspace, "workspace", torch.uint8)
+        _check(lib.p3d_proj_cond_ws(c, n, int(resolution), POINTS[points], camarr, batch, dt,
+                                    _map_array(feats), len(feats), *common[:-1], ws,
+                                    workspace.numel(), common[-1]))
+        return
     if len(feats) == 1 and points == "cell_centres":
         B, H, W, C = feats[0].shape
         _check(lib.p3d_proj_cond(c, n, int(resolution), camarr, batch, _dev(feats[0], "feat"), dt,

@@ -103,6 +103,123 @@ p3d_status check_tokens(const char* fn, const int32_t* coords, int64_t n, int32_
     return P3D_OK;
 }
 
+// Every check of the fused call; on P3D_OK, *a and *tab describe the launch
+// (*nothing set to true when there is no work).
+p3d_status prepare_proj_cond(const char* fn, const int32_t* coords, int64_t n,
+                             int32_t resolution, p3d_points points, const p3d_camera* cams,
+                             int32_t batch, p3d_dtype dtype, const p3d_map* maps,
+                             int32_t n_maps, const void* weight, int32_t out_dim,
+                             int32_t weight_in, const void* bias, int64_t n_null, void* out,
+                             uint8_t* mask, ProjCondArgs* args, CamTable* tab_out,
+                             bool* nothing) {
+    CamTable& tab = *tab_out;
+    *nothing = false;
+    p3d_status st = check_tokens(fn, coords, n, resolution, points, cams, batch, &tab);
+    if (st != P3D_OK) return st;
+    if (!maps || n_maps < 1 || n_maps > 2)
+        return fail(P3D_ERR_INVALID_ARG, "%s: maps must be a host array of 1 or 2 maps, got %d",
+                    fn, maps ? n_maps : 0);
+    if (dtype != P3D_F32 && dtype != P3D_BF16)
+        return fail(P3D_ERR_DTYPE, "%s: dtype must be F32 or BF16, got %d", fn, (int)dtype);
+    const int epv = dtype == P3D_BF16 ? 8 : 4;
+    int64_t channels = 0;
+    for (int32_t m = 0; m < n_maps; ++m) {
+        char what[32];
+        snprintf(what, sizeof what, n_maps > 1 ? "maps[%d]" : "feature map", m);
+        st = check_map_size(fn, what, batch, maps[m].height, maps[m].width);
+        if (st != P3D_OK) return st;
+        if (maps[m].channels < 1)
+            return fail(P3D_ERR_INVALID_ARG, "%s: %s channels must be >= 1, got %d", fn, what,
+                        maps[m].channels);
+        if (maps[m].channels % epv)
+            return fail(P3D_ERR_UNSUPPORTED,
+                        "%s: %s channels must be a multiple of %d for %s (16-byte rows), got %d",
+                        fn, what, epv, dtype_name(dtype), maps[m].channels);
+        if (!aligned(maps[m].feat, 16))
+            return fail(P3D_ERR_UNSUPPORTED, "%s: %s feat must be 16-byte aligned", fn, what);
+        channels += maps[m].channels;
+    }
+    if (n_maps == 2 && maps[0].channels % 64)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: with two maps, maps[0].channels must be a multiple of 64, got %d", fn,
+                    maps[0].channels);
+    if (channels > INT32_MAX / 2)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: too many channels (%lld)", fn,
+                    (long long)channels);
+    if (n_null < 0 || n_null > kMaxTokens)
+        return fail(P3D_ERR_INVALID_ARG, "%s: n_null must be in [0, %lld], got %lld", fn,
+                    (long long)kMaxTokens, (long long)n_null);
+    if (out_dim < 1)
+        return fail(P3D_ERR_INVALID_ARG, "%s: out_dim must be >= 1, got %d", fn, out_dim);
+    if (out_dim > kMaxOutDim)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: out_dim must be <= %d, got %d", fn, kMaxOutDim,
+                    out_dim);
+    if (weight_in != channels) {
+        const p3d_map& m0 = maps[0];
+        if (n_maps == 1)
+            return fail(P3D_ERR_SHAPE,
+                        "%s: proj_linear weight is [%d, %d] but the feature map [%d, %d, %d, %d] "
+                        "has %d channels: the weight's input width must equal the map's channels",
+                        fn, out_dim, weight_in, batch, m0.height, m0.width, m0.channels,
+                        m0.channels);
+        const p3d_map& m1 = maps[1];
+        return fail(P3D_ERR_SHAPE,
+                    "%s: proj_linear weight is [%d, %d] but the feature maps [%d, %d, %d, %d] and "
+                    "[%d, %d, %d, %d] concatenate to %lld channels: the weight's input width must "
+                    "equal the summed channels",
+                    fn, out_dim, weight_in, batch, m0.height, m0.width, m0.channels, batch,
+                    m1.height, m1.width, m1.channels, (long long)channels);
+    }
+    if (out_dim % epv)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: out_dim must be a multiple of %d for %s (16-byte rows), got %d", fn, epv,
+                    dtype_name(dtype), out_dim);
+    if (!aligned(weight, 16) || !aligned(out, 16) || !aligned(bias, 16))
+        return fail(P3D_ERR_UNSUPPORTED, "%s: feat, weight, bias and out must be 16-byte aligned",
+                    fn);
+    if (n == 0 && n_null == 0) {
+        *nothing = true;
+        return P3D_OK;
+    }
+    if (!out) return fail(P3D_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (n > 0 && (!maps[0].feat || (n_maps == 2 && !maps[1].feat) || !weight))
+        return fail(P3D_ERR_INVALID_ARG, "%s: feat and weight must be non-NULL", fn);
+    ProjCondArgs& a = *args;
+    a = ProjCondArgs{};
+    a.coords = coords;
+    a.n = n;
+    a.R = resolution;
+    a.points = (int32_t)points;
+    a.batch = batch;
+    a.feat = maps[0].feat;
+    a.H = maps[0].height;
+    a.W = maps[0].width;
+    a.C = maps[0].channels;
+    if (n_maps == 2) {
+        a.feat1 = maps[1].feat;
+        a.H1 = maps[1].height;
+        a.W1 = maps[1].width;
+        a.C1 = maps[1].channels;
+    }
+    a.weight = weight;
+    a.bias = bias;
+    a.D = out_dim;
+    a.n_null = n_null;
+    a.out = out;
+    a.mask = mask;
+    return P3D_OK;
+}
+
+// Key map of the image-space order: the map with the most texels.
+void key_map(const p3d_map* maps, int32_t n_maps, int32_t* H, int32_t* W) {
+    *H = maps[0].height;
+    *W = maps[0].width;
+    if (n_maps == 2 && (int64_t)maps[1].height * maps[1].width > (int64_t)*H * *W) {
+        *H = maps[1].height;
+        *W = maps[1].width;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,97 +392,79 @@ p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution
                             const void* bias, int64_t n_null, void* out, uint8_t* mask,
                             void* stream) {
     const char* fn = "p3d_proj_cond";
+    ProjCondArgs a;
     CamTable tab;
-    p3d_status st = check_tokens(fn, coords, n, resolution, points, cams, batch, &tab);
+    bool nothing;
+    p3d_status st = prepare_proj_cond(fn, coords, n, resolution, points, cams, batch, dtype, maps,
+                                      n_maps, weight, out_dim, weight_in, bias, n_null, out, mask,
+                                      &a, &tab, &nothing);
     if (st != P3D_OK) return st;
-    if (!maps || n_maps < 1 || n_maps > 2)
-        return fail(P3D_ERR_INVALID_ARG, "%s: maps must be a host array of 1 or 2 maps, got %d",
-                    fn, maps ? n_maps : 0);
-    if (dtype != P3D_F32 && dtype != P3D_BF16)
-        return fail(P3D_ERR_DTYPE, "%s: dtype must be F32 or BF16, got %d", fn, (int)dtype);
-    const int epv = dtype == P3D_BF16 ? 8 : 4;
-    int64_t channels = 0;
-    for (int32_t m = 0; m < n_maps; ++m) {
-        char what[32];
-        snprintf(what, sizeof what, n_maps > 1 ? "maps[%d]" : "feature map", m);
-        st = check_map_size(fn, what, batch, maps[m].height, maps[m].width);
-        if (st != P3D_OK) return st;
-        if (maps[m].channels < 1)
-            return fail(P3D_ERR_INVALID_ARG, "%s: %s channels must be >= 1, got %d", fn, what,
-                        maps[m].channels);
-        if (maps[m].channels % epv)
-            return fail(P3D_ERR_UNSUPPORTED,
-                        "%s: %s channels must be a multiple of %d for %s (16-byte rows), got %d",
-                        fn, what, epv, dtype_name(dtype), maps[m].channels);
-        if (!aligned(maps[m].feat, 16))
-            return fail(P3D_ERR_UNSUPPORTED, "%s: %s feat must be 16-byte aligned", fn, what);
-        channels += maps[m].channels;
-    }
-    if (n_maps == 2 && maps[0].channels % 64)
-        return fail(P3D_ERR_UNSUPPORTED,
-                    "%s: with two maps, maps[0].channels must be a multiple of 64, got %d", fn,
-                    maps[0].channels);
-    if (channels > INT32_MAX / 2)
-        return fail(P3D_ERR_UNSUPPORTED, "%s: too many channels (%lld)", fn,
-                    (long long)channels);
-    if (n_null < 0 || n_null > kMaxTokens)
-        return fail(P3D_ERR_INVALID_ARG, "%s: n_null must be in [0, %lld], got %lld", fn,
-                    (long long)kMaxTokens, (long long)n_null);
-    if (out_dim < 1)
-        return fail(P3D_ERR_INVALID_ARG, "%s: out_dim must be >= 1, got %d", fn, out_dim);
-    if (out_dim > kMaxOutDim)
-        return fail(P3D_ERR_UNSUPPORTED, "%s: out_dim must be <= %d, got %d", fn, kMaxOutDim,
-                    out_dim);
-    if (weight_in != channels) {
-        const p3d_map& m0 = maps[0];
-        if (n_maps == 1)
-            return fail(P3D_ERR_SHAPE,
-                        "%s: proj_linear weight is [%d, %d] but the feature map [%d, %d, %d, %d] "
-                        "has %d channels: the weight's input width must equal the map's channels",
-                        fn, out_dim, weight_in, batch, m0.height, m0.width, m0.channels,
-                        m0.channels);
-        const p3d_map& m1 = maps[1];
-        return fail(P3D_ERR_SHAPE,
-                    "%s: proj_linear weight is [%d, %d] but the feature maps [%d, %d, %d, %d] and "
-                    "[%d, %d, %d, %d] concatenate to %lld channels: the weight's input width must "
-                    "equal the summed channels",
-                    fn, out_dim, weight_in, batch, m0.height, m0.width, m0.channels, batch,
-                    m1.height, m1.width, m1.channels, (long long)channels);
-    }
-    if (out_dim % epv)
-        return fail(P3D_ERR_UNSUPPORTED,
-                    "%s: out_dim must be a multiple of %d for %s (16-byte rows), got %d", fn, epv,
-                    dtype_name(dtype), out_dim);
-    if (!aligned(weight, 16) || !aligned(out, 16) || !aligned(bias, 16))
-        return fail(P3D_ERR_UNSUPPORTED, "%s: feat, weight, bias and out must be 16-byte aligned",
-                    fn);
-    if (n == 0 && n_null == 0) return ok();
-    if (!out) return fail(P3D_ERR_INVALID_ARG, "%s: out is NULL", fn);
-    if (n > 0 && (!maps[0].feat || (n_maps == 2 && !maps[1].feat) || !weight))
-        return fail(P3D_ERR_INVALID_ARG, "%s: feat and weight must be non-NULL", fn);
-    ProjCondArgs a{};
-    a.coords = coords;
-    a.n = n;
-    a.R = resolution;
-    a.points = (int32_t)points;
-    a.batch = batch;
-    a.feat = maps[0].feat;
-    a.H = maps[0].height;
-    a.W = maps[0].width;
-    a.C = maps[0].channels;
-    if (n_maps == 2) {
-        a.feat1 = maps[1].feat;
-        a.H1 = maps[1].height;
-        a.W1 = maps[1].width;
-        a.C1 = maps[1].channels;
-    }
-    a.weight = weight;
-    a.bias = bias;
-    a.D = out_dim;
-    a.n_null = n_null;
-    a.out = out;
-    a.mask = mask;
+    if (nothing) return ok();
     hipError_t e = launch_proj_cond(a, dtype, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+size_t p3d_proj_cond_workspace_size(int64_t n, int32_t batch, const p3d_map* maps,
+                                    int32_t n_maps) {
+    const char* fn = "p3d_proj_cond_workspace_size";
+    if (n < 0 || n > kMaxTokens || batch < 1 || batch > P3D_MAX_BATCH || !maps || n_maps < 1 ||
+        n_maps > 2) {
+        fail(P3D_ERR_INVALID_ARG,
+             "%s: needs 0 <= n <= %lld, 1 <= batch <= %d and a host array of 1 or 2 maps, "
+             "got n = %lld, batch = %d, %d maps",
+             fn, (long long)kMaxTokens, P3D_MAX_BATCH, (long long)n, batch, maps ? n_maps : 0);
+        return 0;
+    }
+    for (int32_t m = 0; m < n_maps; ++m) {
+        if (maps[m].height < 1 || maps[m].width < 1) {
+            fail(P3D_ERR_INVALID_ARG, "%s: maps[%d] height/width must be >= 1, got %dx%d", fn, m,
+                 maps[m].height, maps[m].width);
+            return 0;
+        }
+    }
+    int32_t kH, kW;
+    key_map(maps, n_maps, &kH, &kW);
+    g_err.clear();
+    return order_layout(n, batch, kH, kW, nullptr, nullptr) + (((size_t)n * 4 + 255) & ~(size_t)255);
+}
+
+p3d_status p3d_proj_cond_ws(const int32_t* coords, int64_t n, int32_t resolution,
+                            p3d_points points, const p3d_camera* cams, int32_t batch,
+                            p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                            const void* weight, int32_t out_dim, int32_t weight_in,
+                            const void* bias, int64_t n_null, void* out, uint8_t* mask,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "p3d_proj_cond_ws";
+    ProjCondArgs a;
+    CamTable tab;
+    bool nothing;
+    p3d_status st = prepare_proj_cond(fn, coords, n, resolution, points, cams, batch, dtype, maps,
+                                      n_maps, weight, out_dim, weight_in, bias, n_null, out, mask,
+                                      &a, &tab, &nothing);
+    if (st != P3D_OK) return st;
+    if (nothing) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == P3D_BF16 && n > 0) {
+        int32_t kH, kW;
+        key_map(maps, n_maps, &kH, &kW);
+        OrderBufs ob;
+        const size_t sort_bytes = order_layout(n, batch, kH, kW, workspace, &ob);
+        const size_t need = sort_bytes + (((size_t)n * 4 + 255) & ~(size_t)255);
+        if (!workspace || workspace_bytes < need)
+            return fail(P3D_ERR_INVALID_ARG,
+                        "%s: workspace must be a device buffer of at least %zu bytes "
+                        "(p3d_proj_cond_workspace_size), got %zu bytes at %p",
+                        fn, need, workspace_bytes, workspace);
+        if (!aligned(workspace, 256))
+            return fail(P3D_ERR_UNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+        int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + sort_bytes);
+        const OrderArgs oa{coords, n, resolution, (int32_t)points, batch};
+        hipError_t e = launch_order(oa, tab, ob, order, s);
+        if (e != hipSuccess) return hip_fail(fn, e);
+        a.order = order;
+    }
+    hipError_t e = launch_proj_cond(a, dtype, tab, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }

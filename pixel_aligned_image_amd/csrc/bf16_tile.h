@@ -158,8 +158,9 @@ __device__ __forceinline__ void consume(f32x4_t (&acc)[FJ][TIt], int lane, int c
 // wave's 16 TIt x 64 block in the free W stages (token-major 128-byte rows,
 // the same slot swizzle) and write 16-byte row pieces with non-temporal
 // stores (the output is not read back here). Lane l of block (j, i)
-// holds features 4*(l/16) + r of token l % 16. out is [n, D] bf16; rows at or
-// past n are not touched.
+// holds features 4*(l/16) + r of token l % 16. out is [n, D] bf16; tile row
+// t goes to output row m0 + t, or to rows[t] when an LDS table `rows` is
+// given (-1: not stored); rows at or past n are not touched.
 constexpr int OLD_BATCH = 4;        // residual loads in flight together (registers)
 static_assert(TI % OLD_BATCH == 0, "residual batches");
 
@@ -167,7 +168,8 @@ template <bool Accumulate, int TIt = TI>
 __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TIt], int lane, int cw,
                                            int32_t n0, int64_t m0, int64_t n, int32_t D,
                                            const uint16_t* bias16, void* out,
-                                           uint4* __restrict__ sW0, uint4* __restrict__ sW1) {
+                                           uint4* __restrict__ sW0, uint4* __restrict__ sW1,
+                                           const int32_t* rows = nullptr) {
     constexpr int BATCH = TIt < OLD_BATCH ? TIt : OLD_BATCH;
     static_assert(TIt % BATCH == 0, "residual batches");
     const int fbase = n0 + cw * WN;
@@ -223,9 +225,9 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TIt], int la
     for (int r = 0; r < TIt * 16 * 8 / 64; ++r) {
         const int q = r * 64 + lane;
         const int t = q >> 3, cv = q & 7;
-        const int64_t tok = m0 + t;
+        const int64_t tok = rows ? (int64_t)rows[t] : (m0 + t < n ? m0 + t : -1);
         const int colv = (fbase >> 3) + cv;
-        if (tok < n && colv < dv) store_nt16(out4 + tok * dv + colv, stage4[slot(t, cv)]);
+        if (tok >= 0 && colv < dv) store_nt16(out4 + tok * dv + colv, stage4[slot(t, cv)]);
     }
 }
 

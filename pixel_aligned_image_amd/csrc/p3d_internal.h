@@ -196,6 +196,7 @@ struct ProjCondArgs {
     int64_t n_null;
     void* out;
     uint8_t* mask;
+    const int32_t* order;         // token of each processed position, or NULL (identity)
 };
 
 struct RequantArgs {
@@ -224,6 +225,29 @@ struct GroupedArgs {
     const void* bias[P3D_MAX_GROUPS];   // [D] bf16 or NULL
     void* out[P3D_MAX_GROUPS];          // [n, D] bf16
 };
+
+// Image-space token order (order.hip): a counting sort of the tokens by the
+// texel block their top-left corner projects to on the key map.
+struct OrderArgs {
+    const int32_t* coords;
+    int64_t n;
+    int32_t R, points, batch;
+};
+struct OrderBufs {
+    uint32_t* bins;               // [n] bin of every token
+    uint32_t* hist;               // [nbins] tokens per bin
+    uint32_t* cursor;             // [nbins] next sorted position of each bin
+    int32_t kH, kW, shift;        // key map; texel -> block shift
+    uint32_t per_item;            // bins per batch item
+    int32_t nbins;
+};
+// Workspace layout of the sort for n tokens (pointers relative to `base`,
+// which may be NULL to size it); returns the byte count, a multiple of 256.
+size_t order_layout(int64_t n, int32_t batch, int32_t kH, int32_t kW, void* base,
+                    OrderBufs* ob);
+// order[i] = the token at sorted position i (a permutation of [0, n)).
+hipError_t launch_order(const OrderArgs& a, const CamTable& cams, const OrderBufs& ob,
+                        int32_t* order, hipStream_t s);
 
 hipError_t launch_project(const ProjectArgs& a, const CamTable& cams, hipStream_t s);
 hipError_t launch_grouped(const GroupedArgs& a, bool accumulate, hipStream_t s);

@@ -105,15 +105,18 @@ __device__ __forceinline__ uint4 blend_bf16(const uint4 (&q)[4], const float (&w
 template <int G>
 using Gq = uint4[G][4];
 
-// Corner metadata of token t on an H x W map: (top-left corner row, the 0/1
-// row steps to the right and lower corners, x fraction, y fraction); a token
-// past the end gets weight 0 everywhere (flag 4 in the steps).
+// Corner metadata of the token at position t on an H x W map: (top-left
+// corner row, the 0/1 row steps to the right and lower corners, x fraction,
+// y fraction); a position past the end gets weight 0 everywhere (flag 4 in
+// the steps). Position t holds token a.order[t] (t itself without an order);
+// *mask receives its in-image flag.
 __device__ __forceinline__ int4 token_entry(const ProjCondArgs& a, const CamTable& cams,
                                             int64_t t, int32_t H, int32_t W, uint8_t* mask) {
     int4 e = make_int4(0, 4, 0, 0);
     if (t < a.n) {
+        const int64_t tok = a.order ? (int64_t)a.order[t] : t;
         int32_t b, x, y, z;
-        token_cell(a.coords, t, a.R, b, x, y, z);
+        token_cell(a.coords, tok, a.R, b, x, y, z);
         const Projected pr = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
         const SrcIdx sx = source_index(pr.gx, W);
         const SrcIdx sy = source_index(pr.gy, H);
@@ -377,7 +380,7 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
             const int64_t t = m0 + ptid;
             uint8_t mk = 0;
             s_tok[ptid] = token_entry(a, cams, t, a.H, a.W, &mk);
-            if (a.mask && nt == 0 && t < a.n) a.mask[t] = mk;
+            if (a.mask && nt == 0 && t < a.n) a.mask[a.order ? (int64_t)a.order[t] : t] = mk;
         }
         lds_barrier();                                            // tokens parked
 
@@ -403,6 +406,12 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
         for (int kc = 0; kc < nk2; kc += 2) {
             produce(p, nw, a, cams, m0, k1, kc, nk2, gq, sA1, sW1);
             produce(p, nw, a, cams, m0, k1, kc + 1, nk2, gq, sA0, sW0);
+        }
+        // with a token order, the output row of each tile row, for the
+        // consumers' stores (S stage 0 is free after the last chunk)
+        if (a.order) {
+            int32_t* s_rows = reinterpret_cast<int32_t*>(sA0);
+            if (ptid < BMt) s_rows[ptid] = m0 + ptid < a.n ? a.order[m0 + ptid] : -1;
         }
         __syncthreads();                                          // consumers staged
         return;
@@ -452,7 +461,8 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
     }
 
     store_tile<false, TIt>(acc, lane, cw, n0, m0, a.n, a.D,
-                           reinterpret_cast<const uint16_t*>(a.bias), a.out, sW0, sW1);
+                           reinterpret_cast<const uint16_t*>(a.bias), a.out, sW0, sW1,
+                           a.order ? reinterpret_cast<const int32_t*>(sA0) : nullptr);
 }
 
 // Work of workgroup g, which runs on XCD x = g % 8 as its (g / 8)-th:

@@ -185,3 +185,26 @@ def run_sample(p3d, o, feat_np, grid_np, bidx_np, bf16_in, out_bf16):
     assert np.all(err <= bound), "sample: %d off, worst %.3e" % ((err > bound).sum(),
                                                                 (err / bound).max())
     return np.max(err), np.corrcoef(g.ravel(), ref.ravel())[0, 1] if g.size > 1 else 1.0
+
+
+def tile_edge_rows(n, D, cus, bm=128, bn=512):
+    """First and last token row of every whole tile and of every tail part of
+    the fused bf16 launch (128-token tiles, 512-feature N tiles; the tiles
+    past the last full round on `cus` compute units run as 32- or 64-token
+    parts when four or two times that many fit one round)."""
+    m_tiles = -(-n // bm)
+    n_tiles = -(-D // bn)
+    tiles = m_tiles * n_tiles
+    rem = tiles % cus
+    split = 4 if rem and rem * 4 <= cus else (2 if rem and rem * 2 <= cus else 1)
+    rows = []
+    for mt in range(m_tiles):
+        first = mt * n_tiles
+        parts = split if first >= tiles - rem or (first + n_tiles - 1) >= tiles - rem else 1
+        step = bm // parts
+        for p in range(parts):
+            lo = mt * bm + p * step
+            hi = min(lo + step, n) - 1
+            if lo < n:
+                rows += [lo, hi]
+    return np.unique(np.array(rows, np.int64))

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(p3d):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     lib = ctypes.CDLL(p3d.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -309,3 +309,51 @@ def test_proj_sample_validation(p3d):
     st = p3d.lib.p3d_proj_sample(FAKE, 16, 8, 0, cams, 1, 1, arr, 2, FAKE, NULL, NULL)
     assert st == 4 and "maps[1] channels" in p3d.p3d_last_error()
     assert p3d.lib.p3d_proj_sample(NULL, 0, 8, 0, cams, 1, 1, arr, 1, NULL, NULL, NULL) == 0
+
+
+def _maps(p3d, shapes):
+    arr = (p3d.p3d_map * len(shapes))()
+    for i, (h, w, c) in enumerate(shapes):
+        arr[i].feat = None
+        arr[i].height, arr[i].width, arr[i].channels = h, w, c
+    return arr
+
+
+def test_proj_cond_workspace_size(p3d):
+    lib = p3d.lib
+    one = _maps(p3d, [(512, 512, 2048)])
+    size = lib.p3d_proj_cond_workspace_size(100000, 1, one, 1)
+    # sort keys and the order itself (4 bytes per token each) plus two bin
+    # tables, every part 256-byte aligned
+    assert size % 256 == 0 and 800000 <= size < 800000 + 2 * 4 * 16384 + 4 * 256, size
+    assert lib.p3d_proj_cond_workspace_size(0, 1, one, 1) > 0
+    two = _maps(p3d, [(64, 64, 1024), (512, 512, 1024)])
+    assert lib.p3d_proj_cond_workspace_size(100000, 1, two, 2) == size
+    for args in [(-1, 1, one, 1), (10, 0, one, 1), (10, 1, one, 3), (10, 1, None, 1),
+                 (10, 1, _maps(p3d, [(0, 4, 8)]), 1)]:
+        assert lib.p3d_proj_cond_workspace_size(*args) == 0, args
+        assert p3d.p3d_last_error().startswith("p3d_proj_cond_workspace_size")
+
+
+def test_proj_cond_ws_validation(p3d):
+    """Argument checks run before anything is enqueued: a short workspace
+    names both sizes; the shared checks name the ws entry point."""
+    lib = p3d.lib
+    cams = p3d.make_cameras([(2.0, 2.0)])
+    one = _maps(p3d, [(8, 8, 16)])
+    one[0].feat = 4096
+    need = lib.p3d_proj_cond_workspace_size(40, 1, one, 1)
+    st = lib.p3d_proj_cond_ws(4096, 40, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 16, None,
+                              0, 8192, None, 4096, need - 256, None)
+    assert st == p3d.P3D_ERR_INVALID_ARG
+    msg = p3d.p3d_last_error()
+    assert msg.startswith("p3d_proj_cond_ws") and str(need) in msg and str(need - 256) in msg
+    st = lib.p3d_proj_cond_ws(4096, 40, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 24, None,
+                              0, 8192, None, 4096, need, None)
+    assert st == p3d.P3D_ERR_SHAPE and "[32, 24]" in p3d.p3d_last_error()
+    st = lib.p3d_proj_cond_ws(4096, 40, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 16, None,
+                              0, 8192, None, 4100, need, None)
+    assert st == p3d.P3D_ERR_UNSUPPORTED and "256-byte" in p3d.p3d_last_error()
+    # nothing to do: no workspace needed
+    assert lib.p3d_proj_cond_ws(None, 0, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 16,
+                                None, 0, 8192, None, None, 0, None) == p3d.P3D_OK

@@ -22,7 +22,8 @@ import oracle
 import p3d_synth as synth
 import pixel_aligned_image_amd as p3d
 from parity_util import (Inputs, bf16_to_f64, check_bf16_linear, check_fp32_linear,
-                         oracle_cameras, product_cameras, run_sample, to_dev, to_host)
+                         oracle_cameras, product_cameras, run_sample, tile_edge_rows, to_dev,
+                         to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -200,15 +201,17 @@ def test_bilinear_sample_workloads(orc, wl):
 
 # ---------------------------------------------------------- fused path
 def _run_proj_cond(o, coords, n, R, fovs, dists, feat_np, W_np, b_np, n_null, bf16, rows,
-                   image_size, stream=None):
+                   image_size, stream=None, keep=False, workspace=None):
     B, H, Wd, C = feat_np.shape
     D = W_np.shape[0]
     cp, fo, do = cams_both(o, fovs, dists, image_size)
     dt = torch.bfloat16 if bf16 else torch.float32
     out = torch.full((n + n_null, D), float("nan"), dtype=dt, device="cuda")
     mask = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+    ws = None if workspace is None else p3d.proj_cond_workspace(n, B, feat_np)
     p3d.p3d_proj_cond(to_dev(coords), n, R, cp, to_dev(feat_np, bf16), to_dev(W_np, bf16),
-                      out, bias=to_dev(b_np, bf16), n_null=n_null, mask=mask, stream=stream)
+                      out, bias=to_dev(b_np, bf16), n_null=n_null, mask=mask, stream=stream,
+                      workspace=ws)
     torch.cuda.synchronize()
     Yref, mref = o.proj_cond_rows(coords, n, R, fo, do, feat_np, W_np, b_np, n_null, rows)
     got = to_host(out[torch.from_numpy(rows).cuda()])
@@ -228,6 +231,8 @@ def _run_proj_cond(o, coords, n, R, fovs, dists, feat_np, W_np, b_np, n_null, bf
                              None if b_np is None else np.abs(b_np), n_null, rows[~null])[0]
         check_fp32_linear(got[~null], Yref[~null], S)
         stats = (np.abs(got[~null] - Yref[~null]).max() if (~null).any() else 0, 1)
+    if keep:
+        return gmask, stats, out
     return gmask, stats
 
 
@@ -290,23 +295,73 @@ def test_proj_cond_small(orc, case):
     rows = np.arange(n + case["n_null"])
     _run_proj_cond(orc, coords, n, R, fovs, dists, featf, Wf, bf, case["n_null"],
                    case["bf16"], rows, case["W"])
+    # the same case with the tokens in image-space order: every row and mask
+    # byte against the oracle again
+    _run_proj_cond(orc, coords, n, R, fovs, dists, featf, Wf, bf, case["n_null"],
+                   case["bf16"], rows, case["W"], workspace=True)
 
 
 def test_proj_cond_workloads(orc, wl):
+    """Full size, in the launch configuration the bench times. Every row up to
+    16384 tokens; above: 16384 seeded token rows, the first and last row of
+    every whole tile and tail part, the first and last row of every 128-row null block
+    plus 64 seeded null rows against the oracle; the mask of every token
+    against the oracle's projection; and no output element left unwritten
+    (the output starts as NaN)."""
     w = wl.w
     n, nn = wl.n, wl.n_null
     rng = np.random.default_rng(9)
-    if n <= 4096:
+    if n <= 16384:
         rows = np.arange(n + nn)
     else:
-        pick = rng.choice(n, size=384, replace=False)
-        edge = [0, 1, 127, 128, n - 129, n - 1]
-        nulls = [n, n + nn - 1] + list(rng.integers(n, n + nn, 16)) if nn else []
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        pick = rng.choice(n, size=16384, replace=False)
+        edge = tile_edge_rows(n, w.out_dim, cus)
+        nulls = []
+        if nn:
+            nb = np.arange(0, nn, 128)
+            nulls = np.concatenate([n + nb, n + np.minimum(nb + 127, nn - 1),
+                                    rng.integers(n, n + nn, 64)])
         rows = np.unique(np.concatenate([pick, edge, nulls]).astype(np.int64))
+        say("proj_cond", w.name, "rows checked: %d (16384 seeded, %d tile/part edges, %d null)"
+            % (len(rows), len(edge), len(nulls)))
     say("proj_cond", w.name, "n =", n, "n_null =", nn, "rows checked =", len(rows))
-    gmask, stats = _run_proj_cond(orc, wl.coords, n, w.resolution, wl.fovs, wl.dists, wl.feat,
-                                  wl.weight, wl.bias, nn, wl.bf16, rows, w.width)
-    say("  max|diff| stat %.3e corr %.8f coverage %.4f" % (stats[0], stats[1], gmask.mean()))
+    gmask, stats, out = _run_proj_cond(orc, wl.coords, n, w.resolution, wl.fovs, wl.dists,
+                                       wl.feat, wl.weight, wl.bias, nn, wl.bf16, rows, w.width,
+                                       keep=True)
+    assert not torch.isnan(out.float()).any().item(), "an output element was not written"
+    fo, do = oracle_cameras(orc, wl.fovs, wl.dists, w.width)
+    ref = orc.project(wl.coords, n, w.resolution, fo, do, w.height, w.width)
+    ref_mask = ref["mask"] if isinstance(ref, dict) else ref[-1]
+    assert np.array_equal(gmask, ref_mask), "fused mask differs from the oracle on %d of %d" % (
+        int((gmask != ref_mask).sum()), n)
+    say("  mask: all %d tokens equal; max|diff| stat %.3e corr %.8f coverage %.4f"
+        % (n, stats[0], stats[1], gmask.mean()))
+
+
+def test_proj_cond_ws_workloads_bitwise(orc, wl):
+    """p3d_proj_cond_ws (tokens in image-space order) writes the same bytes
+    as p3d_proj_cond on every row and mask byte of the full-size workload;
+    with the row checks above that carries the oracle comparison over."""
+    w = wl.w
+    n, nn = wl.n, wl.n_null
+    cp = product_cameras(p3d, wl.fovs, wl.dists, w.width)
+    dt = torch.bfloat16 if wl.bf16 else torch.float32
+    args = (to_dev(wl.coords), n, w.resolution, cp, to_dev(wl.feat, wl.bf16),
+            to_dev(wl.weight, wl.bf16))
+    bias = to_dev(wl.bias, wl.bf16)
+    outs, masks = [], []
+    for ws in (None, p3d.proj_cond_workspace(n, w.batch, args[4])):
+        out = torch.full((n + nn, w.out_dim), float("nan"), dtype=dt, device="cuda")
+        mask = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+        p3d.p3d_proj_cond(*args, out, bias=bias, n_null=nn, mask=mask, workspace=ws)
+        outs.append(out)
+        masks.append(mask)
+    torch.cuda.synchronize()
+    bits = torch.int16 if wl.bf16 else torch.int32
+    assert torch.equal(outs[0].view(bits), outs[1].view(bits)), "ordered rows differ"
+    assert torch.equal(masks[0], masks[1]), "ordered mask differs"
+    say("proj_cond_ws", w.name, "all %d rows and %d mask bytes bit-identical" % (n + nn, n))
 
 
 def test_proj_cond_side_stream_matches_default(orc):
@@ -355,3 +410,24 @@ def test_proj_cond_channel_mismatch_names_both_shapes():
         p3d.p3d_proj_cond(coords, 8, 8, [(2.0, 2.0)], feat, weight, out)
     assert e.value.status == p3d.P3D_ERR_SHAPE
     assert "[32, 24]" in e.value.message and "[1, 4, 4, 16]" in e.value.message
+
+
+def test_proj_cond_ws_errors():
+    """A short or misaligned workspace is refused before anything runs, with
+    both sizes in the message; an F32 call ignores the workspace."""
+    feat = torch.zeros((1, 8, 8, 16), dtype=torch.bfloat16, device="cuda")
+    weight = torch.zeros((32, 16), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((40, 32), 5.0, dtype=torch.bfloat16, device="cuda")
+    coords = torch.zeros((40, 4), dtype=torch.int32, device="cuda")
+    need = p3d.p3d_proj_cond_workspace_size(40, 1, feat)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(p3d.P3DError) as e:
+        p3d.p3d_proj_cond(coords, 40, 8, [(2.0, 2.0)], feat, weight, out, workspace=small)
+    assert e.value.status == p3d.P3D_ERR_INVALID_ARG
+    assert str(need) in e.value.message and str(need - 256) in e.value.message
+    torch.cuda.synchronize()
+    assert np.all(bf16_to_f64(to_host(out)) == 5.0)
+    big = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(p3d.P3DError) as e:
+        p3d.p3d_proj_cond(coords, 40, 8, [(2.0, 2.0)], feat, weight, out, workspace=big[1:])
+    assert e.value.status == p3d.P3D_ERR_UNSUPPORTED and "256-byte" in e.value.message

@@ -338,6 +338,24 @@ p3d_status p3d_proj_cond_ws(const int32_t* coords, int64_t n, int32_t resolution
                             void* out, uint8_t* mask,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* p3d_proj_cond_noalloc -- p3d_proj_cond_ws without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The scratch lives in
+ * a static device array of the library, P3D_NOALLOC_MAX_TOKENS tokens' worth
+ * (8.25 MB per GPU, held until the process ends); the call allocates
+ * nothing itself. Same arguments, results and errors as p3d_proj_cond_ex,
+ * plus P3D_ERR_UNSUPPORTED when n > P3D_NOALLOC_MAX_TOKENS (nothing is
+ * enqueued). The array is shared by every call on a GPU and keeps the last
+ * call's contents: calls that overlap on one GPU (several streams or host
+ * threads) race on it and must be serialised by the caller. */
+#define P3D_NOALLOC_MAX_TOKENS 1048576
+p3d_status p3d_proj_cond_noalloc(const int32_t* coords, int64_t n, int32_t resolution,
+                                 p3d_points points, const p3d_camera* cams, int32_t batch,
+                                 p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                 const void* weight, int32_t out_dim, int32_t weight_in,
+                                 const void* bias, int64_t n_null,
+                                 void* out, uint8_t* mask, void* stream);
+
 /* ------------------------------------------------------------------------
  * p3d_projection_stats -- projection diagnostics (PR #38, commits adding the
  * per-stage projection statistics and the cross-resolution agreement). The

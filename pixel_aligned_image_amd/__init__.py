@@ -21,7 +21,7 @@ __all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_versi
            "p3d_project_points", "p3d_bilinear_sample", "p3d_proj_cond",
            "p3d_requantize_coords", "p3d_projection_stats", "stats_summary",
            "p3d_proj_sample", "p3d_proj_linear_grouped", "P3D_MAX_GROUPS",
-           "p3d_proj_cond_workspace_size", "proj_cond_workspace",
+           "p3d_proj_cond_workspace_size", "proj_cond_workspace", "P3D_NOALLOC_MAX_TOKENS",
            "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libp3d.so")
@@ -30,6 +30,7 @@ P3D_OK, P3D_ERR_INVALID_ARG, P3D_ERR_SHAPE, P3D_ERR_DTYPE, P3D_ERR_UNSUPPORTED, 
 P3D_F32, P3D_BF16 = 0, 1
 P3D_MAX_BATCH = 256
 P3D_MAX_GROUPS = 64
+P3D_NOALLOC_MAX_TOKENS = 1048576
 POINTS = {"cell_centres": 0, "grid_nodes": 1}          # p3d_points
 REQUANT = {"round_nodes": 0, "floor_cells": 1}          # p3d_requant
 
@@ -102,6 +103,10 @@ def _load():
     L.p3d_proj_cond_ws.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
                                    ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp, vp,
                                    vp, ctypes.c_size_t, vp]
+    L.p3d_proj_cond_noalloc.restype = ctypes.c_int
+    L.p3d_proj_cond_noalloc.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
+                                        ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp,
+                                        vp, vp]
     return L
 
 
@@ -263,10 +268,11 @@ def proj_cond_workspace(n, batch, feat, device="cuda"):
 
 
 def p3d_proj_cond(coords, n, resolution, cams, feat, weight, out, bias=None, n_null=0,
-                  mask=None, stream=None, points="cell_centres", workspace=None):
+                  mask=None, stream=None, points="cell_centres", workspace=None, noalloc=False):
     """Enqueue p3d_proj_cond (one map, cell centres), p3d_proj_cond_ex, or
     p3d_proj_cond_ws when `workspace` (a uint8 device tensor, e.g. from
-    proj_cond_workspace) is given. feat: [B, H, W, C], or a list of two such
+    proj_cond_workspace) is given, or p3d_proj_cond_noalloc when noalloc is
+    true (the library's own scratch). feat: [B, H, W, C], or a list of two such
     maps (own H, W, C; samples concatenated, map 0 first); weight: [D, C_w]
     (torch Linear layout; C_w is checked against the summed C by the
     library); bias: [D] or None; out: [n + n_null, D]; all of one dtype
@@ -294,6 +300,10 @@ def p3d_proj_cond(coords, n, resolution, cams, feat, weight, out, bias=None, n_n
               _dev(out, "out", dtype, (n + n_null, D)), _dev(mask, "mask", torch.uint8, (n,)),
               _stream(stream))
     c = _dev(coords, "coords", torch.int32, (n, 4))
+    if noalloc:
+        _check(lib.p3d_proj_cond_noalloc(c, n, int(resolution), POINTS[points], camarr, batch, dt,
+                                         _map_array(feats), len(feats), *common))
+        return
     if workspace is not None:
         ws = _dev(workspace, "workspace", torch.uint8)
         _check(lib.p3d_proj_cond_ws(c, n, int(resolution), POINTS[points], camarr, batch, dt,

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "p3d_internal.h"
@@ -220,6 +221,76 @@ void key_map(const p3d_map* maps, int32_t n_maps, int32_t* H, int32_t* W) {
     }
 }
 
+// Bytes of the ordered path's scratch for n tokens: the sort (bins, counts)
+// and the order itself.
+size_t ordered_bytes(int64_t n, int32_t batch, const p3d_map* maps, int32_t n_maps,
+                     OrderBufs* ob, void* base) {
+    int32_t kH, kW;
+    key_map(maps, n_maps, &kH, &kW);
+    return order_layout(n, batch, kH, kW, base, ob) + (((size_t)n * 4 + 255) & ~(size_t)255);
+}
+
+// The launches of p3d_proj_cond_ws once the arguments are checked: BF16
+// calls with tokens sort them in `base` (bytes long) and run the fused kernel
+// through that order; other calls run p3d_proj_cond_ex's kernels.
+p3d_status run_ordered(const char* fn, ProjCondArgs a, const CamTable& tab, p3d_dtype dtype,
+                       const p3d_map* maps, int32_t n_maps, void* base, size_t bytes,
+                       hipStream_t s) {
+    if (dtype == P3D_BF16 && a.n > 0) {
+        OrderBufs ob;
+        const size_t need = ordered_bytes(a.n, a.batch, maps, n_maps, &ob, base);
+        if (!base || bytes < need)
+            return fail(P3D_ERR_INVALID_ARG,
+                        "%s: workspace must be a device buffer of at least %zu bytes "
+                        "(p3d_proj_cond_workspace_size), got %zu bytes at %p",
+                        fn, need, bytes, base);
+        if (!aligned(base, 256))
+            return fail(P3D_ERR_UNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+        int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(base) + need -
+                                                    (((size_t)a.n * 4 + 255) & ~(size_t)255));
+        const OrderArgs oa{a.coords, a.n, a.R, a.points, a.batch};
+        hipError_t e = launch_order(oa, tab, ob, order, s);
+        if (e != hipSuccess) return hip_fail(fn, e);
+        a.order = order;
+    }
+    hipError_t e = launch_proj_cond(a, dtype, tab, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
+// Scratch of p3d_proj_cond_noalloc, for callers that cannot allocate: the
+// sort of up to P3D_NOALLOC_MAX_TOKENS tokens (bins, bin counts, order),
+// 8.25 MB that every GPU the library runs on holds until the process ends.
+// Host code never uses this name as an address (on the host it is only a
+// stand-in for the device variable): scratch_address() looks up the device
+// address once per device, with that device current, and the launches take
+// that pointer. The bin counts are cleared by a kernel on every call; every
+// other byte is written before it is read. Calls that overlap on one GPU
+// share the array and race.
+constexpr size_t kScratchBytes = (size_t)P3D_NOALLOC_MAX_TOKENS * 8 + 2 * 65536 + 1024;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+p3d_status scratch_address(const char* fn, void** out) {
+    static std::mutex lock;
+    static void* addr[64] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64)
+        return fail(P3D_ERR_HIP, "%s: no current device (%s)", fn,
+                    e != hipSuccess ? hipGetErrorString(e) : "device index out of range");
+    std::lock_guard<std::mutex> g(lock);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(P3D_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed: %s",
+                        fn, hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return P3D_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -423,10 +494,8 @@ size_t p3d_proj_cond_workspace_size(int64_t n, int32_t batch, const p3d_map* map
             return 0;
         }
     }
-    int32_t kH, kW;
-    key_map(maps, n_maps, &kH, &kW);
     g_err.clear();
-    return order_layout(n, batch, kH, kW, nullptr, nullptr) + (((size_t)n * 4 + 255) & ~(size_t)255);
+    return ordered_bytes(n, batch, maps, n_maps, nullptr, nullptr);
 }
 
 p3d_status p3d_proj_cond_ws(const int32_t* coords, int64_t n, int32_t resolution,
@@ -444,29 +513,37 @@ p3d_status p3d_proj_cond_ws(const int32_t* coords, int64_t n, int32_t resolution
                                       &a, &tab, &nothing);
     if (st != P3D_OK) return st;
     if (nothing) return ok();
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == P3D_BF16 && n > 0) {
-        int32_t kH, kW;
-        key_map(maps, n_maps, &kH, &kW);
-        OrderBufs ob;
-        const size_t sort_bytes = order_layout(n, batch, kH, kW, workspace, &ob);
-        const size_t need = sort_bytes + (((size_t)n * 4 + 255) & ~(size_t)255);
-        if (!workspace || workspace_bytes < need)
-            return fail(P3D_ERR_INVALID_ARG,
-                        "%s: workspace must be a device buffer of at least %zu bytes "
-                        "(p3d_proj_cond_workspace_size), got %zu bytes at %p",
-                        fn, need, workspace_bytes, workspace);
-        if (!aligned(workspace, 256))
-            return fail(P3D_ERR_UNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
-        int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + sort_bytes);
-        const OrderArgs oa{coords, n, resolution, (int32_t)points, batch};
-        hipError_t e = launch_order(oa, tab, ob, order, s);
-        if (e != hipSuccess) return hip_fail(fn, e);
-        a.order = order;
-    }
-    hipError_t e = launch_proj_cond(a, dtype, tab, s);
-    if (e != hipSuccess) return hip_fail(fn, e);
-    return ok();
+    return run_ordered(fn, a, tab, dtype, maps, n_maps, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream));
+}
+
+// The allocation-free variant of p3d_proj_cond_ws: the same launches, with
+// the sort's scratch in this file's `scratch` array (see its comment).
+p3d_status p3d_proj_cond_noalloc(const int32_t* coords, int64_t n, int32_t resolution,
+                                 p3d_points points, const p3d_camera* cams, int32_t batch,
+                                 p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                 const void* weight, int32_t out_dim, int32_t weight_in,
+                                 const void* bias, int64_t n_null, void* out, uint8_t* mask,
+                                 void* stream) {
+    const char* fn = "p3d_proj_cond_noalloc";
+    ProjCondArgs a;
+    CamTable tab;
+    bool nothing;
+    p3d_status st = prepare_proj_cond(fn, coords, n, resolution, points, cams, batch, dtype, maps,
+                                      n_maps, weight, out_dim, weight_in, bias, n_null, out, mask,
+                                      &a, &tab, &nothing);
+    if (st != P3D_OK) return st;
+    if (n > P3D_NOALLOC_MAX_TOKENS)
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: n must be <= %d (P3D_NOALLOC_MAX_TOKENS, the size of the library's "
+                    "scratch), got %lld; use p3d_proj_cond_ws with a workspace",
+                    fn, P3D_NOALLOC_MAX_TOKENS, (long long)n);
+    if (nothing) return ok();
+    void* base = nullptr;
+    st = scratch_address(fn, &base);
+    if (st != P3D_OK) return st;
+    return run_ordered(fn, a, tab, dtype, maps, n_maps, base, kScratchBytes,
+                       static_cast<hipStream_t>(stream));
 }
 
 p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolution,

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(p3d):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(p3d.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name

@@ -78,6 +78,8 @@ def _declare(lib):
     lib.orc_projection_stats.argtypes = [_i32p, _i64, _i32, _i32, _f32p, _f32p, _i32, _i32,
                                          ctypes.POINTER(_vp), _i32p, _i32p, _i32p, _i32,
                                          _f64p, _f64p]
+    lib.orc_stats_figures.restype = None
+    lib.orc_stats_figures.argtypes = [_f64p, _i32p, _i32, _f64p]
     lib.orc_proj_sample_rows.restype = None
     lib.orc_proj_sample_rows.argtypes = [_i32p, _i64, _i32, _i32, _f32p, _f32p, _i32, _i32,
                                          ctypes.POINTER(_vp), _i32p, _i32p, _i32p, _i32,
@@ -252,6 +254,19 @@ class Oracle:
                                       int(is_bf16), _ptr(out, _f64p), _ptr(S, _f64p))
         return dict(zip(STAT_FIELDS, out.tolist()))
 
+    def stats_figures(self, raw, channels):
+        """Coverage, per-map mean and population std, mean cosine from the
+        raw sums (a dict of STAT_FIELDS, or 8 numbers in that order): a dict
+        with None for a figure whose denominator is empty."""
+        r = np.array([raw[k] for k in STAT_FIELDS] if isinstance(raw, dict) else raw,
+                     np.float64)
+        ch = np.array(list(channels) + [0] * (2 - len(channels)), np.int32)
+        out = np.empty(6, np.float64)
+        self.lib.orc_stats_figures(_ptr(r, _f64p), _ptr(ch, _i32p), len(channels),
+                                   _ptr(out, _f64p))
+        names = ("coverage", "mean0", "std0", "mean1", "std1", "cosine")
+        return {k: (None if np.isnan(v) else float(v)) for k, v in zip(names, out)}
+
     def proj_sample_rows(self, coords, n, resolution, focal, dist, feat, rows,
                          points="cell_centres"):
         """The samples S of tokens `rows` as the whole path forms them before
@@ -350,21 +365,6 @@ class Oracle:
                                        _ptr(rows, _i64p), rows.size, _ptr(Y, _f64p),
                                        _ptr(mask, _u8p), _ptr(S, _f64p))
         return Y, mask
-
-
-def stats_summary(raw, channels):
-    """Derived figures from the raw sums: coverage, per-half mean and std
-    (population), mean cosine between the halves (None when not defined)."""
-    t = raw["tokens"]
-    out = {"coverage": raw["inside"] / t if t else None}
-    for h, c in enumerate(channels):
-        cnt = t * c
-        mean = raw["sum%d" % h] / cnt if cnt else None
-        out["mean%d" % h] = mean
-        out["std%d" % h] = (max(raw["sum_sq%d" % h] / cnt - mean * mean, 0.0) ** 0.5
-                            if cnt else None)
-    out["cosine"] = raw["cos_sum"] / raw["cos_count"] if raw["cos_count"] else None
-    return out
 
 
 _default = None

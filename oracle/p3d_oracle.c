@@ -529,6 +529,39 @@ void orc_projection_stats(const int32_t* coords, int64_t n, int32_t R, int32_t p
     }
 }
 
+/* -------------------------------------------------- diagnostic figures ---
+ * [PR38-diag]: the figures printed per stage, from the sums of
+ * orc_projection_stats (raw[8] in that layout), written out from their
+ * definitions over the N = tokens * C_h samples x of map h:
+ *   coverage  = inside / tokens
+ *   mean_h    = (1/N) sum x
+ *   std_h     = population standard deviation, sqrt((1/N) sum (x - mean)^2),
+ *               which the sums give as sqrt((sum x^2 - N mean^2) / N);
+ *               rounding can take the radicand a hair below 0 for a constant
+ *               map, where the deviation is 0
+ *   cosine    = cos_sum / cos_count (mean cosine over the counted tokens)
+ * out[6] = {coverage, mean_0, std_0, mean_1, std_1, cosine}; a figure with an
+ * empty denominator (no tokens, no map h, no counted token) is NaN. */
+void orc_stats_figures(const double* raw, const int32_t* channels, int32_t n_maps,
+                       double* out)
+{
+    const double tokens = raw[0];
+    out[0] = tokens > 0.0 ? raw[1] / tokens : NAN;
+    for (int32_t h = 0; h < 2; ++h) {
+        out[1 + 2 * h] = NAN;
+        out[2 + 2 * h] = NAN;
+        if (h >= n_maps) continue;
+        const double N = tokens * (double)channels[h];
+        if (!(N > 0.0)) continue;
+        const double mean = raw[2 + h] / N;
+        double var = (raw[4 + h] - N * mean * mean) / N;
+        if (var < 0.0) var = 0.0;
+        out[1 + 2 * h] = mean;
+        out[2 + 2 * h] = sqrt(var);
+    }
+    out[5] = raw[7] > 0.0 ? raw[6] / raw[7] : NAN;
+}
+
 /* ------------------------------------------------------ gather once ---
  * The samples S of tokens rows[k] (the whole path before proj_linear):
  * S_out [nrows, sum Cs] binary64, bf16-rounded values for bf16 maps. */

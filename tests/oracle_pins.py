@@ -614,6 +614,45 @@ def pin_stats_torch_numpy(o):
             assert abs(st["cos_sum"] - cos.sum()) <= 1e-5 * n, (st["cos_sum"], cos.sum())
 
 
+def pin_stats_figures_numpy(o):
+    """The printed figures from the raw sums (orc_stats_figures) against
+    numpy's own statistics of torch grid_sample samples: coverage =
+    mask.mean(), mean and population std (np.std, two-pass) of each map's
+    samples, mean cosine over the tokens where both samples are non-zero.
+    Maps with an offset (mean 0.3 or 2.5 against std 1) make a dropped
+    mean^2 term, a sample (N - 1) std or a wrong count show; a constant map
+    must give std exactly 0 (the radicand may round below 0)."""
+    rng = np.random.default_rng(41)
+    R, n = 12, 300
+    coords = np.concatenate([rng.integers(0, 2, (n, 1)), rng.integers(-4, R + 4, (n, 3))],
+                            1).astype(np.int32)
+    fo, do = o.cameras([45.0, 60.0], [1.2, 0.55])
+    for bf16 in (False, True):
+        m0 = (rng.standard_normal((2, 7, 9, 16)) + 0.3).astype(np.float32)
+        m1 = (rng.standard_normal((2, 20, 13, 16)) * 0.5 + 2.5).astype(np.float32)
+        feats = [o.f32_to_bf16(m0), o.f32_to_bf16(m1)] if bf16 else [m0, m1]
+        st = o.projection_stats(coords, n, R, fo, do, feats)
+        fig = o.stats_figures(st, [16, 16])
+        (S0, S1), mask = _torch_samples(o, feats, coords, n, R, fo, do, "cell_centres", bf16)
+        assert abs(fig["coverage"] - mask.mean()) < 1e-15
+        for h, S in enumerate((S0, S1)):
+            assert abs(fig["mean%d" % h] - S.mean()) <= 1e-6 * np.abs(S).mean(), (h, fig)
+            assert abs(fig["std%d" % h] - S.std()) <= 1e-5 * S.std(), (h, fig, S.std())
+        n0, n1 = np.linalg.norm(S0, axis=1), np.linalg.norm(S1, axis=1)
+        ok = (n0 > 0) & (n1 > 0)
+        cos = (S0 * S1).sum(1)[ok] / (n0[ok] * n1[ok])
+        assert abs(fig["cosine"] - cos.mean()) <= 1e-6, (fig["cosine"], cos.mean())
+        # one map: no second half, no cosine
+        fig1 = o.stats_figures(o.projection_stats(coords, n, R, fo, do, feats[:1]), [16])
+        assert fig1["mean1"] is None and fig1["std1"] is None and fig1["cosine"] is None
+        assert abs(fig1["std0"] - fig["std0"]) <= 1e-12 * fig["std0"]
+    c = np.full((1, 5, 6, 8), 0.1, np.float32)
+    f, d = o.camera(40.0, 1.5)
+    fig = o.stats_figures(o.projection_stats(coords[:40] * 0, 40, R, [f], [d], [c]), [8])
+    assert fig["std0"] == 0.0 and abs(fig["mean0"] - 0.1) < 1e-7
+    assert o.stats_figures([0.0] * 8, [8])["coverage"] is None
+
+
 def pin_stats_scaled_copies(o):
     """A map and a scaled copy of it on the same grid: the cosine is exactly
     +1 (or -1 for a negative scale) at every token, mean and std scale with

@@ -18,6 +18,12 @@ SRC = os.path.join(ROOT, "oracle", "p3d_oracle.c")
 
 # (id, text in the oracle source, replacement)
 MUTANTS = [
+    ("std_without_mean_square", "double var = (raw[4 + h] - N * mean * mean) / N;",
+     "double var = raw[4 + h] / N;"),
+    ("std_sample_not_population", "double var = (raw[4 + h] - N * mean * mean) / N;",
+     "double var = (raw[4 + h] - N * mean * mean) / (N - 1.0);"),
+    ("mean_over_tokens_not_samples", "const double mean = raw[2 + h] / N;",
+     "const double mean = raw[2 + h] / tokens;"),
     ("camera_looks_down_plus_z", "float depth = dist[b] - pz;", "float depth = dist[b] + pz;"),
     ("image_y_not_flipped", "float gy = -((f * py) / depth);", "float gy = ((f * py) / depth);"),
     ("x_y_swapped", "float gx = (f * px) / depth;", "float gx = (f * py) / depth;"),

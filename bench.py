@@ -2,32 +2,41 @@
 on one MI355X, with the roofline of its dominant kernel and the CPU oracle
 timed beside it.
 
-One step = one p3d_proj_cond call over the whole batch: projection of every
-token, bilinear gather, proj_linear on the matrix cores, mask, and the CFG
-null branch. The default workload is the largest one (a 1024^3 sparse shell
-of 100k tokens with a 100k-row null branch, bf16 map 1x512x512x2048,
-proj_linear 2048->1536); inputs are synthetic, seeded and resident in HBM
-before the timed region starts.
+One step = one pass of the whole path over the batch: the image-space token
+order (p3d_token_order), then the fused kernel through it
+(p3d_proj_cond_ordered) -- projection of every token, bilinear gather,
+proj_linear on the matrix cores, mask, and the CFG null branch. Together the
+two calls are p3d_proj_cond_ws; they are issued separately so that HIP events
+bracket the fused kernel alone. The default workload is the largest one (a
+1024^3 sparse shell of 100k tokens with a 100k-row null branch, bf16 map
+1x512x512x2048, proj_linear 2048->1536); inputs are synthetic, seeded and
+resident in HBM before the timed region starts.
 
 Prints ONE JSON line. Fields beyond the common ones:
-  roofline       dominant kernel (the fused gather+MFMA kernel, which a bf16
-                 step launches once, null rows included): algorithmic flops
-                 per launch / its mean duration (HIP events on the launch
-                 stream around the timed steps) against the bf16 dense MFMA
-                 peak; traffic = HBM bytes per launch from the committed
-                 rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled by a copy kernel
-                 of known size, or null if the kernel source changed since.
-  cpu_baseline   the CPU oracle on a bounded prefix of the same tokens.
-  gather         the standalone bilinear gather on the same points: algorithmic
-                 bytes / duration against peak HBM bandwidth.
-  null_fill      the null-branch fill alone: bytes written / duration.
-  extra          the adjacent parts, each on its own workload with its own
-                 roofline: cascade requantization (HBM), the fused kernel on
-                 grid-node points after requantization (MFMA), the fused
-                 kernel over two concatenated maps (MFMA), the projection
-                 diagnostics over those two maps (HBM gather + reduction),
-                 gathering those samples once into S (HBM) and the per-block
-                 proj_linear of 30 DiT blocks over S with residual add (MFMA).
+  roofline          dominant kernel (the fused gather+MFMA kernel, launched
+                    once per step, null rows included): algorithmic flops per
+                    launch / its mean duration (HIP events on the launch
+                    stream around each launch of the timed steps) against the
+                    bf16 dense MFMA peak; traffic = HBM bytes per launch from
+                    the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, scaled
+                    by a copy kernel of known size, or null if the sources
+                    changed since.
+  order_ms          the token order's share of the step (events likewise).
+  cpu_baseline      the CPU oracle on a bounded prefix of the same tokens, on
+                    every core of the affinity mask and on one thread.
+  gather            the standalone bilinear gather on the same points:
+                    algorithmic bytes / duration against peak HBM bandwidth
+                    and against the measured copy ceiling.
+  hbm_copy_ceiling  a streaming device copy: the achievable HBM rate.
+  null_fill         the null-branch fill alone: bytes written / duration.
+  extra             the adjacent parts, each with its own roofline: the fused
+                    call on every other workload (fp32 peak for fp32, bf16
+                    for bf16), the headline without the order, cascade
+                    requantization (HBM) and the fused kernel on grid nodes
+                    (MFMA), the two-map texture stage (fused kernel, the
+                    projection diagnostics and the gather-once samples, all
+                    through one shared order, plus the per-block proj_linear
+                    of 30 DiT blocks), and a plain GEMM reference.
 """
 import argparse
 import hashlib
@@ -47,12 +56,14 @@ DEFAULT_WORKLOAD = "shell1024_cfg_bf16_c2048_d1536"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-# source files each measured kernel is built from (its counters stay valid
-# while these are unchanged)
+# source files each measured kernel is built from, or that decide what it
+# reads (the token order); its counters stay valid while these are unchanged
 KERNEL_SOURCES = {
-    "proj_cond_bf16_kernel": ["proj_cond_bf16.hip", "bf16_tile.h", "p3d_internal.h"],
+    "proj_cond_bf16_kernel": ["proj_cond_bf16.hip", "bf16_tile.h", "p3d_internal.h",
+                              "order.hip"],
     "proj_cond_kernel": ["proj_cond.hip", "p3d_internal.h"],
-    "sample_kernel": ["sample.hip", "p3d_internal.h"],
+    "sample_kernel": ["sample.hip", "p3d_internal.h", "order.hip"],
+    "stats_kernel": ["stats.hip", "p3d_internal.h", "order.hip"],
 }
 
 
@@ -136,17 +147,23 @@ def time_events(fn, reps, stream, lead=None):
     return e0.elapsed_time(e1) / reps
 
 
-def cpu_baseline(inp, cams_o, target_s=12.0):
-    """The oracle, untuned, over a prefix of the same tokens until about
-    target_s seconds of CPU work; tokens/s."""
+def cpu_quota_cores():
+    """CPU share the cgroup grants (cpu.max quota / period), or None."""
+    try:
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()
+        return None if q == "max" else float(q) / float(per)
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_leg(o, inp, cams_o, threads, target_s):
+    """The oracle over a prefix of the tokens on `threads` threads until about
+    target_s seconds of CPU work: (tokens done, seconds, threads used)."""
     import numpy as np
-    import oracle
-    o = oracle.get()
-    want = min(16, len(os.sched_getaffinity(0)))
-    threads = o.set_threads(want)
+    used = o.set_threads(threads)
     w = inp["w"]
     fo, do = cams_o
-    done, t_total, chunk = 0, 0.0, 512
+    done, t_total, chunk = 0, 0.0, max(64, 32 * used)
     while t_total < target_s and done < inp["n"]:
         rows = np.arange(done, min(inp["n"], done + chunk))
         t0 = time.perf_counter()
@@ -154,21 +171,145 @@ def cpu_baseline(inp, cams_o, target_s=12.0):
                          inp["weight"], inp["bias"], inp["n_null"], rows)
         t_total += time.perf_counter() - t0
         done += rows.size
-        if t_total > 0:
-            chunk = int(max(256, min(8192, rows.size * (target_s - t_total) / max(t_total, 1e-3))))
-    return {"value": done / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d of %d tokens of the same workload (the full path per token: "
-                      "projection, gather, bf16 rounding, proj_linear in binary64), %.1f s, "
-                      "CPU %s" % (done, inp["n"], t_total, cpu_model())}
+        rate = rows.size / max(time.perf_counter() - t0, 1e-6)
+        chunk = int(max(64, min(16384, rate * max(target_s - t_total, 0.0) * 0.5)))
+    return done, t_total, used
 
 
-def run_extra(p3d, synth, stream, reps, lead_step):
-    """Adjacent parts on their own workloads: requantization of a res-512
-    shell onto the 64-node grid, the fused kernel on those grid nodes, the
-    fused kernel over the two-map texture-stage workload, its diagnostics,
-    the gather-once samples and the per-block linears; and, as a reference,
-    one block of the plain product through the tile and through a library
-    GEMM."""
+def cpu_baseline(inp, cams_o, target_s=10.0):
+    """The oracle, untuned, on a bounded prefix of the same tokens: one leg
+    on every core this process may run on, one on a single thread; tokens/s
+    (the rate over the prefix, not a full pass)."""
+    import oracle
+    o = oracle.get()
+    cores = len(os.sched_getaffinity(0))
+    many = min(cores, 256)          # a sanity bound on threads, not a tuning
+    d_all, t_all, used = cpu_leg(o, inp, cams_o, many, target_s)
+    d_one, t_one, _ = cpu_leg(o, inp, cams_o, 1, target_s)
+    quota = cpu_quota_cores()
+    what = ("the full path per token: projection, gather, bf16 rounding, proj_linear in "
+            "binary64 (rows of the oracle's proj_cond)")
+    return {"value": d_all / t_all, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "first %d of %d tokens of the same workload, %s, %.1f s on %d threads; "
+                      "CPU %s, %d cores in the affinity mask%s" % (
+                          d_all, inp["n"], what, t_all, used, cpu_model(), cores,
+                          "" if quota is None else ", cgroup CPU quota %.1f cores" % quota),
+            "single_thread": {"value": d_one / t_one, "unit": "tokens/s", "cores": 1,
+                              "sample": "first %d tokens, %.1f s on 1 thread" % (d_one, t_one)},
+            "affinity_cores": cores, "cpu_quota_cores": quota, "cpu_model": cpu_model()}
+
+
+def hbm_copy_ceiling(stream, reps, mib=2048):
+    """A streaming device copy (torch copy_ of mib MiB, read + write) as the
+    achievable HBM rate beside the datasheet peak: GB/s counted as bytes read
+    plus bytes written per launch over its mean duration."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    cp = lambda: b.copy_(a)
+    for _ in range(3):
+        cp()
+    ms = time_events(cp, reps, stream)
+    gbs = 2.0 * n * 4 / (ms * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return {"kernel": "torch copy_ (elementwise copy)", "bytes_per_launch": 2 * n * 4,
+            "mean_ms": ms, "achieved": gbs, "unit": "GB/s", "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
+def order_key(maps):
+    """(H, W) of the map with the most texels: the key map of the order."""
+    return max(((m.shape[1], m.shape[2]) for m in maps), key=lambda hw: hw[0] * hw[1])
+
+
+def make_order(p3d, coords, n, R, cams, maps, points="cell_centres"):
+    """Device order of the tokens and a closure that recomputes it."""
+    import torch
+    kH, kW = order_key(maps)
+    order = torch.empty((n,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((p3d.p3d_token_order_workspace_size(n, len(cams), kH, kW),),
+                     dtype=torch.uint8, device="cuda")
+    run = lambda: p3d.p3d_token_order(coords, n, R, cams, kH, kW, order, workspace=ws,
+                                      points=points)
+    run()
+    return order, run
+
+
+def config_line(p3d, synth, name, stream, reps):
+    """One workload's fused call, timed alone (HIP events), with its own
+    roofline: fp32 MFMA peak for fp32 workloads, bf16 for bf16 ones. bf16
+    workloads also report the ordered call (token order + fused kernel)."""
+    import numpy as np
+    import torch
+    w = synth.workload(name)
+    bf16 = w.dtype == "bf16"
+
+    def dev(a):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16).view(torch.bfloat16) if bf16 and a.dtype == np.uint16
+                else t).cuda()
+
+    coords_np = synth.coords(w)
+    coords = dev(coords_np)
+    feat = dev(synth.feature_map(w))
+    weight = dev(synth.weight(w))
+    bias = dev(synth.bias(w))
+    n, nn = w.n_tokens, w.n_null
+    cams = [p3d.p3d_make_camera(a, w.distance if w.distance is not None else
+                                p3d.p3d_distance_from_fov(a, w.width, 0)) for a in synth.fovs(w)]
+    camarr = p3d.make_cameras(cams)
+    out = torch.empty((n + nn, w.out_dim), dtype=feat.dtype, device="cuda")
+    mask = torch.empty((n,), dtype=torch.uint8, device="cuda")
+    fused = lambda: p3d.p3d_proj_cond(coords, n, w.resolution, camarr, feat, weight, out,
+                                      bias=bias, n_null=nn, mask=mask)
+    for _ in range(reps):
+        fused()
+    ms = time_events(fused, reps, stream)
+    flops = 2.0 * n * w.channels * w.out_dim
+    peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
+    line = {"workload": w.name, "dtype": w.dtype, "tokens": n, "null_rows": nn,
+            "map": "%dx%dx%dx%d" % tuple(feat.shape),
+            "proj_linear": "%d->%d%s" % (w.channels, w.out_dim, " +bias" if bias is not None
+                                         else ""),
+            "kernel": "proj_cond_bf16_kernel" if bf16 else "proj_cond_kernel",
+            "mean_ms": ms, "tokens_per_s": n / (ms * 1e-3), "bound": "mfma",
+            "flops_per_launch": flops, "achieved": flops / (ms * 1e-3) / 1e12, "peak": peak,
+            "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / peak}
+    if bf16 and coords is not None:
+        order, run_order = make_order(p3d, coords, n, w.resolution, camarr, [feat], w.points)
+        ordf = lambda: p3d.p3d_proj_cond(coords, n, w.resolution, camarr, feat, weight, out,
+                                         bias=bias, n_null=nn, mask=mask, order=order)
+        for _ in range(reps):
+            ordf()
+        oms = time_events(ordf, reps, stream)
+        sort_ms = time_events(run_order, reps, stream)
+        line["ordered"] = {"fused_ms": oms, "order_ms": sort_ms,
+                           "frac": flops / (oms * 1e-3) / 1e12 / peak,
+                           "tokens_per_s_incl_order": n / ((oms + sort_ms) * 1e-3)}
+    del coords, feat, weight, bias, out, mask
+    torch.cuda.empty_cache()
+    return line
+
+
+EXTRAS = ("configs", "unordered", "cascade", "two_maps", "gemm_reference")
+
+
+def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
+              headline_flops=None):
+    """Adjacent parts on their own workloads (the names in `which`):
+      configs        the fused call on every other workload, own roofline;
+      unordered      the headline's fused kernel without the token order;
+      cascade        requantization of a res-512 shell onto the 64-node grid,
+                     and the fused kernel on those grid nodes;
+      two_maps       the fused kernel over two concatenated maps, the
+                     projection diagnostics and the gather-once samples over
+                     those maps (all sharing one token order), the per-block
+                     linears of 30 DiT blocks;
+      gemm_reference one block of the plain product through the tile and
+                     through a library GEMM."""
     import numpy as np
     import torch
 
@@ -181,42 +322,63 @@ def run_extra(p3d, synth, stream, reps, lead_step):
             lead_step()
 
     out = {}
-    # ---- cascade: requantize, then grid nodes
-    w = synth.workload("cascade512_grid64_nodes_bf16_c2048_d1536")
-    src = dev(synth.coords(w))
-    n = src.shape[0]
-    q = torch.empty_like(src)
-    rq = lambda: p3d.p3d_requantize_coords(src, w.coords_resolution, w.resolution, q)
-    rq()
-    rq_ms = time_events(rq, reps, stream, lead)
-    rq_bytes = 32 * n
-    feat = dev(synth.feature_map(w), True)
-    weight = dev(synth.weight(w), True)
-    cams = [p3d.p3d_make_camera(a, p3d.p3d_distance_from_fov(a, w.width, 0))
-            for a in synth.fovs(w)]
-    camarr = p3d.make_cameras(cams)
-    y = torch.empty((n, w.out_dim), dtype=torch.bfloat16, device="cuda")
-    fused = lambda: p3d.p3d_proj_cond(q, n, w.resolution, camarr, feat, weight, y,
-                                      points="grid_nodes")
-    for _ in range(reps):
-        fused()
-    nodes_ms = time_events(fused, reps, stream)
-    flops = 2.0 * n * w.k_total * w.out_dim
-    out["requantize"] = {
-        "workload": w.name, "kernel": "requant_kernel", "tokens": n, "mean_ms": rq_ms,
-        "bound": "hbm", "bytes_per_launch": rq_bytes,
-        "achieved": rq_bytes / (rq_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": rq_bytes / (rq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "note": "100k tokens = 3.2 MB: launch-latency bound, far from the HBM roofline"}
-    out["grid_nodes"] = {
-        "workload": w.name, "kernel": bf16_kernel_name(False, n, w.out_dim), "tokens": n,
-        "mean_ms": nodes_ms, "bound": "mfma", "flops_per_launch": flops,
-        "achieved": flops / (nodes_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-        "unit": "TFLOP/s", "frac": flops / (nodes_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        "cascade_tokens_per_s": n / ((rq_ms + nodes_ms) * 1e-3)}
-    del feat, weight, y, q, src
-    torch.cuda.empty_cache()
-    # ---- two maps
+    if "unordered" in which and unordered_step is not None:
+        for _ in range(reps):
+            unordered_step()
+        ums = time_events(unordered_step, reps, stream)
+        out["unordered"] = {"kernel": "proj_cond_bf16_kernel", "mean_ms": ums,
+                            "frac": headline_flops / (ums * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                            "note": "the headline's fused call without the token order "
+                                    "(p3d_proj_cond): tokens in the caller's (x, y, z) order"}
+    if "configs" in which:
+        out["configs"] = [config_line(p3d, synth, w.name, stream, reps)
+                          for w in synth.WORKLOADS if w.name != DEFAULT_WORKLOAD]
+    if "cascade" in which:
+        w = synth.workload("cascade512_grid64_nodes_bf16_c2048_d1536")
+        src = dev(synth.coords(w))
+        n = src.shape[0]
+        q = torch.empty_like(src)
+        rq = lambda: p3d.p3d_requantize_coords(src, w.coords_resolution, w.resolution, q)
+        rq()
+        rq_ms = time_events(rq, reps, stream, lead)
+        rq_bytes = 32 * n
+        feat = dev(synth.feature_map(w), True)
+        weight = dev(synth.weight(w), True)
+        cams = [p3d.p3d_make_camera(a, p3d.p3d_distance_from_fov(a, w.width, 0))
+                for a in synth.fovs(w)]
+        camarr = p3d.make_cameras(cams)
+        y = torch.empty((n, w.out_dim), dtype=torch.bfloat16, device="cuda")
+        fused = lambda: p3d.p3d_proj_cond(q, n, w.resolution, camarr, feat, weight, y,
+                                          points="grid_nodes")
+        for _ in range(reps):
+            fused()
+        nodes_ms = time_events(fused, reps, stream)
+        flops = 2.0 * n * w.k_total * w.out_dim
+        out["requantize"] = {
+            "workload": w.name, "kernel": "requant_kernel", "tokens": n, "mean_ms": rq_ms,
+            "bound": "hbm", "bytes_per_launch": rq_bytes,
+            "achieved": rq_bytes / (rq_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": rq_bytes / (rq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "note": "100k tokens = 3.2 MB: launch-latency bound, far from the HBM roofline"}
+        out["grid_nodes"] = {
+            "workload": w.name, "kernel": bf16_kernel_name(False, n, w.out_dim), "tokens": n,
+            "mean_ms": nodes_ms, "bound": "mfma", "flops_per_launch": flops,
+            "achieved": flops / (nodes_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": flops / (nodes_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "cascade_tokens_per_s": n / ((rq_ms + nodes_ms) * 1e-3)}
+        del feat, weight, y, q, src
+        torch.cuda.empty_cache()
+    if "two_maps" in which or "gemm_reference" in which:
+        out.update(run_two_maps(p3d, synth, stream, reps, which, dev))
+    return out
+
+
+def run_two_maps(p3d, synth, stream, reps, which, dev):
+    """The texture stage's two-map workload: one token order per stage,
+    shared by the fused call, the diagnostics and the gather-once samples."""
+    import numpy as np
+    import torch
+    out = {}
     w = synth.workload("shell1024_cfg_twomap_bf16_c1024x2_d1536")
     coords = dev(synth.coords(w))
     n, nn = w.n_tokens, w.n_null
@@ -225,29 +387,10 @@ def run_extra(p3d, synth, stream, reps, lead_step):
     cams = [p3d.p3d_make_camera(a, p3d.p3d_distance_from_fov(a, w.width, 0))
             for a in synth.fovs(w)]
     camarr = p3d.make_cameras(cams)
-    y = torch.empty((n + nn, w.out_dim), dtype=torch.bfloat16, device="cuda")
-    two = lambda: p3d.p3d_proj_cond(coords, n, w.resolution, camarr, maps, weight, y,
-                                    n_null=nn)
-    for _ in range(reps):
-        two()
-    two_ms = time_events(two, reps, stream)
-    flops = 2.0 * n * w.k_total * w.out_dim
-    out["two_maps"] = {
-        "workload": w.name, "kernel": bf16_kernel_name(True, n, w.out_dim), "tokens": n,
-        "null_rows": nn, "maps": ["%dx%dx%dx%d" % tuple(m.shape) for m in maps],
-        "mean_ms": two_ms, "tokens_per_s": n / (two_ms * 1e-3), "bound": "mfma",
-        "flops_per_launch": flops, "achieved": flops / (two_ms * 1e-3) / 1e12,
-        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": flops / (two_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
-    # ---- diagnostics over the same two maps: coverage, per-map mean/std,
-    # cosine between the maps' samples
-    stats = torch.empty(8, dtype=torch.float64, device="cuda")
-    diag = lambda: p3d.p3d_projection_stats(coords, n, w.resolution, camarr, maps, stats)
-    for _ in range(reps):
-        diag()
-    diag_ms = time_events(diag, reps, stream)
-    raw = dict(zip(p3d.STAT_FIELDS, stats.cpu().numpy().tolist()))
-    # algorithmic bytes: coords + each map's unique corner rows + the sums
+    K = sum(m.shape[3] for m in maps)
+    order, run_order = make_order(p3d, coords, n, w.resolution, camarr, maps)
+    order_ms = time_events(run_order, reps, stream)
+    # algorithmic bytes: coords + each map's unique corner rows
     bidx = synth.coords(w)[:, 0].copy()
     uniq = 0
     for m in maps:
@@ -256,68 +399,124 @@ def run_extra(p3d, synth, stream, reps, lead_step):
                                pixel=pix)
         uniq += unique_corner_rows(pix.cpu().numpy(), bidx, m.shape[1], m.shape[2]) * \
             m.shape[3] * 2
-    dbytes = 16 * n + uniq + 64
-    out["diagnostics"] = {
-        "workload": w.name, "kernel": "stats_kernel<true>", "tokens": n, "mean_ms": diag_ms,
-        "bound": "hbm", "bytes_per_launch": dbytes,
-        "achieved": dbytes / (diag_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": dbytes / (diag_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "figures": p3d.stats_summary(raw, [m.shape[3] for m in maps])}
-    # ---- gather once per stage, then every block's proj_linear per step
-    K = sum(m.shape[3] for m in maps)
-    S = torch.empty((n, K), dtype=torch.bfloat16, device="cuda")
-    gat = lambda: p3d.p3d_proj_sample(coords, n, w.resolution, camarr, maps, S)
-    for _ in range(reps):
-        gat()
-    gat_ms = time_events(gat, reps, stream)
-    gbytes = 16 * n + uniq + n * K * 2
-    out["gather_once"] = {
-        "workload": w.name, "kernel": "sample_kernel<true, true, true> (one launch per map)",
-        "tokens": n, "mean_ms": gat_ms, "bound": "hbm", "bytes_per_launch": gbytes,
-        "achieved": gbytes / (gat_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": gbytes / (gat_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    G = 30
-    rng = np.random.default_rng(801)
-    Wg = [torch.from_numpy(synth.bf16_bits((rng.standard_normal((w.out_dim, K)) * 0.02).astype(
-        np.float32))).view(torch.int16).view(torch.bfloat16).cuda() for _ in range(G)]
-    outs = [torch.zeros((n, w.out_dim), dtype=torch.bfloat16, device="cuda") for _ in range(G)]
-    grp = lambda: p3d.p3d_proj_linear_grouped(S, Wg, outs, accumulate=True)
-    for _ in range(max(3, reps // 4)):
-        grp()
-    grp_ms = time_events(grp, max(5, reps // 4), stream)
-    gflops = 2.0 * n * K * w.out_dim * G
-    out["grouped"] = {
-        "workload": w.name + " x 30 blocks", "kernel": "grouped_kernel<true>", "tokens": n,
-        "blocks": G, "mean_ms": grp_ms, "bound": "mfma", "flops_per_launch": gflops,
-        "achieved": gflops / (grp_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-        "unit": "TFLOP/s", "frac": gflops / (grp_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        "note": "residual add: every block's output is read and rewritten (S 2048 -> 1536)"}
-    # ---- the same product, one block without the residual, through the tile
-    # and through a library GEMM (torch.matmul, ROCm's BLAS): a reference for
-    # what a plain bf16 GEMM of this shape reaches on this device
-    y1 = torch.empty((n, w.out_dim), dtype=torch.bfloat16, device="cuda")
-    wt = Wg[0].t().contiguous()
-    one = lambda: p3d.p3d_proj_linear_grouped(S, Wg[:1], [y1])
-    lib_mm = lambda: torch.matmul(S, wt, out=y1)
-    for f in (one, lib_mm):
-        for _ in range(3):
-            f()
-    # alternating blocks, medians: the two are compared under the same clocks
-    t_one, t_lib = [], []
-    for _ in range(5):
-        t_one.append(time_events(one, reps, stream))
-        t_lib.append(time_events(lib_mm, reps, stream))
-    one_ms, lib_ms = float(np.median(t_one)), float(np.median(t_lib))
-    f1 = 2.0 * n * K * w.out_dim
-    out["gemm_reference"] = {
-        "shape": "[%d, %d] x [%d, %d] bf16" % (n, K, K, w.out_dim),
-        "grouped_kernel_one_block_ms": one_ms,
-        "grouped_kernel_frac": f1 / (one_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        "library_gemm": "torch.matmul (ROCm BLAS)", "library_gemm_ms": lib_ms,
-        "library_gemm_frac": f1 / (lib_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
-    del maps, weight, y, coords, S, Wg, outs, y1, wt
+    if "two_maps" in which:
+        y = torch.empty((n + nn, w.out_dim), dtype=torch.bfloat16, device="cuda")
+        flops = 2.0 * n * w.k_total * w.out_dim
+        res = {}
+        for key, o in (("plain", None), ("ordered", order)):
+            f = lambda: p3d.p3d_proj_cond(coords, n, w.resolution, camarr, maps, weight, y,
+                                          n_null=nn, order=o)
+            for _ in range(reps):
+                f()
+            res[key] = time_events(f, reps, stream)
+        out["two_maps"] = {
+            "workload": w.name, "kernel": bf16_kernel_name(True, n, w.out_dim), "tokens": n,
+            "null_rows": nn, "maps": ["%dx%dx%dx%d" % tuple(m.shape) for m in maps],
+            "mean_ms": res["ordered"], "order_ms": order_ms, "unordered_ms": res["plain"],
+            "tokens_per_s": n / ((res["ordered"] + order_ms) * 1e-3), "bound": "mfma",
+            "flops_per_launch": flops, "achieved": flops / (res["ordered"] * 1e-3) / 1e12,
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": flops / (res["ordered"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "unordered_frac": flops / (res["plain"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        del y
+        # ---- diagnostics over the same two maps: coverage, per-map mean/std,
+        # cosine between the maps' samples
+        stats = torch.empty(8, dtype=torch.float64, device="cuda")
+        res = {}
+        for key, o in (("plain", None), ("ordered", order)):
+            f = lambda: p3d.p3d_projection_stats(coords, n, w.resolution, camarr, maps, stats,
+                                                 order=o)
+            for _ in range(reps):
+                f()
+            res[key] = time_events(f, reps, stream)
+        dbytes = 16 * n + uniq + 64
+        out["diagnostics"] = hbm_part(
+            w.name, "stats_kernel<true>", n, res, order_ms, dbytes,
+            figures=p3d.p3d_stats_figures(stats, [m.shape[3] for m in maps]),
+            traffic=recorded_traffic("stats_kernel", w.name))
+        # ---- gather once per stage
+        S = torch.empty((n, K), dtype=torch.bfloat16, device="cuda")
+        res = {}
+        for key, o in (("plain", None), ("ordered", order)):
+            f = lambda: p3d.p3d_proj_sample(coords, n, w.resolution, camarr, maps, S, order=o)
+            for _ in range(reps):
+                f()
+            res[key] = time_events(f, reps, stream)
+        gbytes = 16 * n + uniq + n * K * 2
+        out["gather_once"] = hbm_part(
+            w.name, "sample_kernel<true, true, true> (one launch per map)", n, res, order_ms,
+            gbytes, traffic=recorded_traffic("sample_kernel", w.name))
+        # ---- every block's proj_linear over the gathered samples
+        G = 30
+        rng = np.random.default_rng(801)
+        Wg = [torch.from_numpy(synth.bf16_bits((rng.standard_normal((w.out_dim, K)) * 0.02)
+                                               .astype(np.float32))).view(torch.int16)
+              .view(torch.bfloat16).cuda() for _ in range(G)]
+        outs = [torch.zeros((n, w.out_dim), dtype=torch.bfloat16, device="cuda")
+                for _ in range(G)]
+        grp = lambda: p3d.p3d_proj_linear_grouped(S, Wg, outs, accumulate=True)
+        for _ in range(max(3, reps // 4)):
+            grp()
+        grp_ms = time_events(grp, max(5, reps // 4), stream)
+        gflops = 2.0 * n * K * w.out_dim * G
+        out["grouped"] = {
+            "workload": w.name + " x 30 blocks", "kernel": "grouped_kernel<true>", "tokens": n,
+            "blocks": G, "mean_ms": grp_ms, "bound": "mfma", "flops_per_launch": gflops,
+            "achieved": gflops / (grp_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": gflops / (grp_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "note": "residual add: every block's output is read and rewritten (S 2048 -> 1536)"}
+        del Wg, outs
+    else:
+        S = torch.empty((n, K), dtype=torch.bfloat16, device="cuda")
+        p3d.p3d_proj_sample(coords, n, w.resolution, camarr, maps, S, order=order)
+    if "gemm_reference" in which:
+        # the same product, one block without the residual, through the tile
+        # and through a library GEMM (torch.matmul, ROCm's BLAS): a reference
+        # for what a plain bf16 GEMM of this shape reaches on this device
+        rng = np.random.default_rng(802)
+        W1 = torch.from_numpy(synth.bf16_bits((rng.standard_normal((w.out_dim, K)) * 0.02)
+                                              .astype(np.float32))).view(torch.int16) \
+            .view(torch.bfloat16).cuda()
+        y1 = torch.empty((n, w.out_dim), dtype=torch.bfloat16, device="cuda")
+        wt = W1.t().contiguous()
+        one = lambda: p3d.p3d_proj_linear_grouped(S, [W1], [y1])
+        lib_mm = lambda: torch.matmul(S, wt, out=y1)
+        for f in (one, lib_mm):
+            for _ in range(3):
+                f()
+        # alternating blocks, medians: the two are compared under the same clocks
+        t_one, t_lib = [], []
+        for _ in range(5):
+            t_one.append(time_events(one, reps, stream))
+            t_lib.append(time_events(lib_mm, reps, stream))
+        one_ms, lib_ms = float(np.median(t_one)), float(np.median(t_lib))
+        f1 = 2.0 * n * K * w.out_dim
+        out["gemm_reference"] = {
+            "shape": "[%d, %d] x [%d, %d] bf16" % (n, K, K, w.out_dim),
+            "grouped_kernel_one_block_ms": one_ms,
+            "grouped_kernel_frac": f1 / (one_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "library_gemm": "torch.matmul (ROCm BLAS)", "library_gemm_ms": lib_ms,
+            "library_gemm_frac": f1 / (lib_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+        del W1, y1, wt
+    del maps, weight, coords, S, order
     torch.cuda.empty_cache()
     return out
+
+
+def hbm_part(workload, kernel, n, res, order_ms, nbytes, **more):
+    """An HBM-bound part timed with and without the token order: frac is the
+    ordered kernel's; the order itself is reported beside it (one per stage,
+    shared with the fused call)."""
+    ms = res["ordered"]
+    d = {"workload": workload, "kernel": kernel, "tokens": n, "mean_ms": ms, "bound": "hbm",
+         "bytes_per_launch": nbytes, "achieved": nbytes / (ms * 1e-3) / 1e9,
+         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+         "order_ms": order_ms,
+         "frac_incl_order": nbytes / ((ms + order_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+         "unordered_ms": res["plain"],
+         "unordered_frac": nbytes / (res["plain"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    d.update(more)
+    return d
 
 
 def main():
@@ -330,6 +529,10 @@ def main():
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the adjacent-part measurements")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma-separated adjacent parts to measure (of %s)" % ", ".join(EXTRAS))
+    ap.add_argument("--extras-only", action="store_true",
+                    help="measure only the adjacent parts named by --extras (profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per launch (counter scale)")
     args = ap.parse_args()
@@ -339,6 +542,10 @@ def main():
               "collective, and only the one-GPU share is measured. Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    which = set(x for x in args.extras.split(",") if x)
+    unknown = which - set(EXTRAS)
+    if unknown:
+        ap.error("unknown extras: %s" % ", ".join(sorted(unknown)))
 
     import numpy as np
     import torch
@@ -348,6 +555,7 @@ def main():
 
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    reps = max(args.steps, 20)
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -358,6 +566,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
                           "launches": args.warmup + args.steps}))
+        return
+
+    if args.extras_only:
+        print(json.dumps({"extra": run_extra(p3d, synth, stream, reps, lambda: None, which)}),
+              flush=True)
         return
 
     w = synth.workload(args.workload)
@@ -392,9 +605,25 @@ def main():
     dt = torch.bfloat16 if bf16 else torch.float32
     out = torch.empty((n + n_null, w.out_dim), dtype=dt, device="cuda")
     mask = torch.empty((n,), dtype=torch.uint8, device="cuda")
+    # bf16 sparse workloads take the tokens in image-space order: the step
+    # computes the order (p3d_token_order) and runs the fused kernel through
+    # it (p3d_proj_cond_ordered), which is what p3d_proj_cond_ws does in one
+    # call; split here so that events bracket the fused kernel alone
+    ordered = bf16 and coords_d is not None
+    if ordered:
+        order, run_order = make_order(p3d, coords_d, n, w.resolution, camarr, [feat], w.points)
     torch.cuda.synchronize()
 
+    def fused():
+        p3d.p3d_proj_cond(coords_d, n, w.resolution, camarr, feat, weight, out, bias=bias,
+                          n_null=n_null, mask=mask, order=order if ordered else None)
+
     def step():
+        if ordered:
+            run_order()
+        fused()
+
+    def unordered_step():
         p3d.p3d_proj_cond(coords_d, n, w.resolution, camarr, feat, weight, out, bias=bias,
                           n_null=n_null, mask=mask)
 
@@ -411,7 +640,6 @@ def main():
     def gather_only():
         p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx)
 
-    reps = max(args.steps, 20)
     for _ in range(reps):
         gather_only()
     gather_ms = time_events(gather_only, reps, stream)
@@ -428,6 +656,7 @@ def main():
             step()
 
     null_ms = time_events(null_only, reps, stream, lead) if n_null else 0.0
+    copy = hbm_copy_ceiling(stream, reps)
     torch.cuda.synchronize()
 
     # ---- the timed steps. An idle GPU takes tens of milliseconds of work to
@@ -441,19 +670,23 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # events on the launch stream around each launch: [start, after order,
+    # after the fused kernel] per step
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        if ordered:
+            run_order()
+        ev[k][1].record(stream)
+        fused()
+        ev[k][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    # the step is one launch of the fused kernel (bf16), so the events around
-    # the timed steps give its mean launch duration
-    fused_ms = e0.elapsed_time(e1) / args.steps
+    fused_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    order_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps if ordered else 0.0
+    gpu_step_ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
 
     U = unique_corner_rows(pixel.cpu().numpy(), bidx_np, w.height, w.width)
     s = 2 if bf16 else 4
@@ -467,6 +700,7 @@ def main():
     achieved = flops / (fused_ms * 1e-3) / 1e12
     kname = "proj_cond_bf16_kernel" if bf16 else "proj_cond_kernel"
     traffic = recorded_traffic(kname, w.name)
+    gather_gbs = gather_bytes / (gather_ms * 1e-3) / 1e9
 
     line = {
         "metric": "projected tokens/sec (project+sample+proj_linear); HBM GB/s & MFMA % of peak",
@@ -485,27 +719,34 @@ def main():
                    "resolution": w.resolution, "batch": w.batch,
                    "map": "%dx%dx%dx%d %s NHWC" % (w.batch, w.height, w.width, C, w.dtype),
                    "proj_linear": "%d->%d%s" % (C, D, " +bias" if bias is not None else ""),
-                   "unique_corner_rows": U},
+                   "unique_corner_rows": U,
+                   "step": ("p3d_token_order + p3d_proj_cond_ordered (= p3d_proj_cond_ws)"
+                            if ordered else "p3d_proj_cond")},
         "rows_per_sec_incl_null": (n + n_null) / (ms_per_step * 1e-3),
+        "gpu_ms_per_step": gpu_step_ms,
+        "order_ms": order_ms,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": kname, "mean_ms": fused_ms,
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": fused_bytes},
-        "gather": {"bound": "hbm", "achieved": gather_bytes / (gather_ms * 1e-3) / 1e9,
+        "gather": {"bound": "hbm", "achieved": gather_gbs,
                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                   "frac": gather_bytes / (gather_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "frac": gather_gbs / HBM_PEAK_GBS,
+                   "frac_of_copy_ceiling": gather_gbs / copy["achieved"],
                    "kernel": "sample_kernel", "mean_ms": gather_ms,
                    "traffic": recorded_traffic("sample_kernel", w.name),
                    "algorithmic_bytes_per_launch": gather_bytes},
+        "hbm_copy_ceiling": copy,
         "null_fill": {"bound": "hbm", "mean_ms": null_ms,
                       "achieved": null_bytes / (null_ms * 1e-3) / 1e9 if null_ms else None,
                       "unit": "GB/s", "bytes_per_launch": null_bytes},
         "input_generation_s": t_gen,
-        "source_digest": {k: kernel_source_digest(k) for k in (kname, "sample_kernel")},
+        "source_digest": {k: kernel_source_digest(k) for k in KERNEL_SOURCES},
     }
     if not args.no_extra:
-        line["extra"] = run_extra(p3d, synth, stream, max(args.steps, 20), step)
+        line["extra"] = run_extra(p3d, synth, stream, reps, step, which,
+                                  unordered_step if ordered else None, flops)
     if not args.no_cpu_baseline:
         import oracle
         o = oracle.get()

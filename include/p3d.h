@@ -82,7 +82,11 @@ typedef enum p3d_dtype {
 /* A per-image pinhole camera on the +Z axis looking down -Z at the origin.
  * focal = 1 / tan(fov / 2) in normalised image units (full-angle FOV);
  * distance = camera-to-origin distance in world units (the unit cube spans
- * [-1/2, 1/2]^3). Both finite and > 0. */
+ * [-1/2, 1/2]^3). Both finite and > 0. A distance of 0.5 or less is
+ * accepted and defined: cells at or behind the camera plane (depth <= 0) get
+ * mask 0; at depth exactly 0, gx and gy are +-inf (NaN for a cell on the
+ * axis), and the sampling index clamp maps them to the edge texel (NaN to
+ * texel 0), the same as for any other out-of-range coordinate. */
 typedef struct p3d_camera {
     float focal;
     float distance;
@@ -404,6 +408,73 @@ p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolu
                                 p3d_proj_stats* stats, void* stream);
 
 /* ------------------------------------------------------------------------
+ * p3d_token_order -- an image-space order of the tokens, to be passed to the
+ * *_ordered calls (and computed inside p3d_proj_cond_ws). The sampling calls
+ * take tokens in runs (tiles, windows); tokens whose bilinear corners share
+ * map rows should share a run, so each row is fetched once instead of once
+ * per token (pixel-aligned head commit of pixal3d_mrp_mlx: every token reads
+ * the four texels around its projection).
+ *
+ * order[i] receives the token at sorted position i, a permutation of
+ * [0, n): tokens sorted by batch item, then by the Morton index of the 16 x
+ * 16-texel block (coarser for very large maps or batches, so that there are
+ * at most 16384 blocks) that contains their top-left corner texel on a
+ * key_height x key_width map -- the largest map the tokens will sample. The
+ * projection is p3d_project_points_ex's. The order among tokens of one block
+ * is unspecified and may change from call to call; results of the *_ordered
+ * calls do not depend on it beyond the order of their floating-point sums.
+ *
+ *   coords .. batch        as p3d_project_points_ex
+ *   key_height, key_width  the key map's size, >= 1
+ *   order                  DEVICE int32 [n], 4-byte aligned, written
+ *   workspace              DEVICE scratch of at least
+ *                          p3d_token_order_workspace_size(n, batch,
+ *                          key_height, key_width) bytes, 256-byte aligned,
+ *                          caller-owned, contents undefined on return;
+ *                          calls sharing one workspace must not overlap
+ * --------------------------------------------------------------------- */
+size_t p3d_token_order_workspace_size(int64_t n, int32_t batch, int32_t key_height,
+                                      int32_t key_width);
+                                      /* 0 on invalid sizes (p3d_last_error says why) */
+p3d_status p3d_token_order(const int32_t* coords, int64_t n, int32_t resolution,
+                           p3d_points points, const p3d_camera* cams, int32_t batch,
+                           int32_t key_height, int32_t key_width, int32_t* order,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* p3d_projection_stats_ordered -- p3d_projection_stats processing the tokens
+ * in the order `order` (DEVICE int32 [n] from p3d_token_order, or any
+ * permutation of [0, n); NULL = the natural order); the sums change only in
+ * the order of their additions. An entry outside [0, n) breaks the
+ * contract: it is clamped into [0, n), so nothing outside the arrays is
+ * touched, and the sums are unspecified. */
+p3d_status p3d_projection_stats_ordered(const int32_t* coords, int64_t n, int32_t resolution,
+                                        p3d_points points, const p3d_camera* cams, int32_t batch,
+                                        p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                        const int32_t* order, p3d_proj_stats* stats,
+                                        void* stream);
+
+/* p3d_stats_figures -- the figures the commit adding the per-stage projection
+ * statistics prints, from the sums of p3d_projection_stats (a HOST copy of
+ * the p3d_proj_stats, read after the stream has finished it):
+ *   coverage = inside / tokens
+ *   mean[h]  = sum[h] / (tokens * channels[h])
+ *   std[h]   = sqrt(max(sum_sq[h] / (tokens * channels[h]) - mean[h]^2, 0)),
+ *              the population standard deviation of map h's samples
+ *   cosine   = cos_sum / cos_count
+ * A figure whose denominator is 0 (no tokens, h >= n_maps, no token with
+ * both samples non-zero) is NaN. Host-only, binary64.
+ *   channels  host array [n_maps] of each map's channel count, >= 1 */
+typedef struct p3d_stats_fig {
+    double coverage;
+    double mean[2];
+    double std[2];
+    double cosine;
+} p3d_stats_fig;
+
+p3d_status p3d_stats_figures(const p3d_proj_stats* stats, const int32_t* channels,
+                             int32_t n_maps, p3d_stats_fig* out);
+
+/* ------------------------------------------------------------------------
  * Gather once per stage, apply every block's proj_linear every step (PR #38,
  * proj-mode commit): the samples do not change within a stage, so they are
  * gathered once (p3d_proj_sample) and each denoising step runs all blocks'
@@ -421,6 +492,32 @@ p3d_status p3d_proj_sample(const int32_t* coords, int64_t n, int32_t resolution,
                            p3d_points points, const p3d_camera* cams, int32_t batch,
                            p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
                            void* S, uint8_t* mask, void* stream);
+
+/* p3d_proj_sample_ordered -- p3d_proj_sample processing the tokens in the
+ * order `order` (as p3d_projection_stats_ordered); row t of S and mask byte
+ * t still belong to token t, so the call writes the same bytes as
+ * p3d_proj_sample. */
+p3d_status p3d_proj_sample_ordered(const int32_t* coords, int64_t n, int32_t resolution,
+                                   p3d_points points, const p3d_camera* cams, int32_t batch,
+                                   p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                   const int32_t* order, void* S, uint8_t* mask, void* stream);
+
+/* p3d_proj_cond_ordered -- p3d_proj_cond_ex over the tokens in the order
+ * `order` (DEVICE int32 [n], 4-byte aligned: p3d_token_order's output for
+ * the map with the most texels, or any permutation of [0, n); required when
+ * n > 0). Row t of `out` and mask byte t still belong to token t, so `out`
+ * and `mask` are identical bit for bit to p3d_proj_cond_ex's. It is
+ * p3d_proj_cond_ws split in two, for callers that compute one order per
+ * stage and share it with p3d_projection_stats_ordered and
+ * p3d_proj_sample_ordered. F32 calls ignore the order. An entry outside
+ * [0, n) breaks the contract: it is clamped into [0, n), so nothing outside
+ * the arrays is touched, and which rows are written is unspecified. */
+p3d_status p3d_proj_cond_ordered(const int32_t* coords, int64_t n, int32_t resolution,
+                                 p3d_points points, const p3d_camera* cams, int32_t batch,
+                                 p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                 const void* weight, int32_t out_dim, int32_t weight_in,
+                                 const void* bias, int64_t n_null, void* out, uint8_t* mask,
+                                 const int32_t* order, void* stream);
 
 /* p3d_proj_linear_grouped -- for each block g in [0, groups):
  *   accumulate == 0:  outs[g][t] = W_g S[t] + b_g

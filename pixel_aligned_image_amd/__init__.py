@@ -19,9 +19,10 @@ import torch
 __all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_version",
            "p3d_status_string", "p3d_last_error", "p3d_distance_from_fov", "p3d_make_camera",
            "p3d_project_points", "p3d_bilinear_sample", "p3d_proj_cond",
-           "p3d_requantize_coords", "p3d_projection_stats", "stats_summary",
+           "p3d_requantize_coords", "p3d_projection_stats", "p3d_stats_figures",
            "p3d_proj_sample", "p3d_proj_linear_grouped", "P3D_MAX_GROUPS",
            "p3d_proj_cond_workspace_size", "proj_cond_workspace", "P3D_NOALLOC_MAX_TOKENS",
+           "p3d_token_order", "p3d_token_order_workspace_size",
            "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libp3d.so")
@@ -103,6 +104,24 @@ def _load():
     L.p3d_proj_cond_ws.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
                                    ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp, vp,
                                    vp, ctypes.c_size_t, vp]
+    L.p3d_proj_cond_ordered.restype = ctypes.c_int
+    L.p3d_proj_cond_ordered.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
+                                        ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp,
+                                        vp, vp, vp]
+    L.p3d_token_order_workspace_size.restype = ctypes.c_size_t
+    L.p3d_token_order_workspace_size.argtypes = [i64, i32, i32, i32]
+    L.p3d_token_order.restype = ctypes.c_int
+    L.p3d_token_order.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, i32, i32, vp, vp,
+                                  ctypes.c_size_t, vp]
+    L.p3d_projection_stats_ordered.restype = ctypes.c_int
+    L.p3d_projection_stats_ordered.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32,
+                                               ctypes.c_int, ctypes.POINTER(p3d_map), i32, vp,
+                                               vp, vp]
+    L.p3d_proj_sample_ordered.restype = ctypes.c_int
+    L.p3d_proj_sample_ordered.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
+                                          ctypes.POINTER(p3d_map), i32, vp, vp, vp, vp]
+    L.p3d_stats_figures.restype = ctypes.c_int
+    L.p3d_stats_figures.argtypes = [vp, vp, i32, vp]
     L.p3d_proj_cond_noalloc.restype = ctypes.c_int
     L.p3d_proj_cond_noalloc.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
                                         ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp,
@@ -268,11 +287,13 @@ def proj_cond_workspace(n, batch, feat, device="cuda"):
 
 
 def p3d_proj_cond(coords, n, resolution, cams, feat, weight, out, bias=None, n_null=0,
-                  mask=None, stream=None, points="cell_centres", workspace=None, noalloc=False):
+                  mask=None, stream=None, points="cell_centres", workspace=None, noalloc=False,
+                  order=None):
     """Enqueue p3d_proj_cond (one map, cell centres), p3d_proj_cond_ex, or
     p3d_proj_cond_ws when `workspace` (a uint8 device tensor, e.g. from
     proj_cond_workspace) is given, or p3d_proj_cond_noalloc when noalloc is
-    true (the library's own scratch). feat: [B, H, W, C], or a list of two such
+    true (the library's own scratch), or p3d_proj_cond_ordered when `order`
+    (int32 [n] device tensor from p3d_token_order) is given. feat: [B, H, W, C], or a list of two such
     maps (own H, W, C; samples concatenated, map 0 first); weight: [D, C_w]
     (torch Linear layout; C_w is checked against the summed C by the
     library); bias: [D] or None; out: [n + n_null, D]; all of one dtype
@@ -300,6 +321,11 @@ def p3d_proj_cond(coords, n, resolution, cams, feat, weight, out, bias=None, n_n
               _dev(out, "out", dtype, (n + n_null, D)), _dev(mask, "mask", torch.uint8, (n,)),
               _stream(stream))
     c = _dev(coords, "coords", torch.int32, (n, 4))
+    if order is not None:
+        _check(lib.p3d_proj_cond_ordered(c, n, int(resolution), POINTS[points], camarr, batch, dt,
+                                         _map_array(feats), len(feats), *common[:-1],
+                                         _dev(order, "order", torch.int32, (n,)), common[-1]))
+        return
     if noalloc:
         _check(lib.p3d_proj_cond_noalloc(c, n, int(resolution), POINTS[points], camarr, batch, dt,
                                          _map_array(feats), len(feats), *common))
@@ -328,8 +354,9 @@ STAT_FIELDS = ("tokens", "inside", "sum0", "sum1", "sum_sq0", "sum_sq1", "cos_su
 
 
 def p3d_projection_stats(coords, n, resolution, cams, feat, stats, points="cell_centres",
-                         stream=None):
-    """Enqueue p3d_projection_stats. feat: one [B, H, W, C] map or a list of
+                         stream=None, order=None):
+    """Enqueue p3d_projection_stats (p3d_projection_stats_ordered with an
+    order from p3d_token_order). feat: one [B, H, W, C] map or a list of
     two; stats: float64 device tensor of 8 elements (p3d_proj_stats, in
     STAT_FIELDS order), overwritten."""
     camarr, batch = _cams(cams)
@@ -344,25 +371,40 @@ def p3d_projection_stats(coords, n, resolution, cams, feat, stats, points="cell_
         maps[i].feat = _dev(f, "feat[%d]" % i)
         maps[i].height, maps[i].width, maps[i].channels = f.shape[1], f.shape[2], f.shape[3]
     n = int(n)
-    _check(lib.p3d_projection_stats(_dev(coords, "coords", torch.int32, (n, 4)), n,
-                                    int(resolution), POINTS[points], camarr, batch, dt, maps,
-                                    len(feats), _dev(stats, "stats", torch.float64, (8,)),
-                                    _stream(stream)))
+    _check(lib.p3d_projection_stats_ordered(_dev(coords, "coords", torch.int32, (n, 4)), n,
+                                            int(resolution), POINTS[points], camarr, batch, dt,
+                                            maps, len(feats),
+                                            _dev(order, "order", torch.int32, (n,)),
+                                            _dev(stats, "stats", torch.float64, (8,)),
+                                            _stream(stream)))
 
 
-def stats_summary(raw, channels):
-    """Coverage, per-map mean and std, mean cosine from the raw sums (a dict
-    of STAT_FIELDS, e.g. dict(zip(STAT_FIELDS, stats.tolist())))."""
-    t = raw["tokens"]
-    out = {"coverage": raw["inside"] / t if t else None}
-    for h, c in enumerate(channels):
-        cnt = t * c
-        mean = raw["sum%d" % h] / cnt if cnt else None
-        out["mean%d" % h] = mean
-        out["std%d" % h] = (max(raw["sum_sq%d" % h] / cnt - mean * mean, 0.0) ** 0.5
-                            if cnt else None)
-    out["cosine"] = raw["cos_sum"] / raw["cos_count"] if raw["cos_count"] else None
-    return out
+class p3d_proj_stats(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_double) for k in ("tokens", "inside", "sum0", "sum1", "sum_sq0",
+                                               "sum_sq1", "cos_sum", "cos_count")]
+
+
+class p3d_stats_fig(ctypes.Structure):
+    _fields_ = [("coverage", ctypes.c_double), ("mean", ctypes.c_double * 2),
+                ("std", ctypes.c_double * 2), ("cosine", ctypes.c_double)]
+
+
+def p3d_stats_figures(raw, channels):
+    """Coverage, per-map mean and std, mean cosine (p3d_stats_figures) from
+    the sums of p3d_projection_stats: raw is the stats tensor (8 float64,
+    any device) or a dict of STAT_FIELDS. Returns a dict; a figure whose
+    denominator is empty is None."""
+    if isinstance(raw, torch.Tensor):
+        vals = raw.detach().double().cpu().tolist()
+    else:
+        vals = [float(raw[k]) for k in STAT_FIELDS]
+    st = p3d_proj_stats(*vals)
+    ch = (ctypes.c_int32 * len(channels))(*[int(c) for c in channels])
+    fig = p3d_stats_fig()
+    _check(lib.p3d_stats_figures(ctypes.byref(st), ch, len(channels), ctypes.byref(fig)))
+    out = {"coverage": fig.coverage, "mean0": fig.mean[0], "std0": fig.std[0],
+           "mean1": fig.mean[1], "std1": fig.std[1], "cosine": fig.cosine}
+    return {k: (None if v != v else v) for k, v in out.items()}
 
 
 def _maps(feat, batch):
@@ -380,18 +422,47 @@ def _maps(feat, batch):
 
 
 def p3d_proj_sample(coords, n, resolution, cams, feat, S, mask=None, points="cell_centres",
-                    stream=None):
-    """Enqueue p3d_proj_sample: S [n, sum C] (dtype of the maps) receives the
-    samples the fused path would feed to proj_linear; feat is one map or a
-    list of two."""
+                    stream=None, order=None):
+    """Enqueue p3d_proj_sample (p3d_proj_sample_ordered with an order from
+    p3d_token_order): S [n, sum C] (dtype of the maps) receives the samples
+    the fused path would feed to proj_linear; feat is one map or a list of
+    two."""
     camarr, batch = _cams(cams)
     feats, maps, dt = _maps(feat, batch)
     n = int(n)
     K = sum(f.shape[3] for f in feats)
-    _check(lib.p3d_proj_sample(_dev(coords, "coords", torch.int32, (n, 4)), n, int(resolution),
-                               POINTS[points], camarr, batch, dt, maps, len(feats),
-                               _dev(S, "S", feats[0].dtype, (n, K)),
-                               _dev(mask, "mask", torch.uint8, (n,)), _stream(stream)))
+    _check(lib.p3d_proj_sample_ordered(_dev(coords, "coords", torch.int32, (n, 4)), n,
+                                       int(resolution), POINTS[points], camarr, batch, dt, maps,
+                                       len(feats), _dev(order, "order", torch.int32, (n,)),
+                                       _dev(S, "S", feats[0].dtype, (n, K)),
+                                       _dev(mask, "mask", torch.uint8, (n,)), _stream(stream)))
+
+
+def p3d_token_order_workspace_size(n, batch, key_height, key_width):
+    """Bytes of device workspace p3d_token_order needs."""
+    size = lib.p3d_token_order_workspace_size(int(n), int(batch), int(key_height),
+                                              int(key_width))
+    if size == 0:
+        raise P3DError(P3D_ERR_INVALID_ARG, lib.p3d_last_error().decode())
+    return int(size)
+
+
+def p3d_token_order(coords, n, resolution, cams, key_height, key_width, order, workspace=None,
+                    points="cell_centres", stream=None):
+    """Enqueue p3d_token_order: order (int32 [n] device tensor) receives an
+    image-space permutation of the tokens for a key_height x key_width map
+    (the largest the tokens sample). workspace: uint8 device tensor, or None
+    for a fresh one (allocated by torch here, not by the library)."""
+    camarr, batch = _cams(cams)
+    n = int(n)
+    if workspace is None:
+        workspace = torch.empty(p3d_token_order_workspace_size(n, batch, key_height, key_width),
+                                dtype=torch.uint8, device="cuda")
+    _check(lib.p3d_token_order(_dev(coords, "coords", torch.int32, (n, 4)), n, int(resolution),
+                               POINTS[points], camarr, batch, int(key_height), int(key_width),
+                               _dev(order, "order", torch.int32, (n,)),
+                               _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                               _stream(stream)))
 
 
 def p3d_proj_linear_grouped(S, weights, outs, biases=None, accumulate=False, stream=None):

@@ -476,6 +476,29 @@ p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution
     return ok();
 }
 
+p3d_status p3d_proj_cond_ordered(const int32_t* coords, int64_t n, int32_t resolution,
+                                 p3d_points points, const p3d_camera* cams, int32_t batch,
+                                 p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                 const void* weight, int32_t out_dim, int32_t weight_in,
+                                 const void* bias, int64_t n_null, void* out, uint8_t* mask,
+                                 const int32_t* order, void* stream) {
+    const char* fn = "p3d_proj_cond_ordered";
+    if (!aligned(order, 4)) return fail(P3D_ERR_UNSUPPORTED, "%s: order must be 4-byte aligned", fn);
+    ProjCondArgs a;
+    CamTable tab;
+    bool nothing;
+    p3d_status st = prepare_proj_cond(fn, coords, n, resolution, points, cams, batch, dtype, maps,
+                                      n_maps, weight, out_dim, weight_in, bias, n_null, out, mask,
+                                      &a, &tab, &nothing);
+    if (st != P3D_OK) return st;
+    if (nothing) return ok();
+    if (n > 0 && !order) return fail(P3D_ERR_INVALID_ARG, "%s: order is NULL", fn);
+    if (dtype == P3D_BF16) a.order = order;
+    hipError_t e = launch_proj_cond(a, dtype, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 size_t p3d_proj_cond_workspace_size(int64_t n, int32_t batch, const p3d_map* maps,
                                     int32_t n_maps) {
     const char* fn = "p3d_proj_cond_workspace_size";
@@ -546,11 +569,13 @@ p3d_status p3d_proj_cond_noalloc(const int32_t* coords, int64_t n, int32_t resol
                        static_cast<hipStream_t>(stream));
 }
 
-p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolution,
-                                p3d_points points, const p3d_camera* cams, int32_t batch,
-                                p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
-                                p3d_proj_stats* stats, void* stream) {
-    const char* fn = "p3d_projection_stats";
+p3d_status p3d_projection_stats_ordered(const int32_t* coords, int64_t n, int32_t resolution,
+                                        p3d_points points, const p3d_camera* cams, int32_t batch,
+                                        p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                        const int32_t* order, p3d_proj_stats* stats,
+                                        void* stream) {
+    const char* fn = order ? "p3d_projection_stats_ordered" : "p3d_projection_stats";
+    if (!aligned(order, 4)) return fail(P3D_ERR_UNSUPPORTED, "%s: order must be 4-byte aligned", fn);
     CamTable tab;
     p3d_status st = check_tokens(fn, coords, n, resolution, points, cams, batch, &tab);
     if (st != P3D_OK) return st;
@@ -594,16 +619,54 @@ p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolu
         a.C1 = maps[1].channels;
     }
     a.stats = stats;
+    a.order = order;
     hipError_t e = launch_stats(a, dtype == P3D_BF16, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }
 
-p3d_status p3d_proj_sample(const int32_t* coords, int64_t n, int32_t resolution,
-                           p3d_points points, const p3d_camera* cams, int32_t batch,
-                           p3d_dtype dtype, const p3d_map* maps, int32_t n_maps, void* S,
-                           uint8_t* mask, void* stream) {
-    const char* fn = "p3d_proj_sample";
+p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolution,
+                                p3d_points points, const p3d_camera* cams, int32_t batch,
+                                p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                p3d_proj_stats* stats, void* stream) {
+    return p3d_projection_stats_ordered(coords, n, resolution, points, cams, batch, dtype, maps,
+                                        n_maps, nullptr, stats, stream);
+}
+
+p3d_status p3d_stats_figures(const p3d_proj_stats* stats, const int32_t* channels,
+                             int32_t n_maps, p3d_stats_fig* out) {
+    const char* fn = "p3d_stats_figures";
+    if (!stats || !out || !channels)
+        return fail(P3D_ERR_INVALID_ARG, "%s: stats, channels and out must be non-NULL", fn);
+    if (n_maps < 1 || n_maps > 2)
+        return fail(P3D_ERR_INVALID_ARG, "%s: n_maps must be 1 or 2, got %d", fn, n_maps);
+    for (int32_t h = 0; h < n_maps; ++h)
+        if (channels[h] < 1)
+            return fail(P3D_ERR_INVALID_ARG, "%s: channels[%d] must be >= 1, got %d", fn, h,
+                        channels[h]);
+    const double t = stats->tokens;
+    out->coverage = t > 0.0 ? stats->inside / t : NAN;
+    for (int32_t h = 0; h < 2; ++h) {
+        out->mean[h] = NAN;
+        out->std[h] = NAN;
+        const double cnt = h < n_maps ? t * (double)channels[h] : 0.0;
+        if (cnt > 0.0) {
+            const double m = stats->sum[h] / cnt;
+            const double m2 = stats->sum_sq[h] / cnt;     // E[x^2]
+            out->mean[h] = m;
+            out->std[h] = sqrt(fmax(m2 - m * m, 0.0));  // rounding may dip below 0
+        }
+    }
+    out->cosine = stats->cos_count > 0.0 ? stats->cos_sum / stats->cos_count : NAN;
+    return ok();
+}
+
+p3d_status p3d_proj_sample_ordered(const int32_t* coords, int64_t n, int32_t resolution,
+                                   p3d_points points, const p3d_camera* cams, int32_t batch,
+                                   p3d_dtype dtype, const p3d_map* maps, int32_t n_maps,
+                                   const int32_t* order, void* S, uint8_t* mask, void* stream) {
+    const char* fn = order ? "p3d_proj_sample_ordered" : "p3d_proj_sample";
+    if (!aligned(order, 4)) return fail(P3D_ERR_UNSUPPORTED, "%s: order must be 4-byte aligned", fn);
     CamTable tab;
     p3d_status st = check_tokens(fn, coords, n, resolution, points, cams, batch, &tab);
     if (st != P3D_OK) return st;
@@ -649,10 +712,62 @@ p3d_status p3d_proj_sample(const int32_t* coords, int64_t n, int32_t resolution,
         a.out_stride = channels;
         a.out_col = col;
         a.mask = m == 0 ? mask : nullptr;
+        a.order = order;
         hipError_t e = launch_sample(a, dtype, dtype, tab, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return hip_fail(fn, e);
         col += maps[m].channels;
     }
+    return ok();
+}
+
+p3d_status p3d_proj_sample(const int32_t* coords, int64_t n, int32_t resolution,
+                           p3d_points points, const p3d_camera* cams, int32_t batch,
+                           p3d_dtype dtype, const p3d_map* maps, int32_t n_maps, void* S,
+                           uint8_t* mask, void* stream) {
+    return p3d_proj_sample_ordered(coords, n, resolution, points, cams, batch, dtype, maps,
+                                   n_maps, nullptr, S, mask, stream);
+}
+
+size_t p3d_token_order_workspace_size(int64_t n, int32_t batch, int32_t key_height,
+                                      int32_t key_width) {
+    if (n < 0 || n > kMaxTokens || batch < 1 || batch > P3D_MAX_BATCH || key_height < 1 ||
+        key_width < 1) {
+        fail(P3D_ERR_INVALID_ARG,
+             "p3d_token_order_workspace_size: needs 0 <= n <= %lld, 1 <= batch <= %d and a "
+             "key map of at least 1x1, got n = %lld, batch = %d, %dx%d",
+             (long long)kMaxTokens, P3D_MAX_BATCH, (long long)n, batch, key_height, key_width);
+        return 0;
+    }
+    g_err.clear();
+    return order_layout(n, batch, key_height, key_width, nullptr, nullptr);
+}
+
+p3d_status p3d_token_order(const int32_t* coords, int64_t n, int32_t resolution,
+                           p3d_points points, const p3d_camera* cams, int32_t batch,
+                           int32_t key_height, int32_t key_width, int32_t* order,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "p3d_token_order";
+    CamTable tab;
+    p3d_status st = check_tokens(fn, coords, n, resolution, points, cams, batch, &tab);
+    if (st != P3D_OK) return st;
+    st = check_map_size(fn, "key map", batch, key_height, key_width);
+    if (st != P3D_OK) return st;
+    if (n == 0) return ok();
+    if (!order || !aligned(order, 4))
+        return fail(P3D_ERR_INVALID_ARG, "%s: order must be a 4-byte aligned device array [n]",
+                    fn);
+    OrderBufs ob;
+    const size_t need = order_layout(n, batch, key_height, key_width, workspace, &ob);
+    if (!workspace || workspace_bytes < need)
+        return fail(P3D_ERR_INVALID_ARG,
+                    "%s: workspace must be a device buffer of at least %zu bytes "
+                    "(p3d_token_order_workspace_size), got %zu bytes at %p",
+                    fn, need, workspace_bytes, workspace);
+    if (!aligned(workspace, 256))
+        return fail(P3D_ERR_UNSUPPORTED, "%s: workspace must be 256-byte aligned", fn);
+    const OrderArgs oa{coords, n, resolution, (int32_t)points, batch};
+    hipError_t e = launch_order(oa, tab, ob, order, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }
 

@@ -43,6 +43,16 @@ __device__ __forceinline__ void token_cell(const int32_t* __restrict__ coords, i
     }
 }
 
+// The token at position t of an image-space order (order.hip), or t itself
+// without one. An order entry outside [0, n) (a caller contract violation)
+// is clamped into it, so no access leaves the coords or output rows.
+__device__ __forceinline__ int64_t ordered_token(const int32_t* __restrict__ order, int64_t t,
+                                                int64_t n) {
+    if (!order) return t;
+    const int64_t k = order[t];
+    return k < 0 ? 0 : (k >= n ? n - 1 : k);
+}
+
 // Cell centre in the unit cube [-1/2, 1/2]: (c + 1/2)/R - 1/2, binary32.
 __device__ __forceinline__ float cell_centre(int32_t c, int32_t R) {
     return ((float)c + 0.5f) / (float)R - 0.5f;
@@ -180,6 +190,7 @@ struct SampleArgs {
     int64_t out_stride;           // elements per output row
     int32_t out_col;
     uint8_t* mask;                // project mode: in-image mask, or NULL
+    const int32_t* order;         // project mode: token of each position, or NULL
 };
 
 struct ProjCondArgs {
@@ -215,6 +226,7 @@ struct StatsArgs {
     const void* feat1;            // or C1 == 0
     int32_t H1, W1, C1;
     p3d_proj_stats* stats;
+    const int32_t* order;         // token of each position, or NULL
 };
 
 struct GroupedArgs {

@@ -114,7 +114,7 @@ __device__ __forceinline__ int4 token_entry(const ProjCondArgs& a, const CamTabl
                                             int64_t t, int32_t H, int32_t W, uint8_t* mask) {
     int4 e = make_int4(0, 4, 0, 0);
     if (t < a.n) {
-        const int64_t tok = a.order ? (int64_t)a.order[t] : t;
+        const int64_t tok = ordered_token(a.order, t, a.n);
         int32_t b, x, y, z;
         token_cell(a.coords, tok, a.R, b, x, y, z);
         const Projected pr = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
@@ -380,7 +380,7 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
             const int64_t t = m0 + ptid;
             uint8_t mk = 0;
             s_tok[ptid] = token_entry(a, cams, t, a.H, a.W, &mk);
-            if (a.mask && nt == 0 && t < a.n) a.mask[a.order ? (int64_t)a.order[t] : t] = mk;
+            if (a.mask && nt == 0 && t < a.n) a.mask[ordered_token(a.order, t, a.n)] = mk;
         }
         lds_barrier();                                            // tokens parked
 
@@ -411,7 +411,8 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
         // consumers' stores (S stage 0 is free after the last chunk)
         if (a.order) {
             int32_t* s_rows = reinterpret_cast<int32_t*>(sA0);
-            if (ptid < BMt) s_rows[ptid] = m0 + ptid < a.n ? a.order[m0 + ptid] : -1;
+            if (ptid < BMt)
+                s_rows[ptid] = m0 + ptid < a.n ? (int32_t)ordered_token(a.order, m0 + ptid, a.n) : -1;
         }
         __syncthreads();                                          // consumers staged
         return;

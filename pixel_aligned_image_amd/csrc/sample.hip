@@ -64,6 +64,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, CamTable
 
     __shared__ int32_t s_row[kTok][4];
     __shared__ float s_w[kTok][4];
+    __shared__ int64_t s_out[kTok];        // output row of each point
 
     const int64_t t0 = tile * kTok;
     const int ntok = (int)((a.n - t0) < kTok ? (a.n - t0) : kTok);
@@ -72,13 +73,16 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, CamTable
         float2 gp;
         int32_t b;
         if constexpr (Project) {
+            const int64_t tk = ordered_token(a.order, t, a.n);
+            s_out[threadIdx.x] = tk;
             int32_t x, y, z;
-            token_cell(a.coords, t, a.R, b, x, y, z);
+            token_cell(a.coords, tk, a.R, b, x, y, z);
             const Projected p = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
             gp = make_float2(p.gx, p.gy);
             b = p.b;
-            if (a.mask && slice == 0) a.mask[t] = p.mask;
+            if (a.mask && slice == 0) a.mask[tk] = p.mask;
         } else {
+            s_out[threadIdx.x] = t;
             gp = reinterpret_cast<const float2*>(a.grid)[t];
             b = a.bidx ? a.bidx[t] : 0;
             b = b < 0 ? 0 : (b >= a.batch ? a.batch - 1 : b);
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, CamTable
 #pragma unroll
             for (int e = 0; e < kEpv; ++e)
                 r[e] = fmaf(w3, f3[e], fmaf(w2, f2[e], fmaf(w1, f1[e], w0 * f0[e])));
-            const int64_t t = t0 + tok[u];
+            const int64_t t = s_out[tok[u]];
             if (OutBf16) {
                 uint4 o;
                 o.x = pack_bf16x2(r[0], r[1]);

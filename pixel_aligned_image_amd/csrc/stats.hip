@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerCU / (kThreads / 64)) void stats
         int in = 0;
         if (valid) {
             int32_t b, x, y, z;
-            token_cell(a.coords, t, a.R, b, x, y, z);
+            token_cell(a.coords, ordered_token(a.order, t, a.n), a.R, b, x, y, z);
             const Projected p = project_cell(b, x, y, z, a.R, a.points, cams, a.batch);
             m0 = meta_of(p, a.H0, a.W0);
             if (two) m1 = meta_of(p, a.H1, a.W1);

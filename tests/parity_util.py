@@ -131,15 +131,17 @@ def run_fused(p3d, o, coords, n, R, fovs, dists, maps_np, W_np, b_np, n_null, bf
     return None
 
 
-def run_stats(p3d, o, coords, n, R, fovs, dists, maps_np, bf16, points, image_size):
-    """p3d_projection_stats on the GPU against the oracle: counts exact, sums
-    within 1e-5 (fp32) or one bf16 rounding (2^-8) of sum |S|, the cosine
-    count exact and its mean within 1e-6 / 1e-3. Returns (got, want)."""
+def run_stats(p3d, o, coords, n, R, fovs, dists, maps_np, bf16, points, image_size,
+              order=None):
+    """p3d_projection_stats (p3d_projection_stats_ordered with a device
+    order) on the GPU against the oracle: counts exact, sums within 1e-5
+    (fp32) or one bf16 rounding (2^-8) of sum |S|, the cosine count exact and
+    its mean within 1e-6 / 1e-3. Returns (got, want)."""
     cp = product_cameras(p3d, fovs, dists, image_size)
     fo, do = oracle_cameras(o, fovs, dists, image_size)
     stats = torch.full((8,), float("nan"), dtype=torch.float64, device="cuda")
     feats = [to_dev(m, bf16) for m in maps_np]
-    p3d.p3d_projection_stats(to_dev(coords), n, R, cp, feats, stats, points=points)
+    p3d.p3d_projection_stats(to_dev(coords), n, R, cp, feats, stats, points=points, order=order)
     torch.cuda.synchronize()
     got = dict(zip(p3d.STAT_FIELDS, stats.cpu().numpy().tolist()))
     want = o.projection_stats(coords, n, R, fo, do, list(maps_np), points=points)
@@ -158,6 +160,26 @@ def run_stats(p3d, o, coords, n, R, fovs, dists, maps_np, bf16, points, image_si
         assert dc <= (1e-3 if bf16 else 1e-6), dc
     else:
         assert got["cos_sum"] == 0.0
+    # the printed figures: the library's p3d_stats_figures on the GPU's sums
+    # against the oracle's own derivation on its sums. With the sums' bounds
+    # above: |d mean| <= tol rms, |d std^2| <= 4 tol E[x^2], so
+    # |d std| <= 2 tol E[x^2] / std.
+    ch = [m.shape[3] for m in maps_np]
+    gf = p3d.p3d_stats_figures(stats, ch)
+    wf = o.stats_figures(want, ch)
+    assert gf["coverage"] == wf["coverage"]
+    for h in range(2):
+        if h >= len(ch):
+            assert gf["mean%d" % h] is None and gf["std%d" % h] is None
+            continue
+        e2 = want["sum_sq%d" % h] / (n * ch[h])
+        assert abs(gf["mean%d" % h] - wf["mean%d" % h]) <= tol * np.sqrt(e2) + 1e-300, h
+        assert abs(gf["std%d" % h] - wf["std%d" % h]) <= \
+            2 * tol * e2 / max(wf["std%d" % h], 1e-300) + 1e-300, h
+    if want["cos_count"]:
+        assert abs(gf["cosine"] - wf["cosine"]) <= (1e-3 if bf16 else 1e-6)
+    else:
+        assert gf["cosine"] is None and wf["cosine"] is None
     return got, want
 
 

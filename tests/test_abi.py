@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(p3d):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 23, names
     lib = ctypes.CDLL(p3d.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -357,3 +357,99 @@ def test_proj_cond_ws_validation(p3d):
     # nothing to do: no workspace needed
     assert lib.p3d_proj_cond_ws(None, 0, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 16,
                                 None, 0, 8192, None, None, 0, None) == p3d.P3D_OK
+
+
+def test_stats_figures_closed_forms(p3d):
+    """p3d_stats_figures is host code: the figures of hand-made sums. Map 0:
+    4 tokens x 2 channels of values {1, 3} (mean 2, std 1); map 1: values
+    all 5 (std 0, sum_sq - N mean^2 rounds to 0); 3 of 4 tokens inside;
+    cosines summing to 1.5 over 2 tokens."""
+    raw = dict(tokens=4.0, inside=3.0, sum0=16.0, sum1=40.0, sum_sq0=40.0, sum_sq1=200.0,
+               cos_sum=1.5, cos_count=2.0)
+    f = p3d.p3d_stats_figures(raw, [2, 2])
+    assert f == dict(coverage=0.75, mean0=2.0, std0=1.0, mean1=5.0, std1=0.0, cosine=0.75)
+    f = p3d.p3d_stats_figures(dict(raw, cos_count=0.0, cos_sum=0.0), [2])
+    assert f["mean1"] is None and f["std1"] is None and f["cosine"] is None
+    assert p3d.p3d_stats_figures(dict.fromkeys(p3d.STAT_FIELDS, 0.0), [8]) == dict(
+        coverage=None, mean0=None, std0=None, mean1=None, std1=None, cosine=None)
+    # E[x^2] a hair below mean^2 after rounding: std is 0, not NaN
+    f = p3d.p3d_stats_figures(dict(raw, sum0=0.3 * 8, sum_sq0=0.09 * 8 * (1 - 1e-16)), [2, 2])
+    assert f["std0"] == 0.0
+    for channels in ([0], [2, 2, 2], [2, -1]):
+        with pytest.raises(p3d.P3DError) as e:
+            p3d.p3d_stats_figures(raw, channels)
+        assert e.value.status == p3d.P3D_ERR_INVALID_ARG
+
+
+def test_token_order_workspace_size(p3d):
+    """Sort keys (4 bytes per token) plus two bin tables of at most 16384
+    counters, each part 256-byte aligned; refusals name the call."""
+    lib = p3d.lib
+    size = lib.p3d_token_order_workspace_size(100000, 1, 512, 512)
+    assert size % 256 == 0 and 400000 <= size <= 400128 + 2 * 4 * 16384 + 2 * 256, size
+    # 32 x 32 blocks of 16 texels per 512 x 512 item: 1024 bins per item, up
+    # to 16 items; 32 items take 32-texel blocks (256 bins each)
+    assert size == 400128 + 2 * 4 * 1024
+    assert lib.p3d_token_order_workspace_size(100000, 16, 512, 512) == 400128 + 2 * 4 * 16384
+    assert lib.p3d_token_order_workspace_size(100000, 32, 512, 512) == 400128 + 2 * 4 * 8192
+    for args in [(-1, 1, 8, 8), (10, 0, 8, 8), (10, 1, 0, 8), (10, 1, 8, 0)]:
+        assert lib.p3d_token_order_workspace_size(*args) == 0, args
+        assert p3d.p3d_last_error().startswith("p3d_token_order_workspace_size")
+
+
+def test_token_order_validation(p3d):
+    lib = p3d.lib
+    cams = p3d.make_cameras([(2.0, 2.0)])
+    need = lib.p3d_token_order_workspace_size(40, 1, 8, 8)
+    st = lib.p3d_token_order(4096, 40, 8, 0, cams, 1, 8, 8, 4096, 4096, need - 256, None)
+    assert st == p3d.P3D_ERR_INVALID_ARG
+    msg = p3d.p3d_last_error()
+    assert msg.startswith("p3d_token_order") and str(need) in msg
+    st = lib.p3d_token_order(4096, 40, 8, 0, cams, 1, 8, 8, None, 4096, need, None)
+    assert st == p3d.P3D_ERR_INVALID_ARG and "order" in p3d.p3d_last_error()
+    st = lib.p3d_token_order(4096, 40, 8, 0, cams, 1, 8, 8, 4096, 4100, need, None)
+    assert st == p3d.P3D_ERR_UNSUPPORTED and "256-byte" in p3d.p3d_last_error()
+    st = lib.p3d_token_order(4096, 40, 8, 0, cams, 1, 0, 8, 4096, 4096, need, None)
+    assert st != p3d.P3D_OK and p3d.p3d_last_error().startswith("p3d_token_order")
+    st = lib.p3d_token_order(4096, 40, 8, 0, cams, 2, 8, 8, 4096, 4096, need, None)
+    assert st != p3d.P3D_OK            # two batch items, one camera
+    assert lib.p3d_token_order(None, 0, 8, 0, cams, 1, 8, 8, None, None, 0, None) == p3d.P3D_OK
+
+
+def test_ordered_stats_and_sample_validation(p3d):
+    """The ordered variants run the checks of the plain calls under their own
+    names, and refuse a misaligned order."""
+    lib = p3d.lib
+    cams = p3d.make_cameras([(2.0, 2.0)])
+    one = _maps(p3d, [(8, 8, 16)])
+    one[0].feat = 4096
+    st = lib.p3d_projection_stats_ordered(4096, 40, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4098,
+                                          4096, None)
+    assert st == p3d.P3D_ERR_UNSUPPORTED
+    assert p3d.p3d_last_error().startswith("p3d_projection_stats_ordered")
+    st = lib.p3d_projection_stats_ordered(4096, 40, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096,
+                                          None, None)
+    assert st == p3d.P3D_ERR_INVALID_ARG and "stats" in p3d.p3d_last_error()
+    st = lib.p3d_proj_sample_ordered(4096, 40, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4098, 4096,
+                                     None, None)
+    assert st == p3d.P3D_ERR_UNSUPPORTED
+    assert p3d.p3d_last_error().startswith("p3d_proj_sample_ordered")
+    st = lib.p3d_proj_sample_ordered(4096, 40, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, None,
+                                     None, None)
+    assert st == p3d.P3D_ERR_INVALID_ARG and "S is NULL" in p3d.p3d_last_error()
+
+
+def test_proj_cond_ordered_validation(p3d):
+    lib = p3d.lib
+    cams = p3d.make_cameras([(2.0, 2.0)])
+    one = _maps(p3d, [(8, 8, 16)])
+    one[0].feat = 4096
+    args = (4096, 40, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 16, None, 0, 8192, None)
+    assert lib.p3d_proj_cond_ordered(*args, 4098, None) == p3d.P3D_ERR_UNSUPPORTED
+    assert p3d.p3d_last_error().startswith("p3d_proj_cond_ordered")
+    assert lib.p3d_proj_cond_ordered(*args, None, None) == p3d.P3D_ERR_INVALID_ARG
+    assert "order is NULL" in p3d.p3d_last_error()
+    bad = (4096, 40, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 24, None, 0, 8192, None)
+    assert lib.p3d_proj_cond_ordered(*bad, 4096, None) == p3d.P3D_ERR_SHAPE
+    assert lib.p3d_proj_cond_ordered(None, 0, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 16,
+                                     None, 0, 8192, None, None, None) == p3d.P3D_OK

@@ -109,7 +109,13 @@ def test_project_points_workloads(orc, wl):
          dists=[None, None, 0.9]),
     dict(R=1024, B=2, H=512, W=512, dense=False, n=777, spill=0, fovs=[40.0, 30.0],
          dists=[None, None]),
-], ids=["R1", "R2_b2", "behind_camera", "R5_b3", "spill_outside_cube", "R1024"])
+    # distance 0.25 with R = 2: the far layer of cell centres sits at z =
+    # 0.25, depth exactly 0, so gx, gy are +-inf (or NaN on the axis) and
+    # the index clamp picks the edge texel (texel 0 for NaN); mask 0
+    dict(R=2, B=1, H=4, W=5, dense=True, fovs=[40.0], dists=[0.25]),
+    dict(R=4, B=2, H=6, W=6, dense=True, fovs=[60.0, 30.0], dists=[0.125, 0.375]),
+], ids=["R1", "R2_b2", "behind_camera", "R5_b3", "spill_outside_cube", "R1024",
+        "depth_zero_R2", "depth_zero_R4_b2"])
 def test_project_points_edges(orc, case):
     say("project edge", case)
     R, B = case["R"], case["B"]
@@ -251,6 +257,12 @@ SMALL = [
          n_null=17),
     dict(name="bf16_outside_frame", bf16=True, R=16, B=1, n=400, H=16, W=16, C=64, D=256,
          bias=True, n_null=0, fov=70.0, dist=0.8, spill=4),
+    # depth exactly 0 (distance 0.25, R = 2): infinite normalised coordinates
+    # reach the sampler from coords; the clamp picks the edge texel
+    dict(name="bf16_depth_zero", bf16=True, R=2, B=1, n=None, H=4, W=4, C=64, D=64, bias=True,
+         n_null=2, dist=0.25),
+    dict(name="f32_depth_zero", bf16=False, R=2, B=1, n=None, H=5, W=3, C=16, D=24, bias=False,
+         n_null=0, dist=0.25),
     # null rows far beyond the token rows, ragged, 25 vectors per row
     dict(name="bf16_null_heavy", bf16=True, R=16, B=1, n=130, H=8, W=8, C=64, D=200,
          bias=True, n_null=700),

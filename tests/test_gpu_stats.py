@@ -4,7 +4,9 @@ squares within 1e-5 of sum |S| for binary32 maps and within one bf16
 rounding (2^-8 of sum |S|) for bf16 maps, where a sample's rounding may fall
 on the other side of a tie between the kernel's binary32 blend and the
 oracle's binary64 one; the cosine count exact, its mean within 1e-6 (fp32)
-or 1e-3 (bf16)."""
+or 1e-3 (bf16); the printed figures (p3d_stats_figures on the GPU's sums)
+against the oracle's derivation (orc_stats_figures on its sums) within the
+bounds those sums imply."""
 import os
 import sys
 
@@ -84,4 +86,4 @@ def test_stats_workloads(orc, name):
     say(name, "tokens", w.n_tokens)
     got, want = _check(orc, coords, w.n_tokens, w.resolution, synth.fovs(w), [None] * w.batch,
                        maps, w.dtype == "bf16", w.points, w.width)
-    say("  ", p3d.stats_summary(got, [m.shape[3] for m in maps]))
+    say("  ", p3d.p3d_stats_figures(got, [m.shape[3] for m in maps]))

@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# P3D_ORACLE_LIB names another build of the same source (the sanitizer
+# runs load an AddressSanitizer/UBSan build through it)
+LIB_PATH = os.environ.get("P3D_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)

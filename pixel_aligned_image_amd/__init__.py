@@ -25,7 +25,10 @@ __all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_versi
            "p3d_token_order", "p3d_token_order_workspace_size",
            "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libp3d.so")
+# P3D_LIB names another build of the same sources (the sanitizer run of the
+# host validation layer loads a host-AddressSanitizer build through it)
+LIB_PATH = os.environ.get("P3D_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                      "libp3d.so")
 
 P3D_OK, P3D_ERR_INVALID_ARG, P3D_ERR_SHAPE, P3D_ERR_DTYPE, P3D_ERR_UNSUPPORTED, P3D_ERR_HIP = range(6)
 P3D_F32, P3D_BF16 = 0, 1

@@ -29,9 +29,11 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(out=LIB, extra=(), jobs=8, verbose=False):
-    """Compile every HIP source and link the shared library; returns its path."""
-    objdir = os.path.join(HERE, "_build")
+def build(out=LIB, extra=(), jobs=8, verbose=False, objdir=None, link_extra=()):
+    """Compile every HIP source and link the shared library; returns its path.
+    extra: more compile flags (later flags win, e.g. another -O level);
+    objdir: where the objects go (default _build/ next to this file)."""
+    objdir = objdir or os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs, objs = [], []
     for src in sources():
@@ -46,8 +48,8 @@ def build(out=LIB, extra=(), jobs=8, verbose=False):
     for p in procs:
         _wait(p)
     tmp = out + ".tmp%d" % os.getpid()
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
-                   check=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_extra, *objs,
+                    "-o", tmp], check=True)
     os.replace(tmp, out)
     return out
 

@@ -1,0 +1,149 @@
+"""Stream semantics: every device entry point only enqueues work on the
+caller's stream and returns; none waits for the device.
+
+A spin kernel (torch.cuda._sleep) is queued first on the stream and holds it
+for about 100 ms; each call is then made behind it. The call must return
+while the stream is still busy (stream.query() is False right after it) and
+its host time must stay far below the spin -- a call that synchronised the
+device, the stream, or copied to the host with a blocking copy would wait for
+the spin to end. The results are checked after the spin (the queued work ran
+in order), so nothing here trusts an output that was not yet written.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import p3d_synth as synth
+import pixel_aligned_image_amd as p3d
+from parity_util import product_cameras, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SPIN_MS = 100.0
+
+
+def say(*a):
+    print("[async]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def spin_cycles():
+    """Cycles of torch.cuda._sleep that hold the stream for about SPIN_MS."""
+    torch.cuda.synchronize()
+    probe = 10_000_000
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(probe)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    cycles = int(probe * SPIN_MS / max(ms, 1e-3))
+    say("spin: %d cycles = %.2f ms -> %d cycles for %.0f ms" % (probe, ms, cycles, SPIN_MS))
+    return cycles
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    rng = np.random.default_rng(12)
+    R, B, n, C, D = 64, 2, 5000, 256, 192
+    coords = synth.random_coords(R, B, n, seed=4, spill=1)
+    feat = to_dev(synth.bf16_bits(rng.standard_normal((B, 32, 32, C)).astype(np.float32)), True)
+    feat2 = to_dev(synth.bf16_bits(rng.standard_normal((B, 64, 64, 128)).astype(np.float32)),
+                   True)
+    W = to_dev(synth.bf16_bits((rng.standard_normal((D, C)) * 0.05).astype(np.float32)), True)
+    cams = product_cameras(p3d, [40.0, 50.0], [None, None], 32)
+    return dict(R=R, B=B, n=n, C=C, D=D, coords=to_dev(coords), feat=feat, feat2=feat2, W=W,
+                cams=cams)
+
+
+def _behind_spin(cycles, fn):
+    s = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(cycles)
+    t0 = time.perf_counter()
+    fn()
+    dt = (time.perf_counter() - t0) * 1e3
+    busy = not s.query()
+    torch.cuda.synchronize()
+    return dt, busy
+
+
+def _calls(x):
+    n, R, cams = x["n"], x["R"], x["cams"]
+    out = torch.empty((n + 7, x["D"]), dtype=torch.bfloat16, device="cuda")
+    mask = torch.empty((n,), dtype=torch.uint8, device="cuda")
+    ws = p3d.proj_cond_workspace(n, x["B"], x["feat"])
+    order = torch.arange(n, dtype=torch.int32, device="cuda")
+    ows = torch.empty((p3d.p3d_token_order_workspace_size(n, x["B"], 32, 32),), dtype=torch.uint8,
+                      device="cuda")
+    grid = torch.zeros((n, 2), device="cuda")
+    S = torch.zeros((n, x["C"] + 128), dtype=torch.bfloat16, device="cuda")
+    s0 = torch.empty((n, x["C"]), dtype=torch.bfloat16, device="cuda")
+    stats = torch.empty(8, dtype=torch.float64, device="cuda")
+    q = torch.empty_like(x["coords"])
+    ys = [torch.zeros((n, x["D"]), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    Wk = to_dev(synth.bf16_bits(np.full((x["D"], x["C"] + 128), 0.01, np.float32)), True)
+    bidx = x["coords"][:, 0].contiguous()
+    feat, W, coords = x["feat"], x["W"], x["coords"]
+    return {
+        "p3d_project_points": lambda: p3d.p3d_project_points(coords, n, R, cams, 32, 32,
+                                                             grid=grid, mask=mask),
+        "p3d_requantize_coords": lambda: p3d.p3d_requantize_coords(coords, R, 16, q),
+        "p3d_bilinear_sample": lambda: p3d.p3d_bilinear_sample(feat, grid, s0,
+                                                               batch_index=bidx),
+        "p3d_proj_cond": lambda: p3d.p3d_proj_cond(coords, n, R, cams, feat, W, out, n_null=7,
+                                                   mask=mask),
+        "p3d_proj_cond_ws": lambda: p3d.p3d_proj_cond(coords, n, R, cams, feat, W, out,
+                                                      n_null=7, mask=mask, workspace=ws),
+        "p3d_proj_cond_noalloc": lambda: p3d.p3d_proj_cond(coords, n, R, cams, feat, W, out,
+                                                           n_null=7, mask=mask, noalloc=True),
+        "p3d_token_order": lambda: p3d.p3d_token_order(coords, n, R, cams, 32, 32, order,
+                                                       workspace=ows),
+        "p3d_proj_cond_ordered": lambda: p3d.p3d_proj_cond(coords, n, R, cams, feat, W, out,
+                                                           n_null=7, mask=mask, order=order),
+        "p3d_projection_stats": lambda: p3d.p3d_projection_stats(coords, n, R, cams,
+                                                                 [feat, x["feat2"]], stats),
+        "p3d_proj_sample": lambda: p3d.p3d_proj_sample(coords, n, R, cams, [feat, x["feat2"]], S,
+                                                       order=order),
+        "p3d_proj_linear_grouped": lambda: p3d.p3d_proj_linear_grouped(S, [Wk, Wk], ys,
+                                                                       accumulate=True),
+    }
+
+
+CALLS = ["p3d_project_points", "p3d_requantize_coords", "p3d_bilinear_sample", "p3d_proj_cond",
+         "p3d_proj_cond_ws", "p3d_proj_cond_noalloc", "p3d_token_order", "p3d_proj_cond_ordered",
+         "p3d_projection_stats", "p3d_proj_sample", "p3d_proj_linear_grouped"]
+
+
+@pytest.mark.parametrize("name", CALLS)
+def test_call_returns_before_the_stream_drains(spin_cycles, inputs, name):
+    calls = _calls(inputs)
+    fn = calls[name]
+    fn()                               # first call: lazy set-up (module load, symbol lookup)
+    torch.cuda.synchronize()
+    dt, busy = _behind_spin(spin_cycles, fn)
+    say("%s: returned after %.3f ms, stream busy %s" % (name, dt, busy))
+    assert busy, "%s: the stream had drained when the call returned" % name
+    assert dt < SPIN_MS / 4, "%s: the call took %.1f ms behind a %.0f ms spin" % (name, dt,
+                                                                                  SPIN_MS)
+
+
+def test_ordered_results_after_spin(spin_cycles, inputs):
+    """The calls queued behind the spin produce the same bytes as without it."""
+    x = inputs
+    calls = _calls(x)
+    n, R, cams = x["n"], x["R"], x["cams"]
+    ref = torch.empty((n + 7, x["D"]), dtype=torch.bfloat16, device="cuda")
+    p3d.p3d_proj_cond(x["coords"], n, R, cams, x["feat"], x["W"], ref, n_null=7)
+    torch.cuda.synchronize()
+    out = torch.full_like(ref, float("nan"))
+    torch.cuda._sleep(spin_cycles)
+    p3d.p3d_proj_cond(x["coords"], n, R, cams, x["feat"], x["W"], out, n_null=7,
+                      workspace=p3d.proj_cond_workspace(n, x["B"], x["feat"]))
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
+    del calls

@@ -695,28 +695,31 @@ p3d_status p3d_proj_sample_ordered(const int32_t* coords, int64_t n, int32_t res
     if (!aligned(S, 16)) return fail(P3D_ERR_UNSUPPORTED, "%s: S must be 16-byte aligned", fn);
     if (n == 0) return ok();
     if (!S) return fail(P3D_ERR_INVALID_ARG, "%s: S is NULL", fn);
-    int32_t col = 0;
-    for (int32_t m = 0; m < n_maps; ++m) {
-        SampleArgs a{};
-        a.feat = maps[m].feat;
-        a.batch = batch;
-        a.H = maps[m].height;
-        a.W = maps[m].width;
-        a.C = maps[m].channels;
-        a.coords = coords;
-        a.R = resolution;
-        a.points = (int32_t)points;
-        a.project = true;
-        a.n = n;
-        a.out = S;
-        a.out_stride = channels;
-        a.out_col = col;
-        a.mask = m == 0 ? mask : nullptr;
-        a.order = order;
-        hipError_t e = launch_sample(a, dtype, dtype, tab, static_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return hip_fail(fn, e);
-        col += maps[m].channels;
+    // both maps in one launch: map 1's samples follow map 0's in each S row
+    SampleArgs a{};
+    a.feat = maps[0].feat;
+    a.batch = batch;
+    a.H = maps[0].height;
+    a.W = maps[0].width;
+    a.C = maps[0].channels;
+    if (n_maps == 2) {
+        a.feat1 = maps[1].feat;
+        a.H1 = maps[1].height;
+        a.W1 = maps[1].width;
+        a.C1 = maps[1].channels;
     }
+    a.coords = coords;
+    a.R = resolution;
+    a.points = (int32_t)points;
+    a.project = true;
+    a.n = n;
+    a.out = S;
+    a.out_stride = channels;
+    a.out_col = 0;
+    a.mask = mask;
+    a.order = order;
+    hipError_t e = launch_sample(a, dtype, dtype, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
 }
 

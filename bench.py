@@ -214,7 +214,7 @@ def hbm_copy_ceiling(stream, reps, mib=2048):
     gbs = 2.0 * n * 4 / (ms * 1e-3) / 1e9
     del a, b
     torch.cuda.empty_cache()
-    return {"kernel": "torch copy_ (elementwise copy)", "bytes_per_launch": 2 * n * 4,
+    return {"kernel": "torch copy_ of a contiguous tensor (the HIP runtime's device-to-device copy kernel)", "bytes_per_launch": 2 * n * 4,
             "mean_ms": ms, "achieved": gbs, "unit": "GB/s", "frac_of_peak": gbs / HBM_PEAK_GBS}
 
 

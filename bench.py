@@ -179,7 +179,7 @@ def cpu_leg(o, inp, cams_o, threads, target_s):
 def cpu_baseline(inp, cams_o, target_s=10.0):
     """The oracle, untuned, on a bounded prefix of the same tokens: one leg
     on every core this process may run on, one on a single thread; tokens/s
-    (the rate over the prefix, not a full pass)."""
+    is the rate over the prefix, and a full pass is extrapolated from it."""
     import oracle
     o = oracle.get()
     cores = len(os.sched_getaffinity(0))
@@ -194,8 +194,10 @@ def cpu_baseline(inp, cams_o, target_s=10.0):
                       "CPU %s, %d cores in the affinity mask%s" % (
                           d_all, inp["n"], what, t_all, used, cpu_model(), cores,
                           "" if quota is None else ", cgroup CPU quota %.1f cores" % quota),
+            "extrapolated_full_pass_s": inp["n"] / (d_all / t_all),
             "single_thread": {"value": d_one / t_one, "unit": "tokens/s", "cores": 1,
-                              "sample": "first %d tokens, %.1f s on 1 thread" % (d_one, t_one)},
+                              "sample": "first %d tokens, %.1f s on 1 thread" % (d_one, t_one),
+                              "extrapolated_full_pass_s": inp["n"] / (d_one / t_one)},
             "affinity_cores": cores, "cpu_quota_cores": quota, "cpu_model": cpu_model()}
 
 

@@ -32,7 +32,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTok = 16;        // points per workgroup
-constexpr int kUnroll = 4;      // 16-byte items in flight per thread per step
+// 16-byte items in flight per thread per step: 4 for the standalone gather,
+// 3 for the projected gather (swept on the 1024^3 shell gather and the
+// texture stage's two maps: 2 / 3 / 4 / 8 items gave 0.206 / 0.204 / 0.202 /
+// 0.248 ms and 0.165 / 0.165 / 0.169 / 0.210 ms)
+template <bool Project>
+constexpr int unroll_items() { return Project ? 3 : 4; }
 constexpr int kSlice = 64;      // 16-byte vectors per channel slice (1 KB)
 
 struct Vec8 {
@@ -133,6 +138,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, CamTable
     const int items = ntok * svpr;
     const uint4* __restrict__ feat = reinterpret_cast<const uint4*>(map);
 
+    constexpr int kUnroll = unroll_items<Project>();
     for (int base = threadIdx.x; base < items; base += kThreads * kUnroll) {
         uint4 q[kUnroll][4];
         int tok[kUnroll], vec[kUnroll];

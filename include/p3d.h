@@ -320,7 +320,7 @@ p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution
  *
  * For BF16 and n > 0 the call first sorts the tokens by the texel block
  * their top-left bilinear corner falls in (batch item, then the Morton index
- * of 16 x 16-texel blocks on the map with the most texels) with a counting
+ * of 4 x 4-texel blocks on the map with the most texels) with a counting
  * sort in the workspace, then runs p3d_proj_cond_ex's fused kernel over the
  * tokens in that order, writing each token's row and mask byte at the
  * token's own index. Tokens that share corner rows are then processed
@@ -416,9 +416,9 @@ p3d_status p3d_projection_stats(const int32_t* coords, int64_t n, int32_t resolu
  * the four texels around its projection).
  *
  * order[i] receives the token at sorted position i, a permutation of
- * [0, n): tokens sorted by batch item, then by the Morton index of the 16 x
- * 16-texel block (coarser for very large maps or batches, so that there are
- * at most 16384 blocks) that contains their top-left corner texel on a
+ * [0, n): tokens sorted by batch item, then by the Morton index of the 4 x
+ * 4-texel block (coarser for large maps or batches, so that there are at
+ * most 16384 blocks) that contains their top-left corner texel on a
  * key_height x key_width map -- the largest map the tokens will sample. The
  * projection is p3d_project_points_ex's. The order among tokens of one block
  * is unspecified and may change from call to call; results of the *_ordered

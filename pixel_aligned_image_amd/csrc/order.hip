@@ -16,8 +16,12 @@
 //   2. bin_kernel: project every token (the same binary32 steps as every
 //      other kernel: pixel-aligned head commit of pixal3d_mrp_mlx) onto the
 //      key map -- the one with the most texels -- and give it the bin (batch
-//      item, Morton index of the 16 x 16-texel block holding its top-left
+//      item, Morton index of the 4 x 4-texel block holding its top-left
 //      corner texel); blocks are coarser when the bins would exceed 16384.
+//      (On the 1024^3 shell workload, 4 x 4 blocks left the fused kernel
+//      1.8 % faster than 16 x 16 ones, 8 x 8 1.4 %; 32 x 32 1.2 % slower: a
+//      128-token tile covers about 13 x 13 texels, and inside a block the
+//      order is arbitrary.)
 //      Counts go to LDS first, then one device atomic per bin and workgroup;
 //   3. scan_kernel: exclusive prefix sum of the counts;
 //   4. scatter_kernel: every token takes the next position of its bin. The
@@ -45,6 +49,46 @@ __device__ __forceinline__ uint32_t spread_bits(uint32_t v) {
     return v;
 }
 
+// Zero the first nbins LDS counters, rounded up to whole 16-byte vectors
+// (kMaxBins, the array's size, is a multiple of 4).
+__device__ __forceinline__ void zero_counts(uint32_t* cnt, int nbins, int tid) {
+    uint4* c4 = reinterpret_cast<uint4*>(cnt);
+    for (int i = tid; i < (nbins + 3) / 4; i += kThreads) c4[i] = make_uint4(0, 0, 0, 0);
+}
+
+// For every non-zero LDS counter c[i] (i < nbins): old = atomicAdd(&dst[i], c[i]);
+// with Return, c[i] becomes old. Sixteen counters per thread and step (four
+// runs of four), their atomics all issued before any result is used.
+template <bool Return>
+__device__ __forceinline__ void flush_counts(uint32_t* cnt, uint32_t* __restrict__ dst, int nbins,
+                                             int tid) {
+    constexpr int kPer = 16;                  // counters per thread and step
+    for (int i0 = tid * 4; i0 < nbins; i0 += kThreads * kPer) {
+        uint32_t c[kPer], r[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = i0 + (k / 4) * kThreads * 4 + (k % 4);
+            c[k] = i < nbins ? cnt[i] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = i0 + (k / 4) * kThreads * 4 + (k % 4);
+            r[k] = 0u;
+            if (c[k]) {
+                if constexpr (Return) r[k] = atomicAdd(&dst[i], c[k]);
+                else atomicAdd(&dst[i], c[k]);
+            }
+        }
+        if constexpr (Return) {
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int i = i0 + (k / 4) * kThreads * 4 + (k % 4);
+                if (c[k]) cnt[i] = r[k];
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void clear_kernel(uint32_t* __restrict__ hist,
                                                          int32_t nbins) {
     const int i = blockIdx.x * kThreads + threadIdx.x;
@@ -54,9 +98,9 @@ __global__ __launch_bounds__(kThreads) void clear_kernel(uint32_t* __restrict__ 
 // Workgroup w bins tokens [kBinTokens w, kBinTokens (w + 1)).
 __global__ __launch_bounds__(kThreads) void bin_kernel(OrderArgs a, CamTable cams,
                                                        OrderBufs ob) {
-    __shared__ uint32_t cnt[kMaxBins];
+    __shared__ __align__(16) uint32_t cnt[kMaxBins];
     const int tid = threadIdx.x;
-    for (int i = tid; i < ob.nbins; i += kThreads) cnt[i] = 0;
+    zero_counts(cnt, ob.nbins, tid);
     __syncthreads();
     const int64_t t0 = (int64_t)blockIdx.x * kBinTokens;
     for (int i = tid; i < kBinTokens; i += kThreads) {
@@ -74,32 +118,66 @@ __global__ __launch_bounds__(kThreads) void bin_kernel(OrderArgs a, CamTable cam
         atomicAdd(&cnt[bin], 1u);
     }
     __syncthreads();
-    for (int i = tid; i < ob.nbins; i += kThreads)
-        if (cnt[i]) atomicAdd(&ob.hist[i], cnt[i]);
+    flush_counts<false>(cnt, ob.hist, ob.nbins, tid);
 }
 
-// Exclusive prefix sum of hist[0, nbins) into cursor, in one workgroup:
-// thread i sums its run of nbins / kScanThreads counts, the run totals are
-// scanned in LDS, then each thread writes its run's prefixes.
+// Exclusive prefix sum of hist[0, nbins) into cursor, in one workgroup. The
+// counts are taken as rows of kScanThreads (row r: bins r kScanThreads ..):
+// every thread loads its column of all rows first (coalesced, all loads in
+// flight together: one workgroup alone is latency-bound), then each row is
+// scanned across the workgroup (wave scans with shuffles, then the wave
+// totals) and offset by the total of the rows before it.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(OrderBufs ob) {
-    __shared__ uint32_t part[kScanThreads];
-    const int tid = threadIdx.x;
-    const int per = (ob.nbins + kScanThreads - 1) / kScanThreads;
-    const int lo = tid * per, hi = min(lo + per, ob.nbins);
-    uint32_t sum = 0;
-    for (int i = lo; i < hi; ++i) sum += ob.hist[i];
-    part[tid] = sum;
-    __syncthreads();
-    for (int d = 1; d < kScanThreads; d <<= 1) {     // inclusive Hillis-Steele scan
-        const uint32_t v = tid >= d ? part[tid - d] : 0u;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
+    constexpr int kRows = kMaxBins / kScanThreads;
+    constexpr int kWaves = kScanThreads / 64;
+    __shared__ uint32_t wsum[kRows][kWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t c[kRows], v[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int i = r * kScanThreads + tid;
+        c[r] = i < ob.nbins ? ob.hist[i] : 0u;
     }
-    uint32_t run = part[tid] - sum;
-    for (int i = lo; i < hi; ++i) {
-        ob.cursor[i] = run;
-        run += ob.hist[i];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        v[r] = c[r];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {           // inclusive scan in the wave
+            const uint32_t u = __shfl_up(v[r], d);
+            if (lane >= d) v[r] += u;
+        }
+        if (lane == 63) wsum[r][wave] = v[r];
+    }
+    __syncthreads();
+    // wave 0: exclusive scan of the kRows x kWaves totals in (row, wave)
+    // order, four per lane, back into wsum
+    static_assert(kRows * kWaves == 4 * 64, "four totals per lane");
+    if (wave == 0) {
+        uint32_t* flat = &wsum[0][0];
+        uint32_t t[4], sum = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            t[k] = flat[4 * lane + k];
+            sum += t[k];
+        }
+        uint32_t incl = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t u = __shfl_up(incl, d);
+            if (lane >= d) incl += u;
+        }
+        uint32_t run = incl - sum;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            flat[4 * lane + k] = run;
+            run += t[k];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int i = r * kScanThreads + tid;
+        if (i < ob.nbins) ob.cursor[i] = wsum[r][wave] + v[r] - c[r];
     }
 }
 
@@ -108,10 +186,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(OrderBufs ob) {
 // positions, then every token lands at run start + rank.
 __global__ __launch_bounds__(kThreads) void scatter_kernel(int64_t n, OrderBufs ob,
                                                            int32_t* __restrict__ order) {
-    __shared__ uint32_t cnt[kMaxBins];
+    __shared__ __align__(16) uint32_t cnt[kMaxBins];
     constexpr int PER = kBinTokens / kThreads;
     const int tid = threadIdx.x;
-    for (int i = tid; i < ob.nbins; i += kThreads) cnt[i] = 0;
+    zero_counts(cnt, ob.nbins, tid);
     __syncthreads();
     const int64_t t0 = (int64_t)blockIdx.x * kBinTokens;
     uint32_t bin[PER], rank[PER];
@@ -122,8 +200,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(int64_t n, OrderBufs 
         rank[r] = t < n ? atomicAdd(&cnt[bin[r]], 1u) : 0u;
     }
     __syncthreads();
-    for (int i = tid; i < ob.nbins; i += kThreads)
-        if (cnt[i]) cnt[i] = atomicAdd(&ob.cursor[i], cnt[i]);
+    flush_counts<true>(cnt, ob.cursor, ob.nbins, tid);
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
@@ -141,10 +218,10 @@ size_t order_layout(int64_t n, int32_t batch, int32_t kH, int32_t kW, void* base
     OrderBufs o{};
     o.kH = kH;
     o.kW = kW;
-    // 16 x 16-texel blocks, coarser until batch * P^2 <= kMaxBins (P: blocks
+    // 4 x 4-texel blocks, coarser until batch * P^2 <= kMaxBins (P: blocks
     // per axis, rounded up to a power of 2 for the Morton index)
     const int32_t side = kH > kW ? kH : kW;
-    for (o.shift = 4;; ++o.shift) {
+    for (o.shift = 2;; ++o.shift) {
         int64_t P = 1;
         while (P * ((int64_t)1 << o.shift) < side) P <<= 1;
         if ((int64_t)batch * P * P <= kMaxBins || o.shift >= 30) {

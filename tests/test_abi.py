@@ -387,9 +387,10 @@ def test_token_order_workspace_size(p3d):
     lib = p3d.lib
     size = lib.p3d_token_order_workspace_size(100000, 1, 512, 512)
     assert size % 256 == 0 and 400000 <= size <= 400128 + 2 * 4 * 16384 + 2 * 256, size
-    # 32 x 32 blocks of 16 texels per 512 x 512 item: 1024 bins per item, up
-    # to 16 items; 32 items take 32-texel blocks (256 bins each)
-    assert size == 400128 + 2 * 4 * 1024
+    # 128 x 128 blocks of 4 texels per 512 x 512 item: 16384 bins for one
+    # item; 16 items take 16-texel blocks (1024 bins each), 32 items
+    # 32-texel blocks (256 bins each)
+    assert size == 400128 + 2 * 4 * 16384
     assert lib.p3d_token_order_workspace_size(100000, 16, 512, 512) == 400128 + 2 * 4 * 16384
     assert lib.p3d_token_order_workspace_size(100000, 32, 512, 512) == 400128 + 2 * 4 * 8192
     for args in [(-1, 1, 8, 8), (10, 0, 8, 8), (10, 1, 0, 8), (10, 1, 8, 0)]:

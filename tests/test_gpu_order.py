@@ -40,10 +40,10 @@ def orc():
 
 def _blocks(batch, kH, kW):
     """Block side (log2 texels) and blocks per item of the documented rule:
-    16-texel blocks, coarser until batch * P^2 <= 16384, P the blocks per
+    4-texel blocks, coarser until batch * P^2 <= 16384, P the blocks per
     axis rounded up to a power of two."""
     side = max(kH, kW)
-    shift = 4
+    shift = 2
     while True:
         P = 1
         while P * (1 << shift) < side:

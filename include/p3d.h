@@ -111,6 +111,17 @@ const char* p3d_status_string(p3d_status s);
 /* Message of this thread's last failed call ("" if none). */
 const char* p3d_last_error(void);
 
+/* p3d_stream_copy -- copy `bytes` from src to dst on the device with
+ * 16-byte non-temporal loads and stores: the achievable HBM rate (read plus
+ * write) that measurements set beside the datasheet bandwidth. Not a step of
+ * the method.
+ *   src, dst  DEVICE pointers, 16-byte aligned, not overlapping
+ *   bytes     a multiple of 16 (0 enqueues nothing)
+ *   stream    hipStream_t, NULL = default stream
+ * P3D_ERR_INVALID_ARG for NULL pointers with bytes > 0, P3D_ERR_UNSUPPORTED
+ * for misalignment or a size that is not a multiple of 16. */
+p3d_status p3d_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 /* Closed-form camera distance (pixal3d.cpp camera solve; extend_pixel worked
  * example: 49.13 deg on a 512 px frame gives 1.094 / 0.875 / 0.729 for
  * extend_px = 0 / 64 / 128). The distance puts the corner of the unit cube's

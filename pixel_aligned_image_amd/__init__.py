@@ -22,7 +22,7 @@ __all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_versi
            "p3d_requantize_coords", "p3d_projection_stats", "p3d_stats_figures",
            "p3d_proj_sample", "p3d_proj_linear_grouped", "P3D_MAX_GROUPS",
            "p3d_proj_cond_workspace_size", "proj_cond_workspace", "P3D_NOALLOC_MAX_TOKENS",
-           "p3d_token_order", "p3d_token_order_workspace_size",
+           "p3d_token_order", "p3d_token_order_workspace_size", "p3d_stream_copy",
            "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
 
 # P3D_LIB names another build of the same sources (the sanitizer run of the
@@ -111,6 +111,8 @@ def _load():
     L.p3d_proj_cond_ordered.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
                                         ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp,
                                         vp, vp, vp]
+    L.p3d_stream_copy.restype = ctypes.c_int
+    L.p3d_stream_copy.argtypes = [vp, vp, i64, vp]
     L.p3d_token_order_workspace_size.restype = ctypes.c_size_t
     L.p3d_token_order_workspace_size.argtypes = [i64, i32, i32, i32]
     L.p3d_token_order.restype = ctypes.c_int
@@ -439,6 +441,16 @@ def p3d_proj_sample(coords, n, resolution, cams, feat, S, mask=None, points="cel
                                        len(feats), _dev(order, "order", torch.int32, (n,)),
                                        _dev(S, "S", feats[0].dtype, (n, K)),
                                        _dev(mask, "mask", torch.uint8, (n,)), _stream(stream)))
+
+
+def p3d_stream_copy(src, dst, stream=None):
+    """Enqueue p3d_stream_copy: dst[:] = src[:] (contiguous device tensors of
+    equal byte size, a multiple of 16); a measurement helper, not a step of
+    the method."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    _check(lib.p3d_stream_copy(_dev(src, "src"), _dev(dst, "dst"), nbytes, _stream(stream)))
 
 
 def p3d_token_order_workspace_size(n, batch, key_height, key_width):

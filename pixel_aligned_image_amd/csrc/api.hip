@@ -297,6 +297,22 @@ extern "C" {
 
 const char* p3d_version(void) { return "p3d 1.0.0 gfx950"; }
 
+p3d_status p3d_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    const char* fn = "p3d_stream_copy";
+    if (bytes < 0) return fail(P3D_ERR_INVALID_ARG, "%s: bytes must be >= 0, got %lld", fn,
+                               (long long)bytes);
+    if (bytes % 16)
+        return fail(P3D_ERR_UNSUPPORTED, "%s: bytes must be a multiple of 16, got %lld", fn,
+                    (long long)bytes);
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(P3D_ERR_INVALID_ARG, "%s: src and dst must be non-NULL", fn);
+    if (!aligned(src, 16) || !aligned(dst, 16))
+        return fail(P3D_ERR_UNSUPPORTED, "%s: src and dst must be 16-byte aligned", fn);
+    hipError_t e = launch_stream_copy(src, dst, bytes / 16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+}
+
 const char* p3d_status_string(p3d_status s) {
     switch (s) {
         case P3D_OK: return "P3D_OK";

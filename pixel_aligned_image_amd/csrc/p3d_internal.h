@@ -264,6 +264,7 @@ hipError_t launch_order(const OrderArgs& a, const CamTable& cams, const OrderBuf
                         int32_t* order, hipStream_t s);
 
 hipError_t launch_project(const ProjectArgs& a, const CamTable& cams, hipStream_t s);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t vectors, hipStream_t s);
 hipError_t launch_grouped(const GroupedArgs& a, bool accumulate, hipStream_t s);
 hipError_t launch_stats(const StatsArgs& a, bool bf16, const CamTable& cams, hipStream_t s);
 hipError_t launch_requantize(const RequantArgs& a, hipStream_t s);

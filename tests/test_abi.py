@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(p3d):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     lib = ctypes.CDLL(p3d.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -454,3 +454,14 @@ def test_proj_cond_ordered_validation(p3d):
     assert lib.p3d_proj_cond_ordered(*bad, 4096, None) == p3d.P3D_ERR_SHAPE
     assert lib.p3d_proj_cond_ordered(None, 0, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 16,
                                      None, 0, 8192, None, None, None) == p3d.P3D_OK
+
+
+def test_stream_copy_validation(p3d):
+    lib = p3d.lib
+    assert lib.p3d_stream_copy(None, None, 0, None) == p3d.P3D_OK
+    assert lib.p3d_stream_copy(4096, 8192, -16, None) == p3d.P3D_ERR_INVALID_ARG
+    assert lib.p3d_stream_copy(4096, 8192, 24, None) == p3d.P3D_ERR_UNSUPPORTED
+    assert "multiple of 16" in p3d.p3d_last_error()
+    assert lib.p3d_stream_copy(None, 8192, 32, None) == p3d.P3D_ERR_INVALID_ARG
+    assert lib.p3d_stream_copy(4100, 8192, 32, None) == p3d.P3D_ERR_UNSUPPORTED
+    assert p3d.p3d_last_error().startswith("p3d_stream_copy")

@@ -88,6 +88,8 @@ def _calls(x):
     ys = [torch.zeros((n, x["D"]), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     Wk = to_dev(synth.bf16_bits(np.full((x["D"], x["C"] + 128), 0.01, np.float32)), True)
     bidx = x["coords"][:, 0].contiguous()
+    big = torch.zeros((8 << 20,), dtype=torch.int32, device="cuda")
+    big2 = torch.empty_like(big)
     feat, W, coords = x["feat"], x["W"], x["coords"]
     return {
         "p3d_project_points": lambda: p3d.p3d_project_points(coords, n, R, cams, 32, 32,
@@ -111,12 +113,14 @@ def _calls(x):
                                                        order=order),
         "p3d_proj_linear_grouped": lambda: p3d.p3d_proj_linear_grouped(S, [Wk, Wk], ys,
                                                                        accumulate=True),
+        "p3d_stream_copy": lambda: p3d.p3d_stream_copy(big, big2),
     }
 
 
 CALLS = ["p3d_project_points", "p3d_requantize_coords", "p3d_bilinear_sample", "p3d_proj_cond",
          "p3d_proj_cond_ws", "p3d_proj_cond_noalloc", "p3d_token_order", "p3d_proj_cond_ordered",
-         "p3d_projection_stats", "p3d_proj_sample", "p3d_proj_linear_grouped"]
+         "p3d_projection_stats", "p3d_proj_sample", "p3d_proj_linear_grouped",
+         "p3d_stream_copy"]
 
 
 @pytest.mark.parametrize("name", CALLS)
@@ -147,3 +151,17 @@ def test_ordered_results_after_spin(spin_cycles, inputs):
     torch.cuda.synchronize()
     assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
     del calls
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 16, 64 << 20])
+def test_stream_copy_exact(nbytes):
+    """p3d_stream_copy writes exactly the source bytes (ragged grids and a
+    large copy), and nothing past the end."""
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    n = nbytes // 4
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda", generator=g)
+    dst = torch.full((n + 8,), 7, dtype=torch.int32, device="cuda")
+    p3d.p3d_stream_copy(src, dst[:n])
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src)
+    assert torch.all(dst[n:] == 7)

@@ -24,9 +24,10 @@ Prints ONE JSON line. Fields beyond the common ones:
   order_ms          the token order's share of the step (events likewise).
   cpu_baseline      the CPU oracle on a bounded prefix of the same tokens, on
                     every core of the affinity mask and on one thread.
-  gather            the standalone bilinear gather on the same points:
-                    algorithmic bytes / duration against peak HBM bandwidth
-                    and against the measured copy ceiling.
+  gather            the standalone bilinear gather on the same points (in
+                    the step's token order): algorithmic bytes / duration
+                    against peak HBM bandwidth and against the measured copy
+                    ceiling.
   hbm_copy_ceiling  a streaming device copy (p3d_stream_copy, 16-byte
                     non-temporal loads and stores): the achievable read plus
                     write HBM rate; the runtime's own copy beside it.
@@ -311,10 +312,11 @@ EXTRAS = ("configs", "unordered", "cascade", "two_maps", "gemm_reference")
 
 
 def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
-              headline_flops=None):
+              headline_flops=None, plain_gather=None):
     """Adjacent parts on their own workloads (the names in `which`):
       configs        the fused call on every other workload, own roofline;
-      unordered      the headline's fused kernel without the token order;
+      unordered      the headline's fused kernel and standalone gather without
+                     the token order;
       cascade        requantization of a res-512 shell onto the 64-node grid,
                      and the fused kernel on those grid nodes;
       two_maps       the fused kernel over two concatenated maps, the
@@ -343,6 +345,13 @@ def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
                             "frac": headline_flops / (ums * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                             "note": "the headline's fused call without the token order "
                                     "(p3d_proj_cond): tokens in the caller's (x, y, z) order"}
+        if plain_gather is not None:
+            g, gbytes = plain_gather
+            for _ in range(reps):
+                g()
+            gms = time_events(g, reps, stream)
+            out["unordered"]["gather_ms"] = gms
+            out["unordered"]["gather_frac"] = gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS
     if "configs" in which:
         out["configs"] = [config_line(p3d, synth, w.name, stream, reps)
                           for w in synth.WORKLOADS if w.name != DEFAULT_WORKLOAD]
@@ -655,7 +664,14 @@ def main():
     bidx = dev(bidx_np)
     s_out = torch.empty((n, w.channels), dtype=dt, device="cuda")
 
+    # the standalone gather at the same points, in the step's token order
+    # when there is one (p3d_bilinear_sample_ordered; the plain call is timed
+    # with the adjacent parts)
     def gather_only():
+        p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx,
+                                order=order if ordered else None)
+
+    def gather_plain():
         p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx)
 
     for _ in range(reps):
@@ -753,6 +769,8 @@ def main():
                    "frac": gather_gbs / HBM_PEAK_GBS,
                    "frac_of_copy_ceiling": gather_gbs / copy["achieved"],
                    "kernel": "sample_kernel", "mean_ms": gather_ms,
+                   "call": ("p3d_bilinear_sample_ordered (the step's token order)" if ordered
+                            else "p3d_bilinear_sample"),
                    "traffic": recorded_traffic("sample_kernel", w.name),
                    "algorithmic_bytes_per_launch": gather_bytes},
         "hbm_copy_ceiling": copy,
@@ -764,7 +782,8 @@ def main():
     }
     if not args.no_extra:
         line["extra"] = run_extra(p3d, synth, stream, reps, step, which,
-                                  unordered_step if ordered else None, flops)
+                                  unordered_step if ordered else None, flops,
+                                  (gather_plain, gather_bytes) if ordered else None)
     if not args.no_cpu_baseline:
         import oracle
         o = oracle.get()

@@ -198,6 +198,21 @@ p3d_status p3d_bilinear_sample(const void* feat, p3d_dtype feat_dtype,
                                const float* grid, const int32_t* batch_index, int64_t n,
                                void* out, p3d_dtype out_dtype, void* stream);
 
+/* p3d_bilinear_sample_ordered -- p3d_bilinear_sample processing the points in
+ * the order `order` (DEVICE int32 [n], 4-byte aligned: p3d_token_order's
+ * output when the points are projected tokens, or any permutation of
+ * [0, n); NULL = the natural order). Row p of out still belongs to point p,
+ * so the call writes the same bytes as p3d_bilinear_sample; points that
+ * share corner rows are sampled together. An entry outside [0, n) breaks the
+ * contract: it is clamped into [0, n), so nothing outside the arrays is
+ * touched, and which rows are written is unspecified. */
+p3d_status p3d_bilinear_sample_ordered(const void* feat, p3d_dtype feat_dtype,
+                                       int32_t batch, int32_t height, int32_t width,
+                                       int32_t channels, const float* grid,
+                                       const int32_t* batch_index, int64_t n,
+                                       const int32_t* order, void* out, p3d_dtype out_dtype,
+                                       void* stream);
+
 /* ------------------------------------------------------------------------
  * p3d_proj_cond -- the whole path, fused (pixal3d.cpp commit: grid
  * projection and ProjCond; FlowCond commit: proj_linear and the null proj

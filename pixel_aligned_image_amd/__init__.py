@@ -79,6 +79,9 @@ def _load():
     L.p3d_bilinear_sample.restype = ctypes.c_int
     L.p3d_bilinear_sample.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, vp, vp, i64, vp,
                                       ctypes.c_int, vp]
+    L.p3d_bilinear_sample_ordered.restype = ctypes.c_int
+    L.p3d_bilinear_sample_ordered.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, vp, vp, i64,
+                                              vp, vp, ctypes.c_int, vp]
     L.p3d_proj_cond.restype = ctypes.c_int
     L.p3d_proj_cond.argtypes = [vp, i64, i32, cam_p, i32, vp, ctypes.c_int, i32, i32, i32,
                                 vp, i32, i32, vp, i64, vp, vp, vp]
@@ -246,8 +249,9 @@ def p3d_requantize_coords(src, src_resolution, grid, dst, mode="round_nodes", st
                                      _dev(dst, "dst", torch.int32, (n, 4)), _stream(stream)))
 
 
-def p3d_bilinear_sample(feat, grid, out, batch_index=None, stream=None):
-    """Enqueue p3d_bilinear_sample. feat: [B, H, W, C] float32/bfloat16;
+def p3d_bilinear_sample(feat, grid, out, batch_index=None, stream=None, order=None):
+    """Enqueue p3d_bilinear_sample (p3d_bilinear_sample_ordered with an
+    order, int32 [n] device tensor). feat: [B, H, W, C] float32/bfloat16;
     grid: float32 [n, 2]; out: [n, C] float32 (any map) or bfloat16 (bf16
     map); batch_index: int32 [n] or None."""
     if feat.dim() != 4:
@@ -258,10 +262,11 @@ def p3d_bilinear_sample(feat, grid, out, batch_index=None, stream=None):
     odt = _DT.get(out.dtype)
     if fdt is None or odt is None:
         raise TypeError("feat/out must be float32 or bfloat16")
-    _check(lib.p3d_bilinear_sample(
+    _check(lib.p3d_bilinear_sample_ordered(
         _dev(feat, "feat"), fdt, B, H, W, C, _dev(grid, "grid", torch.float32, (n, 2)),
         _dev(batch_index, "batch_index", torch.int32, (n,)), n,
-        _dev(out, "out", None, (n, C)), odt, _stream(stream)))
+        _dev(order, "order", torch.int32, (n,)), _dev(out, "out", None, (n, C)), odt,
+        _stream(stream)))
 
 
 def _map_array(feats):

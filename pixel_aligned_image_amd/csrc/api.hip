@@ -419,11 +419,13 @@ p3d_status p3d_requantize_coords(const int32_t* src, int64_t n, int32_t src_reso
     return ok();
 }
 
-p3d_status p3d_bilinear_sample(const void* feat, p3d_dtype feat_dtype, int32_t batch,
-                               int32_t height, int32_t width, int32_t channels,
-                               const float* grid, const int32_t* batch_index, int64_t n,
-                               void* out, p3d_dtype out_dtype, void* stream) {
-    const char* fn = "p3d_bilinear_sample";
+p3d_status p3d_bilinear_sample_ordered(const void* feat, p3d_dtype feat_dtype, int32_t batch,
+                                       int32_t height, int32_t width, int32_t channels,
+                                       const float* grid, const int32_t* batch_index, int64_t n,
+                                       const int32_t* order, void* out, p3d_dtype out_dtype,
+                                       void* stream) {
+    const char* fn = order ? "p3d_bilinear_sample_ordered" : "p3d_bilinear_sample";
+    if (!aligned(order, 4)) return fail(P3D_ERR_UNSUPPORTED, "%s: order must be 4-byte aligned", fn);
     if (n < 0) return fail(P3D_ERR_INVALID_ARG, "%s: n must be >= 0, got %lld", fn, (long long)n);
     if (n > kMaxTokens)
         return fail(P3D_ERR_UNSUPPORTED, "%s: n must be <= %lld, got %lld", fn,
@@ -465,11 +467,20 @@ p3d_status p3d_bilinear_sample(const void* feat, p3d_dtype feat_dtype, int32_t b
     a.n = n;
     a.out = out;
     a.out_stride = channels;
+    a.order = order;
     static const CamTable no_cams{};
     hipError_t e = launch_sample(a, feat_dtype, out_dtype, no_cams,
                                  static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return ok();
+}
+
+p3d_status p3d_bilinear_sample(const void* feat, p3d_dtype feat_dtype, int32_t batch,
+                               int32_t height, int32_t width, int32_t channels,
+                               const float* grid, const int32_t* batch_index, int64_t n,
+                               void* out, p3d_dtype out_dtype, void* stream) {
+    return p3d_bilinear_sample_ordered(feat, feat_dtype, batch, height, width, channels, grid,
+                                       batch_index, n, nullptr, out, out_dtype, stream);
 }
 
 p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution,

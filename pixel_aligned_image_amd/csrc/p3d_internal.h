@@ -190,7 +190,7 @@ struct SampleArgs {
     int64_t out_stride;           // elements per output row
     int32_t out_col;
     uint8_t* mask;                // project mode: in-image mask, or NULL
-    const int32_t* order;         // project mode: token of each position, or NULL
+    const int32_t* order;         // point (token) of each position, or NULL
     const void* feat1;            // project mode: a second map [batch, H1, W1, C1]
     int32_t H1, W1, C1;           // (C1 == 0: none); its samples follow map 0's
 };

@@ -119,9 +119,10 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a, CamTable
             b = p.b;
             if (a.mask && slice_all == 0) a.mask[tk] = p.mask;
         } else {
-            s_out[threadIdx.x] = t;
-            gp = reinterpret_cast<const float2*>(a.grid)[t];
-            b = a.bidx ? a.bidx[t] : 0;
+            const int64_t tk = ordered_token(a.order, t, a.n);
+            s_out[threadIdx.x] = tk;
+            gp = reinterpret_cast<const float2*>(a.grid)[tk];
+            b = a.bidx ? a.bidx[tk] : 0;
             b = b < 0 ? 0 : (b >= a.batch ? a.batch - 1 : b);
         }
         const Corners c = corners_of(gp.x, gp.y, b, H, W);

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(p3d):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     lib = ctypes.CDLL(p3d.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -465,3 +465,14 @@ def test_stream_copy_validation(p3d):
     assert lib.p3d_stream_copy(None, 8192, 32, None) == p3d.P3D_ERR_INVALID_ARG
     assert lib.p3d_stream_copy(4100, 8192, 32, None) == p3d.P3D_ERR_UNSUPPORTED
     assert p3d.p3d_last_error().startswith("p3d_stream_copy")
+
+
+def test_bilinear_sample_ordered_validation(p3d):
+    lib = p3d.lib
+    st = lib.p3d_bilinear_sample_ordered(4096, p3d.P3D_BF16, 1, 8, 8, 16, 4096, None, 10, 4098,
+                                         8192, p3d.P3D_BF16, None)
+    assert st == p3d.P3D_ERR_UNSUPPORTED
+    assert p3d.p3d_last_error().startswith("p3d_bilinear_sample_ordered")
+    st = lib.p3d_bilinear_sample_ordered(4096, p3d.P3D_BF16, 1, 8, 8, 12, 4096, None, 10, 4096,
+                                         8192, p3d.P3D_BF16, None)
+    assert st == p3d.P3D_ERR_UNSUPPORTED and "multiple of 8" in p3d.p3d_last_error()

@@ -301,3 +301,59 @@ def test_proj_cond_ordered_workload():
     order = _order(to_dev(coords), n, w.resolution, cams, w.batch, w.height, w.width, w.points)
     say(w.name, n, "tokens +", w.n_null, "null rows")
     _fused_pair(coords, n, w.resolution, cams, feat, weight, None, w.n_null, order, w.points)
+
+
+GATHER_CASES = [
+    dict(name="bf16_to_bf16", R=48, B=2, n=3001, H=24, W=40, C=256, out="bf16"),
+    dict(name="bf16_to_f32_one_item", R=33, B=1, n=1025, H=17, W=13, C=72, out="f32"),
+    dict(name="f32_to_f32", R=20, B=3, n=700, H=9, W=30, C=36, out="f32"),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c["name"] for c in GATHER_CASES])
+def test_ordered_bilinear_sample_bitwise(case):
+    """p3d_bilinear_sample_ordered at the tokens' projected points, with the
+    token order and with a random permutation, writes the bytes of
+    p3d_bilinear_sample."""
+    say(case)
+    rng = np.random.default_rng(len(case["name"]) + 11)
+    B, n, R, H, W, C = case["B"], case["n"], case["R"], case["H"], case["W"], case["C"]
+    coords = synth.random_coords(R, B, n, seed=n + 1, spill=2)
+    featf = rng.standard_normal((B, H, W, C)).astype(np.float32)
+    bf_in = case["name"].startswith("bf16")
+    feat = to_dev(synth.bf16_bits(featf), True) if bf_in else to_dev(featf)
+    odt = torch.bfloat16 if case["out"] == "bf16" else torch.float32
+    cams = product_cameras(p3d, [40.0 + 3 * b for b in range(B)], [None] * B, W)
+    cd = to_dev(coords)
+    grid = torch.empty((n, 2), device="cuda")
+    p3d.p3d_project_points(cd, n, R, cams, H, W, grid=grid)
+    bidx = to_dev(coords[:, 0].copy())
+    order = _order(cd, n, R, cams, B, H, W)
+    ref = torch.full((n, C), float("nan"), dtype=odt, device="cuda")
+    p3d.p3d_bilinear_sample(feat, grid, ref, batch_index=bidx)
+    iv = torch.int16 if odt == torch.bfloat16 else torch.int32
+    for o in (order, torch.from_numpy(rng.permutation(n).astype(np.int32)).cuda()):
+        got = torch.full_like(ref, float("nan"))
+        p3d.p3d_bilinear_sample(feat, grid, got, batch_index=bidx, order=o)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(iv), ref.view(iv))
+
+
+def test_ordered_bilinear_sample_workload():
+    w = synth.workload("shell1024_cfg_bf16_c2048_d1536")
+    coords = synth.coords(w)
+    n = w.n_tokens
+    feat = to_dev(synth.feature_map(w), True)
+    cams = product_cameras(p3d, synth.fovs(w), [None] * w.batch, w.width)
+    cd = to_dev(coords)
+    grid = torch.empty((n, 2), device="cuda")
+    p3d.p3d_project_points(cd, n, w.resolution, cams, w.height, w.width, grid=grid)
+    bidx = to_dev(coords[:, 0].copy())
+    order = _order(cd, n, w.resolution, cams, w.batch, w.height, w.width)
+    ref = torch.empty((n, w.channels), dtype=torch.bfloat16, device="cuda")
+    got = torch.full_like(ref, float("nan"))
+    p3d.p3d_bilinear_sample(feat, grid, ref, batch_index=bidx)
+    p3d.p3d_bilinear_sample(feat, grid, got, batch_index=bidx, order=order)
+    torch.cuda.synchronize()
+    say(w.name, "ordered gather of", n, "points")
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))

@@ -24,10 +24,9 @@ Prints ONE JSON line. Fields beyond the common ones:
   order_ms          the token order's share of the step (events likewise).
   cpu_baseline      the CPU oracle on a bounded prefix of the same tokens, on
                     every core of the affinity mask and on one thread.
-  gather            the standalone bilinear gather on the same points (in
-                    the step's token order): algorithmic bytes / duration
-                    against peak HBM bandwidth and against the measured copy
-                    ceiling.
+  gather            the standalone bilinear gather on the same points:
+                    algorithmic bytes / duration against peak HBM bandwidth
+                    and against the measured copy ceiling.
   hbm_copy_ceiling  a streaming device copy (p3d_stream_copy, 16-byte
                     non-temporal loads and stores): the achievable read plus
                     write HBM rate; the runtime's own copy beside it.
@@ -308,15 +307,15 @@ def config_line(p3d, synth, name, stream, reps):
     return line
 
 
-EXTRAS = ("configs", "unordered", "cascade", "two_maps", "gemm_reference")
+EXTRAS = ("configs", "variants", "cascade", "two_maps", "gemm_reference")
 
 
 def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
-              headline_flops=None, plain_gather=None):
+              headline_flops=None, ordered_gather=None):
     """Adjacent parts on their own workloads (the names in `which`):
       configs        the fused call on every other workload, own roofline;
-      unordered      the headline's fused kernel and standalone gather without
-                     the token order;
+      variants       the headline's fused kernel without the token order, the
+                     standalone gather with it;
       cascade        requantization of a res-512 shell onto the 64-node grid,
                      and the fused kernel on those grid nodes;
       two_maps       the fused kernel over two concatenated maps, the
@@ -337,21 +336,25 @@ def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
             lead_step()
 
     out = {}
-    if "unordered" in which and unordered_step is not None:
+    if "variants" in which and unordered_step is not None:
         for _ in range(reps):
             unordered_step()
         ums = time_events(unordered_step, reps, stream)
-        out["unordered"] = {"kernel": "proj_cond_bf16_kernel", "mean_ms": ums,
-                            "frac": headline_flops / (ums * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                            "note": "the headline's fused call without the token order "
-                                    "(p3d_proj_cond): tokens in the caller's (x, y, z) order"}
-        if plain_gather is not None:
-            g, gbytes = plain_gather
+        out["unordered_fused"] = {
+            "kernel": "proj_cond_bf16_kernel", "mean_ms": ums,
+            "frac": headline_flops / (ums * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "note": "the headline's fused call without the token order (p3d_proj_cond): "
+                    "tokens in the caller's (x, y, z) order"}
+        if ordered_gather is not None:
+            g, gbytes = ordered_gather
             for _ in range(reps):
                 g()
             gms = time_events(g, reps, stream)
-            out["unordered"]["gather_ms"] = gms
-            out["unordered"]["gather_frac"] = gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS
+            out["ordered_gather"] = {
+                "kernel": "sample_kernel", "mean_ms": gms,
+                "frac": gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "note": "the standalone gather at the same points in the step's token order "
+                        "(p3d_bilinear_sample_ordered)"}
     if "configs" in which:
         out["configs"] = [config_line(p3d, synth, w.name, stream, reps)
                           for w in synth.WORKLOADS if w.name != DEFAULT_WORKLOAD]
@@ -664,15 +667,14 @@ def main():
     bidx = dev(bidx_np)
     s_out = torch.empty((n, w.channels), dtype=dt, device="cuda")
 
-    # the standalone gather at the same points, in the step's token order
-    # when there is one (p3d_bilinear_sample_ordered; the plain call is timed
-    # with the adjacent parts)
+    # the standalone gather at the same points, in the caller's order (the
+    # same points in the step's token order, p3d_bilinear_sample_ordered, are
+    # timed with the adjacent parts)
     def gather_only():
-        p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx,
-                                order=order if ordered else None)
-
-    def gather_plain():
         p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx)
+
+    def gather_ordered():
+        p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx, order=order)
 
     for _ in range(reps):
         gather_only()
@@ -769,8 +771,7 @@ def main():
                    "frac": gather_gbs / HBM_PEAK_GBS,
                    "frac_of_copy_ceiling": gather_gbs / copy["achieved"],
                    "kernel": "sample_kernel", "mean_ms": gather_ms,
-                   "call": ("p3d_bilinear_sample_ordered (the step's token order)" if ordered
-                            else "p3d_bilinear_sample"),
+                   "call": "p3d_bilinear_sample",
                    "traffic": recorded_traffic("sample_kernel", w.name),
                    "algorithmic_bytes_per_launch": gather_bytes},
         "hbm_copy_ceiling": copy,
@@ -783,7 +784,7 @@ def main():
     if not args.no_extra:
         line["extra"] = run_extra(p3d, synth, stream, reps, step, which,
                                   unordered_step if ordered else None, flops,
-                                  (gather_plain, gather_bytes) if ordered else None)
+                                  (gather_ordered, gather_bytes) if ordered else None)
     if not args.no_cpu_baseline:
         import oracle
         o = oracle.get()

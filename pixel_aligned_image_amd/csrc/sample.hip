@@ -40,10 +40,6 @@ template <bool Project>
 constexpr int unroll_items() { return Project ? 3 : 4; }
 constexpr int kSlice = 64;      // 16-byte vectors per channel slice (1 KB)
 
-struct Vec8 {
-    float v[8];
-};
-
 // One 16-byte input vector -> values (8 for bf16, 4 for f32).
 __device__ __forceinline__ void widen(const uint4& q, float* v, bool bf16) {
     if (bf16) {

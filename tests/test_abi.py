@@ -18,7 +18,7 @@ def _gpu_present():
     return torch.cuda.device_count() > 0
 
 
-pytestmark = pytest.mark.skipif(_gpu_present(), reason="host-only checks (GPU box runs parity)")
+pytestmark = pytest.mark.skipif(_gpu_present(), reason="host-only checks (with a GPU the parity tests run instead)")
 
 
 @pytest.fixture(scope="module")

@@ -307,7 +307,46 @@ def config_line(p3d, synth, name, stream, reps):
     return line
 
 
-EXTRAS = ("configs", "variants", "cascade", "two_maps", "gemm_reference")
+def channel_sweep(p3d, synth, stream, reps):
+    """The 1024^3 shell's tokens (in the token order, no null rows) through
+    the fused kernel on seeded 512 x 512 maps of 512 .. 2048 channels, D =
+    1536; the least-squares line through the mean durations gives the
+    launch's fixed cost and its time per 64-channel K chunk, and the MFMA
+    rate of that steady state."""
+    import numpy as np
+    import torch
+    w = synth.workload(DEFAULT_WORKLOAD)
+    coords = torch.from_numpy(synth.coords(w)).cuda()
+    n, D = w.n_tokens, w.out_dim
+    cams = p3d.make_cameras([p3d.p3d_make_camera(a, p3d.p3d_distance_from_fov(a, w.width, 0))
+                             for a in synth.fovs(w)])
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    order = None
+    chans, ms = [], []
+    out = torch.empty((n, D), dtype=torch.bfloat16, device="cuda")
+    for C in (512, 1024, 1536, 2048):
+        feat = torch.randn((1, w.height, w.width, C), device="cuda", generator=g).to(torch.bfloat16)
+        weight = (torch.randn((D, C), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        if order is None:
+            order, _ = make_order(p3d, coords, n, w.resolution, cams, [feat], w.points)
+        f = lambda: p3d.p3d_proj_cond(coords, n, w.resolution, cams, feat, weight, out,
+                                      order=order)
+        for _ in range(reps):
+            f()
+        chans.append(C)
+        ms.append(time_events(f, reps, stream))
+        del feat, weight
+    slope, icpt = np.polyfit(np.array(chans, float), np.array(ms), 1)
+    chunk_flops = 2.0 * n * 64 * D
+    torch.cuda.empty_cache()
+    return {"workload": w.name + " tokens, no null rows, seeded maps 512x512xC, D 1536",
+            "channels": chans, "mean_ms": ms, "fixed_ms": float(icpt),
+            "ms_per_k_chunk": float(slope * 64),
+            "steady_state_frac": chunk_flops / (slope * 64 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "fixed_share_at_2048": float(icpt / ms[-1])}
+
+
+EXTRAS = ("configs", "variants", "channel_sweep", "cascade", "two_maps", "gemm_reference")
 
 
 def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
@@ -316,6 +355,10 @@ def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
       configs        the fused call on every other workload, own roofline;
       variants       the headline's fused kernel without the token order, the
                      standalone gather with it;
+      channel_sweep  the headline's fused kernel (token order, no null rows)
+                     on maps of 512 .. 2048 channels: a line through the
+                     means splits the launch into a fixed cost (tile starts
+                     and ends) and a rate per K chunk;
       cascade        requantization of a res-512 shell onto the 64-node grid,
                      and the fused kernel on those grid nodes;
       two_maps       the fused kernel over two concatenated maps, the
@@ -358,6 +401,8 @@ def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
     if "configs" in which:
         out["configs"] = [config_line(p3d, synth, w.name, stream, reps)
                           for w in synth.WORKLOADS if w.name != DEFAULT_WORKLOAD]
+    if "channel_sweep" in which:
+        out["channel_sweep"] = channel_sweep(p3d, synth, stream, reps)
     if "cascade" in which:
         w = synth.workload("cascade512_grid64_nodes_bf16_c2048_d1536")
         src = dev(synth.coords(w))

@@ -357,3 +357,20 @@ def test_ordered_bilinear_sample_workload():
     torch.cuda.synchronize()
     say(w.name, "ordered gather of", n, "points")
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+def test_proj_cond_ordered_twomap_workload():
+    """The texture stage's two maps at full size: the fused call through the
+    token order (key map: the 512 x 512 one) writes the bytes of the
+    unordered call, null rows and mask included."""
+    w = synth.workload("shell1024_cfg_twomap_bf16_c1024x2_d1536")
+    coords = synth.coords(w)
+    n = w.n_tokens
+    feats = [to_dev(m, True) for m in synth.feature_maps(w)]
+    weight = to_dev(synth.weight(w), True)
+    cams = product_cameras(p3d, synth.fovs(w), [None] * w.batch, w.width)
+    kH = max(f.shape[1] for f in feats)
+    kW = max(f.shape[2] for f in feats)
+    order = _order(to_dev(coords), n, w.resolution, cams, w.batch, kH, kW, w.points)
+    say(w.name, n, "tokens +", w.n_null, "null rows, two maps")
+    _fused_pair(coords, n, w.resolution, cams, feats, weight, None, w.n_null, order, w.points)

@@ -355,7 +355,7 @@ p3d_status p3d_proj_cond_ex(const int32_t* coords, int64_t n, int32_t resolution
  * `mask` are identical bit for bit to p3d_proj_cond_ex's (pixel-aligned
  * head commit of pixal3d_mrp_mlx; FlowCond commit of trellis.cpp PR #38).
  * F32 calls and null-only calls run p3d_proj_cond_ex unchanged and do not
- * touch the workspace. The sort costs about 20 us on 100k tokens; a launch
+ * touch the workspace. The sort costs 20-30 us on 100k tokens; a launch
  * whose tiles (128 tokens x 512 features) fit one round on the device gains
  * less than that (7000 tokens on 256 compute units: 5 us), and is better
  * served by p3d_proj_cond_ex.

@@ -170,7 +170,7 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[FJ][TIt], int la
                                            const uint16_t* bias16, void* out,
                                            uint4* __restrict__ sW0, uint4* __restrict__ sW1,
                                            const int32_t* rows = nullptr) {
-    constexpr int BATCH = TIt < OLD_BATCH ? TIt : OLD_BATCH;
+    constexpr int BATCH = TIt % OLD_BATCH == 0 ? OLD_BATCH : (TIt % 2 == 0 ? 2 : 1);
     static_assert(TIt % BATCH == 0, "residual batches");
     const int fbase = n0 + cw * WN;
     const int dv = D >> 3;                            // 16-byte vectors per output row

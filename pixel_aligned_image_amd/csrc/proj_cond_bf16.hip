@@ -63,7 +63,9 @@
 // each of them runs as four 32-token parts (the same code with two token
 // blocks per consumer and one gathered vector per producer thread), else,
 // when they fit twice over, as two 64-token parts (four token blocks, two
-// vectors); the parts are queued after every whole tile.
+// vectors); the parts are queued after every whole tile. A launch of fewer
+// tiles than CUs that neither split fits runs as 96-token tiles when those
+// still fit one round.
 #include <atomic>
 #include <type_traits>
 
@@ -79,6 +81,10 @@ using namespace tile;
 // (TI_HALF) of a 128-token tile.
 constexpr int TI_QUARTER = 2;
 constexpr int TI_HALF = 4;
+// A launch whose 128-token tiles fill less than one round, too many to split
+// into parts: 96-token tiles throughout (TI_ROUND token blocks), when they
+// still fit one round.
+constexpr int TI_ROUND = 6;
 
 // Gathered vectors per producer thread for a tile of TIt token blocks.
 template <int TIt>
@@ -311,17 +317,19 @@ __device__ __forceinline__ void produce(Producer<TwoMaps, Off32, G>& p, NullWrit
     lds_barrier();
 }
 
-// One tile: 16 TIt tokens starting at token m0 (TIt = TI: a whole 128-token
-// tile; TIt = TI_QUARTER or TI_HALF: sub-tile `sub` of tile mt), features
-// n0 .. n0 + 511.
-// The tile also writes its share of the null rows: rows m0 - 128 mt ..
-// m0 - 128 mt + 16 TIt - 1 of every 128-row null block q = mt, mt + m_tiles,
-// ..., for the same features.
+// One tile: 16 TIt tokens starting at token m0 = MRows mt + 16 TIt sub,
+// features n0 .. n0 + 511. MRows is the height the launch numbers its token
+// tiles by: 128 (TIt = TI: a whole tile; TIt = TI_QUARTER or TI_HALF:
+// sub-tile `sub` of tile mt), or 96 for the 96-token tiles (TIt = TI_ROUND,
+// sub 0).
+// The tile also writes its share of the null rows: rows m0 - MRows mt ..
+// m0 - MRows mt + 16 TIt - 1 of every MRows-row null block q = mt,
+// mt + m_tiles, ..., for the same features.
 //
 // Kernel tags the instantiation with the kernel's part size: two kernels that
 // inline one shared instantiation of the whole tile both spill registers to
 // scratch (hipcc of ROCm 7.2), while a copy per kernel does not.
-template <bool TwoMaps, bool Off32, int TIt, int Kernel>
+template <bool TwoMaps, bool Off32, int TIt, int MRows, int Kernel>
 __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& cams,
                                          int32_t mt, int32_t nt, int sub, int32_t m_tiles,
                                          int32_t null_tiles, uint4* __restrict__ sW0,
@@ -335,8 +343,8 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
     const int wave = tid >> 6;
     const bool producer = wave >= N_CONS;
 
-    const int32_t r0 = sub * BMt;                          // first row within the 128-row tile
-    const int64_t m0 = (int64_t)mt * BM + r0;
+    const int32_t r0 = sub * BMt;                          // first row within the MRows-row tile
+    const int64_t m0 = (int64_t)mt * MRows + r0;
     const int32_t n0 = nt * BN;
     const int nk = (a.C + a.C1 + BK - 1) / BK;
     const int k1 = a.C1 > 0 ? a.C / BK : 1 << 30;     // first chunk of map 1
@@ -354,8 +362,8 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
         nw.dv = dv;
         nw.colv = (n0 >> 3) + (ptid & 63);                    // 64 vectors per 512-wide row
         nw.ipt = NULL_VEC / kProdThreads;
-        nw.row0 = a.n + (int64_t)mt * BM + r0 + (ptid >> 6);
-        nw.q_rows = (int64_t)m_tiles * BM;
+        nw.row0 = a.n + (int64_t)mt * MRows + r0 + (ptid >> 6);
+        nw.q_rows = (int64_t)m_tiles * MRows;
         nw.n_end = a.n + a.n_null;
         nw.j = 0;
         nw.total = mt < null_tiles ? ((null_tiles - 1 - mt) / m_tiles + 1) * nw.ipt : 0;
@@ -426,7 +434,10 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
         // not live yet), while the producers queue chunk 1. Vector v of the
         // chunk goes to consumer thread v % 512; a 32-token part has 256
         // vectors, so only the first four waves take one, a 64-token part
-        // one per thread.
+        // one per thread; of a 96-token tile's 768 vectors the first four
+        // waves take two, the others one (their second item is a padding
+        // token: weight 0 on row 0, stored to a tile row past the tokens,
+        // which no consumer reads).
         constexpr int NV = TIt * 16 * (BK / 8);
         constexpr int CT = N_CONS * 64;
         constexpr int GC = (NV + CT - 1) / CT;
@@ -442,7 +453,14 @@ __device__ __forceinline__ void run_tile(const ProjCondArgs& a, const CamTable& 
             c.vstride = CT;
             c.gv = tid & 7;
 #pragma unroll
-            for (int u = 0; u < GC; ++u) c.gt[u] = s_tok[c.row(u)];
+            for (int u = 0; u < GC; ++u) {
+                if constexpr (NV % CT == 0) {
+                    c.gt[u] = s_tok[c.row(u)];
+                } else {
+                    c.gt[u] = c.vfirst + u * c.vstride < NV ? s_tok[c.row(u)]
+                                                            : make_int4(0, 4, 0, 0);
+                }
+            }
             c.set_items();
             Gq<GC> gq;
             c.gather_issue(gq, 0);
@@ -487,16 +505,34 @@ __global__ __launch_bounds__(kThreads) void proj_cond_bf16_kernel(
         const int32_t tile = x * big_per_xcd + i;
         if (tile >= n_big) return;
         const int32_t mt = tile / n_tiles;
-        run_tile<TwoMaps, Off32, TI, TIp>(a, cams, mt, tile - mt * n_tiles, 0, m_tiles,
-                                          null_tiles, sW0, sW1, sA0, sA1);
+        run_tile<TwoMaps, Off32, TI, BM, TIp>(a, cams, mt, tile - mt * n_tiles, 0, m_tiles,
+                                              null_tiles, sW0, sW1, sA0, sA1);
     } else {
         const int32_t st = x * small_per_xcd + (i - big_per_xcd);
         if (st >= n_small) return;
         const int32_t tile = n_big + st / split;
         const int32_t mt = tile / n_tiles;
-        run_tile<TwoMaps, Off32, TIp, TIp>(a, cams, mt, tile - mt * n_tiles, st % split,
-                                           m_tiles, null_tiles, sW0, sW1, sA0, sA1);
+        run_tile<TwoMaps, Off32, TIp, BM, TIp>(a, cams, mt, tile - mt * n_tiles, st % split,
+                                               m_tiles, null_tiles, sW0, sW1, sA0, sA1);
     }
+}
+
+// A launch of one round of 96-token tiles: workgroup g runs on XCD x = g % 8
+// as its (g / 8)-th and takes tile x * per_xcd + g / 8 (below `tiles`),
+// numbered as above with 96-token tiles.
+template <bool TwoMaps, bool Off32>
+__global__ __launch_bounds__(kThreads) void proj_cond_bf16_round_kernel(
+    ProjCondArgs a, CamTable cams, int32_t m_tiles, int32_t n_tiles, int32_t tiles,
+    int32_t per_xcd, int32_t null_tiles) {
+    __shared__ uint4 sW0[BN * 8], sW1[BN * 8];     // 2 x 64 KB
+    __shared__ uint4 sA0[BM * 8], sA1[BM * 8];     // 2 x 16 KB
+
+    const int32_t g = blockIdx.x;
+    const int32_t tile = (g & 7) * per_xcd + (g >> 3);
+    if (tile >= tiles) return;
+    const int32_t mt = tile / n_tiles;
+    run_tile<TwoMaps, Off32, TI_ROUND, 16 * TI_ROUND, TI_ROUND>(
+        a, cams, mt, tile - mt * n_tiles, 0, m_tiles, null_tiles, sW0, sW1, sA0, sA1);
 }
 
 // Compute units of the current device (queried once per device).
@@ -524,6 +560,10 @@ int device_cus() {
 // 64-token sub-tiles (2 R <= CUs), they run as sub-tiles instead: each
 // moves the full W stream of its N tile and a quarter or half of the
 // gather, so it takes well under a whole tile's time.
+// A launch of fewer tiles than CUs that neither split fits (more than
+// CUs / 2 tiles) takes one tile's time however many CUs it leaves idle: it
+// runs as 96-token tiles when those still fit one round, each with three
+// quarters of a tile's gather and products (and the same W stream).
 hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hipStream_t s) {
     int32_t m_tiles = (int32_t)((a.n + BM - 1) / BM);
     int32_t n_tiles = (a.D + BN - 1) / BN;
@@ -533,6 +573,33 @@ hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hi
     int32_t split = 0;
     if (rem > 0 && rem * (TI / TI_QUARTER) <= cus) split = TI / TI_QUARTER;
     else if (rem > 0 && rem * (TI / TI_HALF) <= cus) split = TI / TI_HALF;
+    // corner offsets fit 32 bits when every map is under 4 GiB
+    const auto map_bytes = [&](int32_t H, int32_t W, int32_t C) {
+        return (uint64_t)a.batch * (uint64_t)H * (uint64_t)W * (uint64_t)C * 2u;
+    };
+    const bool off32 = map_bytes(a.H, a.W, a.C) < ((uint64_t)1 << 32) &&
+                       (a.C1 == 0 || map_bytes(a.H1, a.W1, a.C1) < ((uint64_t)1 << 32));
+    using yes = std::true_type;
+    using no = std::false_type;
+    constexpr int RM = 16 * TI_ROUND;
+    if (split == 0 && tiles < cus) {
+        int32_t m_r = (int32_t)((a.n + RM - 1) / RM);
+        int32_t tiles_r = m_r * n_tiles;
+        if (tiles_r <= cus) {
+            int32_t per_xcd = (tiles_r + 7) / 8;
+            int32_t null_r = (int32_t)((a.n_null + RM - 1) / RM);
+            ProjCondArgs args = a;
+            CamTable tab = cams;
+            void* params[] = {&args, &tab, &m_r, &n_tiles, &tiles_r, &per_xcd, &null_r};
+            const auto pick = [&](auto two_maps, auto o32) -> const void* {
+                constexpr bool T = decltype(two_maps)::value, O = decltype(o32)::value;
+                return reinterpret_cast<const void*>(&proj_cond_bf16_round_kernel<T, O>);
+            };
+            const void* fn = a.C1 > 0 ? (off32 ? pick(yes{}, yes{}) : pick(yes{}, no{}))
+                                      : (off32 ? pick(no{}, yes{}) : pick(no{}, no{}));
+            return hipLaunchKernel(fn, dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
+        }
+    }
     int32_t n_big = split ? tiles - rem : tiles;
     int32_t n_small = split ? rem * split : 0;
     int32_t big_per_xcd = (n_big + 7) / 8;
@@ -542,20 +609,12 @@ hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hi
     CamTable tab = cams;
     void* params[] = {&args,    &tab,        &m_tiles,       &n_tiles,   &n_big,
                       &big_per_xcd, &n_small, &small_per_xcd, &null_tiles};
-    // corner offsets fit 32 bits when every map is under 4 GiB
-    const auto map_bytes = [&](int32_t H, int32_t W, int32_t C) {
-        return (uint64_t)a.batch * (uint64_t)H * (uint64_t)W * (uint64_t)C * 2u;
-    };
-    const bool off32 = map_bytes(a.H, a.W, a.C) < ((uint64_t)1 << 32) &&
-                       (a.C1 == 0 || map_bytes(a.H1, a.W1, a.C1) < ((uint64_t)1 << 32));
     const bool half = split == TI / TI_HALF;
     const auto pick = [&](auto two_maps, auto o32) -> const void* {
         constexpr bool T = decltype(two_maps)::value, O = decltype(o32)::value;
         return half ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<T, O, TI_HALF>)
                     : reinterpret_cast<const void*>(&proj_cond_bf16_kernel<T, O, TI_QUARTER>);
     };
-    using yes = std::true_type;
-    using no = std::false_type;
     const void* fn = a.C1 > 0 ? (off32 ? pick(yes{}, yes{}) : pick(yes{}, no{}))
                               : (off32 ? pick(no{}, yes{}) : pick(no{}, no{}));
     return hipLaunchKernel(fn, dim3((unsigned)(big_per_xcd + small_per_xcd) * 8), dim3(kThreads),

@@ -213,12 +213,17 @@ def tile_edge_rows(n, D, cus, bm=128, bn=512):
     """First and last token row of every whole tile and of every tail part of
     the fused bf16 launch (128-token tiles, 512-feature N tiles; the tiles
     past the last full round on `cus` compute units run as 32- or 64-token
-    parts when four or two times that many fit one round)."""
+    parts when four or two times that many fit one round; a launch of fewer
+    tiles than CUs that neither split fits runs as 96-token tiles when those
+    fit one round)."""
     m_tiles = -(-n // bm)
     n_tiles = -(-D // bn)
     tiles = m_tiles * n_tiles
     rem = tiles % cus
     split = 4 if rem and rem * 4 <= cus else (2 if rem and rem * 2 <= cus else 1)
+    if split == 1 and tiles < cus and -(-n // 96) * n_tiles <= cus:
+        lo = np.arange(0, n, 96)
+        return np.unique(np.concatenate([lo, np.minimum(lo + 95, n - 1)]).astype(np.int64))
     rows = []
     for mt in range(m_tiles):
         first = mt * n_tiles

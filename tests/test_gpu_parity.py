@@ -275,10 +275,25 @@ SMALL = [
     # many for 32-token parts) as 64-token parts, null blocks included
     dict(name="bf16_whole_and_half_tiles", bf16=True, R=64, B=1, n=356 * 128 + 45, H=48,
          W=40, C=136, D=264, bias=True, n_null=200 * 128 + 3),
-    # 140 whole tiles (too many past a round to split), each writing two or
-    # three null blocks inside a three-chunk K loop
-    dict(name="bf16_whole_tiles_null_blocks", bf16=True, R=48, B=2, n=140 * 128 - 5, H=32,
+    # 230 whole tiles: one round, too many to split and too many for one
+    # round of 96-token tiles; each writes two or three null blocks inside a
+    # three-chunk K loop
+    dict(name="bf16_whole_tiles_null_blocks", bf16=True, R=48, B=2, n=230 * 128 - 5, H=32,
+         W=36, C=136, D=264, bias=True, n_null=80000),
+    # 140 tiles of 128 tokens (too many to split) run as one round of 187
+    # 96-token tiles, each writing two or three 96-row null blocks
+    dict(name="bf16_round_tiles_null_blocks", bf16=True, R=48, B=2, n=140 * 128 - 5, H=32,
          W=36, C=136, D=264, bias=True, n_null=50000),
+    # exactly 256 96-token tiles (192 of 128), and one token more: 257 would
+    # not fit one round, so that launch runs 193 whole tiles
+    dict(name="bf16_round_tiles_every_cu", bf16=True, R=48, B=1, n=256 * 96, H=32, W=36,
+         C=72, D=264, bias=True, n_null=300),
+    dict(name="bf16_round_tiles_one_past", bf16=True, R=48, B=1, n=256 * 96 + 1, H=32, W=36,
+         C=72, D=264, bias=True, n_null=300),
+    # two N tiles, the second ragged (features 512 .. 999): 158 tiles of 128
+    # tokens run as 210 of 96; 72 channels (one whole chunk and one vector)
+    dict(name="bf16_round_tiles_two_n", bf16=True, R=40, B=2, n=10000, H=24, W=20, C=72,
+         D=1000, bias=False, n_null=96 * 3 + 1),
     # 70 tiles as 140 64-token parts, each writing its half of two or three
     # null blocks
     dict(name="bf16_half_parts_null_blocks", bf16=True, R=48, B=2, n=70 * 128 - 5, H=32,

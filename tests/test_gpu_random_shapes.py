@@ -7,8 +7,10 @@ sizes, feature width D (not a multiple of 512, up to three 512-wide tiles),
 bias or none, cell centres or grid nodes, and a token count picked so that
 the launch runs as 32-token parts only, as whole tiles only, or as whole
 tiles plus parts; a further set draws 65 to 128 tiles past a full round, so
-that the leftover tiles run as 64-token parts. Each case is named by the
-regime its tile count takes on 256 compute units. Null rows range from none
+that the leftover tiles run as 64-token parts. A bf16 launch of fewer whole
+tiles than compute units that fits one round of 96-token tiles runs as
+those ("round96"). Each case is named by the regime its tile count takes on
+256 compute units. Null rows range from none
 to several 128-row blocks per tile. Bar as in the other fused tests: masks bit-exact, null rows equal to
 the bias bit for bit, token rows within 2e-2 (bf16) / 1e-5 (fp32), and
 every checked row written (the output starts as NaN).
@@ -85,10 +87,13 @@ def _draw_half(i):
     return c
 
 
-def _regime(T):
-    """How a launch of T tiles runs on CUS compute units."""
+def _regime(c):
+    """How a launch of T tiles (of 128 tokens) runs on CUS compute units."""
+    T = c["T"]
     rem = T % CUS
     tail = "quarters" if rem and 4 * rem <= CUS else "halves" if rem and 2 * rem <= CUS else ""
+    if c["bf16"] and not tail and T < CUS and -(-c["n"] // 96) * -(-c["D"] // 512) <= CUS:
+        return "round96"                 # one round of 96-token tiles
     whole = T - rem if tail else T
     return "+".join(x for x in (["whole"] if whole else []) + ([tail] if tail else []))
 
@@ -96,7 +101,7 @@ def _regime(T):
 CASES = [_draw(i) for i in range(40)] + [_draw_half(i) for i in range(40, 52)]
 
 
-@pytest.mark.parametrize("case", CASES, ids=["%d_%s_T%d" % (c["i"], _regime(c["T"]), c["T"])
+@pytest.mark.parametrize("case", CASES, ids=["%d_%s_T%d" % (c["i"], _regime(c), c["T"])
                                               for c in CASES])
 def test_proj_cond_random_shape(orc, case):
     say(case)
@@ -119,6 +124,7 @@ def test_proj_cond_random_shape(orc, case):
         # and a sample of the rest; null rows: the first and last blocks and
         # a sample
         edge = np.concatenate([np.arange(0, n, 128), np.arange(127, n, 128),
+                               np.arange(0, n, 96), np.arange(95, n, 96),
                                np.arange(max(0, n - 64 * 128), n)])
         pick = rng.choice(n, size=min(n, 3000), replace=False)
         nulls = np.concatenate([np.arange(n, min(n + 256, n + nn)),

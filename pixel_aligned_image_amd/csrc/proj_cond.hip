@@ -13,8 +13,11 @@
 // K chunk gathers the four corner rows of each token (16-byte vectors,
 // eight lanes per 128-byte corner segment), blends them in binary32 and
 // writes the chunk into LDS next to the matching chunk of W; the matrix
-// cores (v_mfma_f32_16x16x4_f32) accumulate in binary32. The next chunk's
-// global loads are issued before the current chunk's MFMAs. Tiles are
+// cores (v_mfma_f32_16x16x4_f32) accumulate in binary32. Eight waves, two
+// per SIMD, each own a 64 x 32 block of the 128 x 128 tile, so that one
+// wave's blend and barrier wait run under the other's MFMAs; the chunks
+// alternate between two LDS stages (one barrier per chunk), and the next
+// chunk's global loads are issued before the current chunk's MFMAs. Tiles are
 // mapped so that the D-tiles of one token tile run on the same XCD and share
 // its gathered corner rows in that XCD's L2. With a second map (NAF commit:
 // the DINOv3 map and its upsampled version, concatenated along K) the tokens
@@ -26,9 +29,10 @@ namespace p3d {
 
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves, 2 (M) x 2 (N)
+constexpr int WAVES_M = 2, WAVES_N = 4;         // 8 waves, two per SIMD
+constexpr int kThreads = 64 * WAVES_M * WAVES_N;
 constexpr int BM = 128, BN = 128, BK = 32;       // K chunk: 32 floats = 128 bytes
-constexpr int WM = BM / 2, WN = BN / 2;          // wave tile
+constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
 constexpr int MI = WM / 16, NJ = WN / 16;        // 16x16 blocks per wave
 constexpr int A_ITEMS = BM * 8 / kThreads;       // gathered vectors per thread
 constexpr int B_ITEMS = BN * 8 / kThreads;       // weight vectors per thread
@@ -57,13 +61,13 @@ __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, Cam
                                                              int32_t per_xcd) {
     __shared__ int32_t s_row[2][BM][4];    // corner rows per map
     __shared__ float s_w[2][BM][4];
-    __shared__ uint4 s_a[BM * 8];
-    __shared__ uint4 s_b[BN * 8];
+    __shared__ uint4 s_a[2][BM * 8];      // two stages: chunk kc uses stage kc % 2
+    __shared__ uint4 s_b[2][BN * 8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WAVES_M, wn = wave / WAVES_M;
 
     const int32_t g = blockIdx.x;
     const int32_t tile = (g & 7) * per_xcd + (g >> 3);
@@ -150,16 +154,19 @@ __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, Cam
             const int m = (tid + u * kThreads) >> 3;
             av[u] = blend4(qa[u], s_w[mp][m][0], s_w[mp][m][1], s_w[mp][m][2], s_w[mp][m][3]);
         }
-        __syncthreads();   // previous chunk's MFMA reads are done
+        // stage kc % 2 was last read by the MFMAs of chunk kc - 2, which
+        // every wave finished before the barrier of chunk kc - 1
+        uint4* __restrict__ sa = s_a[kc & 1];
+        uint4* __restrict__ sb = s_b[kc & 1];
 #pragma unroll
         for (int u = 0; u < A_ITEMS; ++u) {
             const int i = tid + u * kThreads;
-            s_a[swz(i >> 3, i & 7)] = av[u];
+            sa[swz(i >> 3, i & 7)] = av[u];
         }
 #pragma unroll
         for (int u = 0; u < B_ITEMS; ++u) {
             const int i = tid + u * kThreads;
-            s_b[swz(i >> 3, i & 7)] = qb[u];
+            sb[swz(i >> 3, i & 7)] = qb[u];
         }
         __syncthreads();
         if (kc + 1 < nk) issue_loads(kc + 1);
@@ -175,12 +182,12 @@ __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, Cam
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const int row = wm * WM + i * 16 + (lane & 15);
-                af[i] = __builtin_bit_cast(float4, s_a[swz(row, v)]);
+                af[i] = __builtin_bit_cast(float4, sa[swz(row, v)]);
             }
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int row = wn * WN + j * 16 + (lane & 15);
-                bfr[j] = __builtin_bit_cast(float4, s_b[swz(row, v)]);
+                bfr[j] = __builtin_bit_cast(float4, sb[swz(row, v)]);
             }
 #pragma unroll
             for (int i = 0; i < MI; ++i)
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void proj_cond_kernel(ProjCondArgs a, Cam
     }
     constexpr int STAGE_VEC = 16 * WN / 4;           // 16-byte vectors per wave stage
     constexpr int ROW_VEC = WN / 4;                  // vectors per staged row
-    float* stage = reinterpret_cast<float*>(s_a) + wave * (16 * WN);
+    float* stage = reinterpret_cast<float*>(s_a[0]) + wave * (16 * WN);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         __syncthreads();

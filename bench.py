@@ -124,12 +124,19 @@ def unique_corner_rows(pixel, bidx, H, W):
 def bf16_kernel_name(two_maps, n, D):
     """The fused bf16 kernel instantiation a launch of n tokens and D features
     runs: the last template argument is its tail part size in 16-token blocks
-    (4 when the tiles past the last full round run as 64-token parts, else 2)."""
+    (4 when the tiles past the last full round run as 64-token parts, else 2);
+    a launch of fewer tiles than CUs that neither part size fits runs as one
+    round of 96-token tiles when those fit (the round kernel)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    rem = (-(-n // 128) * -(-D // 512)) % cus
+    n_tiles = -(-D // 512)
+    tiles = -(-n // 128) * n_tiles
+    rem = tiles % cus
+    two = "true" if two_maps else "false"
+    if not (rem and 2 * rem <= cus) and tiles < cus and -(-n // 96) * n_tiles <= cus:
+        return "proj_cond_bf16_round_kernel<%s, true>" % two
     tip = 4 if rem and 4 * rem > cus and 2 * rem <= cus else 2
-    return "proj_cond_bf16_kernel<%s, true, %d>" % ("true" if two_maps else "false", tip)
+    return "proj_cond_bf16_kernel<%s, true, %d>" % (two, tip)
 
 
 def time_events(fn, reps, stream, lead=None):

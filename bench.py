@@ -121,22 +121,19 @@ def unique_corner_rows(pixel, bidx, H, W):
     return int(np.unique(rows).size)
 
 
-def bf16_kernel_name(two_maps, n, D):
+def bf16_kernel_name(p3d, two_maps, n, D):
     """The fused bf16 kernel instantiation a launch of n tokens and D features
-    runs: the last template argument is its tail part size in 16-token blocks
-    (4 when the tiles past the last full round run as 64-token parts, else 2);
-    a launch of fewer tiles than CUs that neither part size fits runs as one
-    round of 96-token tiles when those fit (the round kernel)."""
+    runs, from the library's own tiling rule (p3d_proj_cond_plan): the round
+    kernel for one round of 96-token tiles, else the kernel whose last
+    template argument is its tail part size in 16-token blocks (4 for
+    64-token parts, else 2)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    n_tiles = -(-D // 512)
-    tiles = -(-n // 128) * n_tiles
-    rem = tiles % cus
+    plan = p3d.p3d_proj_cond_plan(n, D, cus)
     two = "true" if two_maps else "false"
-    if not (rem and 2 * rem <= cus) and tiles < cus and -(-n // 96) * n_tiles <= cus:
+    if plan["tile_rows"] != 128:
         return "proj_cond_bf16_round_kernel<%s, true>" % two
-    tip = 4 if rem and 4 * rem > cus and 2 * rem <= cus else 2
-    return "proj_cond_bf16_kernel<%s, true, %d>" % (two, tip)
+    return "proj_cond_bf16_kernel<%s, true, %d>" % (two, 4 if plan["part_rows"] == 64 else 2)
 
 
 def time_events(fn, reps, stream, lead=None):
@@ -438,7 +435,7 @@ def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
             "frac": rq_bytes / (rq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "note": "100k tokens = 3.2 MB: launch-latency bound, far from the HBM roofline"}
         out["grid_nodes"] = {
-            "workload": w.name, "kernel": bf16_kernel_name(False, n, w.out_dim), "tokens": n,
+            "workload": w.name, "kernel": bf16_kernel_name(p3d, False, n, w.out_dim), "tokens": n,
             "mean_ms": nodes_ms, "bound": "mfma", "flops_per_launch": flops,
             "achieved": flops / (nodes_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": flops / (nodes_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
@@ -487,7 +484,7 @@ def run_two_maps(p3d, synth, stream, reps, which, dev):
                 f()
             res[key] = time_events(f, reps, stream)
         out["two_maps"] = {
-            "workload": w.name, "kernel": bf16_kernel_name(True, n, w.out_dim), "tokens": n,
+            "workload": w.name, "kernel": bf16_kernel_name(p3d, True, n, w.out_dim), "tokens": n,
             "null_rows": nn, "maps": ["%dx%dx%dx%d" % tuple(m.shape) for m in maps],
             "mean_ms": res["ordered"], "order_ms": order_ms, "unordered_ms": res["plain"],
             "tokens_per_s": n / ((res["ordered"] + order_ms) * 1e-3), "bound": "mfma",

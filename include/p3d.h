@@ -237,7 +237,10 @@ p3d_status p3d_bilinear_sample_ordered(const void* feat, p3d_dtype feat_dtype,
  *                           width is checked against the map's channels; a
  *                           mismatch is P3D_ERR_SHAPE naming both shapes)
  *   bias [out_dim] device, or NULL
- *   out_dim                 1 <= D <= 2^20; D % 8 == 0 (BF16) or D % 4 == 0 (F32)
+ *   out_dim                 1 <= D <= 2^20; D % 8 == 0 (BF16) or D % 4 == 0 (F32);
+ *                           the tile count ceil(n / 128) * ceil(D / 512) (BF16) or
+ *                           ceil(n / 128) * ceil(D / 128) (F32) must stay below
+ *                           2^31 (P3D_ERR_UNSUPPORTED)
  *   n_null                  >= 0 null rows appended after the n token rows
  *   out [(n + n_null), D] device; mask [n] uint8 device or NULL
  *   Alignment: feat, weight, bias and out 16-byte aligned.
@@ -547,6 +550,38 @@ p3d_status p3d_proj_cond_ordered(const int32_t* coords, int64_t n, int32_t resol
                                  const void* weight, int32_t out_dim, int32_t weight_in,
                                  const void* bias, int64_t n_null, void* out, uint8_t* mask,
                                  const int32_t* order, void* stream);
+
+/* p3d_proj_cond_plan -- how a BF16 fused call (p3d_proj_cond, _ex, _ws,
+ * _noalloc, _ordered) of n tokens and out_dim features is cut into
+ * workgroup tiles on a device of compute_units CUs; one workgroup fills a
+ * CU, so the tiles run in rounds of compute_units. Host-only, no device
+ * call; the launches use the same rule:
+ *   - whole tiles are 128 tokens x 512 features, numbered token tile major;
+ *   - when the R tiles past the last full round fit one round four times
+ *     over (4 R <= compute_units), each runs as four 32-token parts, else
+ *     when they fit twice over as two 64-token parts (parts follow the
+ *     whole tiles; a part covers rows part * part_rows of its tile);
+ *   - a launch of fewer tiles than CUs that neither split fits runs as
+ *     96-token tiles throughout when those still fit one round.
+ * The CFG null rows go with the token tiles: token tile q writes the
+ * tile_rows-row null blocks q, q + token_tiles, ...
+ *   n              tokens, 0 <= n <= 2^30 (0: no tiles)
+ *   out_dim        1 <= D <= 2^20
+ *   compute_units  >= 1
+ * P3D_ERR_INVALID_ARG for a NULL plan or a value out of range,
+ * P3D_ERR_UNSUPPORTED when ceil(n / 128) * ceil(out_dim / 512) >= 2^31 (the
+ * fused calls refuse such sizes too). */
+typedef struct p3d_tile_plan {
+    int32_t tile_rows;      /* tokens per whole tile: 128, or 96 */
+    int32_t token_tiles;    /* ceil(n / tile_rows) */
+    int32_t feature_tiles;  /* ceil(out_dim / 512) */
+    int32_t whole_tiles;    /* tiles that run whole */
+    int32_t part_rows;      /* tokens per tail part: 32, 64, or 0 (no parts) */
+    int32_t parts;          /* tail parts (4 or 2 per split tile) */
+} p3d_tile_plan;
+
+p3d_status p3d_proj_cond_plan(int64_t n, int32_t out_dim, int32_t compute_units,
+                              p3d_tile_plan* plan);
 
 /* p3d_proj_linear_grouped -- for each block g in [0, groups):
  *   accumulate == 0:  outs[g][t] = W_g S[t] + b_g

@@ -23,7 +23,7 @@ __all__ = ["P3DError", "P3D_F32", "P3D_BF16", "P3D_MAX_BATCH", "lib", "p3d_versi
            "p3d_proj_sample", "p3d_proj_linear_grouped", "P3D_MAX_GROUPS",
            "p3d_proj_cond_workspace_size", "proj_cond_workspace", "P3D_NOALLOC_MAX_TOKENS",
            "p3d_token_order", "p3d_token_order_workspace_size", "p3d_stream_copy",
-           "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
+           "p3d_proj_cond_plan", "make_cameras", "POINTS", "REQUANT", "LIB_PATH"]
 
 # P3D_LIB names another build of the same sources (the sanitizer run of the
 # host validation layer loads a host-AddressSanitizer build through it)
@@ -130,6 +130,8 @@ def _load():
                                           ctypes.POINTER(p3d_map), i32, vp, vp, vp, vp]
     L.p3d_stats_figures.restype = ctypes.c_int
     L.p3d_stats_figures.argtypes = [vp, vp, i32, vp]
+    L.p3d_proj_cond_plan.restype = ctypes.c_int
+    L.p3d_proj_cond_plan.argtypes = [i64, i32, i32, vp]
     L.p3d_proj_cond_noalloc.restype = ctypes.c_int
     L.p3d_proj_cond_noalloc.argtypes = [vp, i64, i32, ctypes.c_int, cam_p, i32, ctypes.c_int,
                                         ctypes.POINTER(p3d_map), i32, vp, i32, i32, vp, i64, vp,
@@ -415,6 +417,21 @@ def p3d_stats_figures(raw, channels):
     out = {"coverage": fig.coverage, "mean0": fig.mean[0], "std0": fig.std[0],
            "mean1": fig.mean[1], "std1": fig.std[1], "cosine": fig.cosine}
     return {k: (None if v != v else v) for k, v in out.items()}
+
+
+class p3d_tile_plan(ctypes.Structure):
+    _fields_ = [("tile_rows", ctypes.c_int32), ("token_tiles", ctypes.c_int32),
+                ("feature_tiles", ctypes.c_int32), ("whole_tiles", ctypes.c_int32),
+                ("part_rows", ctypes.c_int32), ("parts", ctypes.c_int32)]
+
+
+def p3d_proj_cond_plan(n, out_dim, compute_units):
+    """How a bf16 fused call of n tokens and out_dim features is cut into
+    tiles on compute_units CUs (p3d_proj_cond_plan; host-only). Returns a
+    dict of the p3d_tile_plan fields."""
+    plan = p3d_tile_plan()
+    _check(lib.p3d_proj_cond_plan(int(n), int(out_dim), int(compute_units), ctypes.byref(plan)))
+    return {k: getattr(plan, k) for k, _ in p3d_tile_plan._fields_}
 
 
 def _maps(feat, batch):

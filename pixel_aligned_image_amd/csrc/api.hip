@@ -155,6 +155,16 @@ p3d_status prepare_proj_cond(const char* fn, const int32_t* coords, int64_t n,
     if (out_dim > kMaxOutDim)
         return fail(P3D_ERR_UNSUPPORTED, "%s: out_dim must be <= %d, got %d", fn, kMaxOutDim,
                     out_dim);
+    {
+        // tile counts are int32 in the launches: 128-token tiles of 512
+        // (BF16) or 128 (F32) features
+        const int64_t fw = dtype == P3D_BF16 ? 512 : 128;
+        const int64_t tiles = ((n + 127) / 128) * ((out_dim + fw - 1) / fw);
+        if (tiles >= ((int64_t)1 << 31))
+            return fail(P3D_ERR_UNSUPPORTED,
+                        "%s: %lld tokens x %d features make %lld tiles; the limit is 2^31 - 1",
+                        fn, (long long)n, out_dim, (long long)tiles);
+    }
     if (weight_in != channels) {
         const p3d_map& m0 = maps[0];
         if (n_maps == 1)
@@ -685,6 +695,28 @@ p3d_status p3d_stats_figures(const p3d_proj_stats* stats, const int32_t* channel
         }
     }
     out->cosine = stats->cos_count > 0.0 ? stats->cos_sum / stats->cos_count : NAN;
+    return ok();
+}
+
+p3d_status p3d_proj_cond_plan(int64_t n, int32_t out_dim, int32_t compute_units,
+                              p3d_tile_plan* plan) {
+    const char* fn = "p3d_proj_cond_plan";
+    if (!plan) return fail(P3D_ERR_INVALID_ARG, "%s: plan is NULL", fn);
+    if (n < 0 || n > kMaxTokens)
+        return fail(P3D_ERR_INVALID_ARG, "%s: n must be in [0, %lld], got %lld", fn,
+                    (long long)kMaxTokens, (long long)n);
+    if (out_dim < 1 || out_dim > kMaxOutDim)
+        return fail(P3D_ERR_INVALID_ARG, "%s: out_dim must be in [1, %d], got %d", fn,
+                    kMaxOutDim, out_dim);
+    if (compute_units < 1)
+        return fail(P3D_ERR_INVALID_ARG, "%s: compute_units must be >= 1, got %d", fn,
+                    compute_units);
+    const int64_t tiles = ((n + 127) / 128) * (((int64_t)out_dim + 511) / 512);
+    if (tiles >= ((int64_t)1 << 31))
+        return fail(P3D_ERR_UNSUPPORTED,
+                    "%s: %lld tokens x %d features make %lld tiles; the limit is 2^31 - 1", fn,
+                    (long long)n, out_dim, (long long)tiles);
+    *plan = plan_proj_cond_bf16(n, out_dim, compute_units);
     return ok();
 }
 

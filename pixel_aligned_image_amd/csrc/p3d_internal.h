@@ -274,5 +274,8 @@ hipError_t launch_proj_cond(const ProjCondArgs& a, p3d_dtype dt, const CamTable&
                             hipStream_t s);
 // bf16 fused kernel; writes the null rows too when a.n > 0
 hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hipStream_t s);
+// how that kernel cuts n tokens x D features into tiles on `cus` CUs (the
+// rule p3d_proj_cond_plan documents); host-only
+p3d_tile_plan plan_proj_cond_bf16(int64_t n, int32_t D, int32_t cus);
 
 }  // namespace p3d

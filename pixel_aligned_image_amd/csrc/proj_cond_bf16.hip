@@ -564,15 +564,36 @@ int device_cus() {
 // CUs / 2 tiles) takes one tile's time however many CUs it leaves idle: it
 // runs as 96-token tiles when those still fit one round, each with three
 // quarters of a tile's gather and products (and the same W stream).
-hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hipStream_t s) {
-    int32_t m_tiles = (int32_t)((a.n + BM - 1) / BM);
-    int32_t n_tiles = (a.D + BN - 1) / BN;
-    const int32_t tiles = m_tiles * n_tiles;
-    const int32_t cus = device_cus();
+p3d_tile_plan plan_proj_cond_bf16(int64_t n, int32_t D, int32_t cus) {
+    p3d_tile_plan p{};
+    p.tile_rows = BM;
+    p.feature_tiles = (D + BN - 1) / BN;
+    p.token_tiles = (int32_t)((n + BM - 1) / BM);
+    if (n == 0) return p;                          // no tiles
+    const int32_t tiles = p.token_tiles * p.feature_tiles;
     const int32_t rem = tiles % cus;
     int32_t split = 0;
     if (rem > 0 && rem * (TI / TI_QUARTER) <= cus) split = TI / TI_QUARTER;
     else if (rem > 0 && rem * (TI / TI_HALF) <= cus) split = TI / TI_HALF;
+    constexpr int RM = 16 * TI_ROUND;
+    const int32_t round_tiles = (int32_t)((n + RM - 1) / RM) * p.feature_tiles;
+    if (split == 0 && tiles < cus && round_tiles <= cus) {
+        p.tile_rows = RM;
+        p.token_tiles = (int32_t)((n + RM - 1) / RM);
+        p.whole_tiles = round_tiles;
+        return p;
+    }
+    p.whole_tiles = split ? tiles - rem : tiles;
+    p.part_rows = split ? BM / split : 0;
+    p.parts = split ? rem * split : 0;
+    return p;
+}
+
+hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hipStream_t s) {
+    const p3d_tile_plan plan = plan_proj_cond_bf16(a.n, a.D, device_cus());
+    int32_t m_tiles = plan.token_tiles;
+    int32_t n_tiles = plan.feature_tiles;
+    int32_t null_tiles = (int32_t)((a.n_null + plan.tile_rows - 1) / plan.tile_rows);
     // corner offsets fit 32 bits when every map is under 4 GiB
     const auto map_bytes = [&](int32_t H, int32_t W, int32_t C) {
         return (uint64_t)a.batch * (uint64_t)H * (uint64_t)W * (uint64_t)C * 2u;
@@ -581,35 +602,28 @@ hipError_t launch_proj_cond_bf16(const ProjCondArgs& a, const CamTable& cams, hi
                        (a.C1 == 0 || map_bytes(a.H1, a.W1, a.C1) < ((uint64_t)1 << 32));
     using yes = std::true_type;
     using no = std::false_type;
-    constexpr int RM = 16 * TI_ROUND;
-    if (split == 0 && tiles < cus) {
-        int32_t m_r = (int32_t)((a.n + RM - 1) / RM);
-        int32_t tiles_r = m_r * n_tiles;
-        if (tiles_r <= cus) {
-            int32_t per_xcd = (tiles_r + 7) / 8;
-            int32_t null_r = (int32_t)((a.n_null + RM - 1) / RM);
-            ProjCondArgs args = a;
-            CamTable tab = cams;
-            void* params[] = {&args, &tab, &m_r, &n_tiles, &tiles_r, &per_xcd, &null_r};
-            const auto pick = [&](auto two_maps, auto o32) -> const void* {
-                constexpr bool T = decltype(two_maps)::value, O = decltype(o32)::value;
-                return reinterpret_cast<const void*>(&proj_cond_bf16_round_kernel<T, O>);
-            };
-            const void* fn = a.C1 > 0 ? (off32 ? pick(yes{}, yes{}) : pick(yes{}, no{}))
-                                      : (off32 ? pick(no{}, yes{}) : pick(no{}, no{}));
-            return hipLaunchKernel(fn, dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
-        }
-    }
-    int32_t n_big = split ? tiles - rem : tiles;
-    int32_t n_small = split ? rem * split : 0;
-    int32_t big_per_xcd = (n_big + 7) / 8;
-    int32_t small_per_xcd = (n_small + 7) / 8;
-    int32_t null_tiles = (int32_t)((a.n_null + BM - 1) / BM);
     ProjCondArgs args = a;
     CamTable tab = cams;
+    if (plan.tile_rows != BM) {
+        // one round of 96-token tiles
+        int32_t tiles = plan.whole_tiles;
+        int32_t per_xcd = (tiles + 7) / 8;
+        void* params[] = {&args, &tab, &m_tiles, &n_tiles, &tiles, &per_xcd, &null_tiles};
+        const auto pick = [&](auto two_maps, auto o32) -> const void* {
+            constexpr bool T = decltype(two_maps)::value, O = decltype(o32)::value;
+            return reinterpret_cast<const void*>(&proj_cond_bf16_round_kernel<T, O>);
+        };
+        const void* fn = a.C1 > 0 ? (off32 ? pick(yes{}, yes{}) : pick(yes{}, no{}))
+                                  : (off32 ? pick(no{}, yes{}) : pick(no{}, no{}));
+        return hipLaunchKernel(fn, dim3((unsigned)per_xcd * 8), dim3(kThreads), params, 0, s);
+    }
+    int32_t n_big = plan.whole_tiles;
+    int32_t n_small = plan.parts;
+    int32_t big_per_xcd = (n_big + 7) / 8;
+    int32_t small_per_xcd = (n_small + 7) / 8;
     void* params[] = {&args,    &tab,        &m_tiles,       &n_tiles,   &n_big,
                       &big_per_xcd, &n_small, &small_per_xcd, &null_tiles};
-    const bool half = split == TI / TI_HALF;
+    const bool half = plan.part_rows == 16 * TI_HALF;
     const auto pick = [&](auto two_maps, auto o32) -> const void* {
         constexpr bool T = decltype(two_maps)::value, O = decltype(o32)::value;
         return half ? reinterpret_cast<const void*>(&proj_cond_bf16_kernel<T, O, TI_HALF>)

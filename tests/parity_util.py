@@ -209,29 +209,17 @@ def run_sample(p3d, o, feat_np, grid_np, bidx_np, bf16_in, out_bf16):
     return np.max(err), np.corrcoef(g.ravel(), ref.ravel())[0, 1] if g.size > 1 else 1.0
 
 
-def tile_edge_rows(n, D, cus, bm=128, bn=512):
+def tile_edge_rows(n, D, cus):
     """First and last token row of every whole tile and of every tail part of
-    the fused bf16 launch (128-token tiles, 512-feature N tiles; the tiles
-    past the last full round on `cus` compute units run as 32- or 64-token
-    parts when four or two times that many fit one round; a launch of fewer
-    tiles than CUs that neither split fits runs as 96-token tiles when those
-    fit one round)."""
-    m_tiles = -(-n // bm)
-    n_tiles = -(-D // bn)
-    tiles = m_tiles * n_tiles
-    rem = tiles % cus
-    split = 4 if rem and rem * 4 <= cus else (2 if rem and rem * 2 <= cus else 1)
-    if split == 1 and tiles < cus and -(-n // 96) * n_tiles <= cus:
-        lo = np.arange(0, n, 96)
-        return np.unique(np.concatenate([lo, np.minimum(lo + 95, n - 1)]).astype(np.int64))
+    the fused bf16 launch of n tokens and D features on `cus` compute units,
+    as the library's tiling rule (p3d_proj_cond_plan) cuts it."""
+    import pixel_aligned_image_amd as p3d
+    plan = p3d.p3d_proj_cond_plan(n, D, cus)
+    bm, nt = plan["tile_rows"], plan["feature_tiles"]
+    first_split = plan["whole_tiles"] // nt          # token tiles before the split ones
     rows = []
-    for mt in range(m_tiles):
-        first = mt * n_tiles
-        parts = split if first >= tiles - rem or (first + n_tiles - 1) >= tiles - rem else 1
-        step = bm // parts
-        for p in range(parts):
-            lo = mt * bm + p * step
-            hi = min(lo + step, n) - 1
-            if lo < n:
-                rows += [lo, hi]
+    for mt in range(plan["token_tiles"]):
+        step = plan["part_rows"] if plan["parts"] and mt >= first_split else bm
+        for lo in range(mt * bm, min((mt + 1) * bm, n), step):
+            rows += [lo, min(lo + step, n) - 1]
     return np.unique(np.array(rows, np.int64))

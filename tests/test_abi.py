@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(p3d):
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     lib = ctypes.CDLL(p3d.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -117,6 +117,9 @@ def _pc(p3d, **kw):
     (dict(H=65536, W=65536), 4, "2^31"),
     (dict(n=(1 << 30) + 1), 4, "n must be <="),
     (dict(D=(1 << 20) + 8), 4, "out_dim must be <="),
+    # 2^23 token tiles x 2048 feature tiles: past the int32 tile counts
+    (dict(n=1 << 30, D=1 << 20), 4, "tiles"),
+    (dict(dtype=0, C=64, n=1 << 30, D=1 << 18), 4, "tiles"),
 ], ids=lambda v: str(v)[:40])
 def test_proj_cond_validation(p3d, kw, status, needle):
     st, msg = _pc(p3d, **kw)
@@ -357,6 +360,48 @@ def test_proj_cond_ws_validation(p3d):
     # nothing to do: no workspace needed
     assert lib.p3d_proj_cond_ws(None, 0, 8, 0, cams, 1, p3d.P3D_BF16, one, 1, 4096, 32, 16,
                                 None, 0, 8192, None, None, 0, None) == p3d.P3D_OK
+
+
+@pytest.mark.parametrize("n,D,cus,want", [
+    # 782 x 3 = 2346 tiles = 9 rounds of 256 + 42: 4 x 42 <= 256, quarters
+    (100000, 1536, 256, dict(tile_rows=128, token_tiles=782, feature_tiles=3,
+                             whole_tiles=2304, part_rows=32, parts=168)),
+    # 1563 x 3 = 4689 = 18 x 256 + 81: 4 x 81 > 256 >= 2 x 81, halves
+    (200000, 1536, 256, dict(tile_rows=128, token_tiles=1563, feature_tiles=3,
+                             whole_tiles=4608, part_rows=64, parts=162)),
+    # 55 x 3 = 165 tiles: no split fits; 73 x 3 = 219 tiles of 96 tokens do
+    (7000, 1536, 256, dict(tile_rows=96, token_tiles=73, feature_tiles=3,
+                           whole_tiles=219, part_rows=0, parts=0)),
+    # 192 tiles -> exactly 256 of 96; one token more -> 257, so 193 whole
+    (24576, 512, 256, dict(tile_rows=96, token_tiles=256, feature_tiles=1,
+                           whole_tiles=256, part_rows=0, parts=0)),
+    (24577, 512, 256, dict(tile_rows=128, token_tiles=193, feature_tiles=1,
+                           whole_tiles=193, part_rows=0, parts=0)),
+    # whole rounds only; one token (a single tile as four parts); no tokens
+    (32768, 512, 256, dict(tile_rows=128, token_tiles=256, feature_tiles=1,
+                           whole_tiles=256, part_rows=0, parts=0)),
+    (1, 8, 256, dict(tile_rows=128, token_tiles=1, feature_tiles=1,
+                     whole_tiles=0, part_rows=32, parts=4)),
+    (0, 1000, 256, dict(tile_rows=128, token_tiles=0, feature_tiles=2,
+                        whole_tiles=0, part_rows=0, parts=0)),
+    # one CU: every tile count is a whole number of rounds
+    (1000, 8, 1, dict(tile_rows=128, token_tiles=8, feature_tiles=1,
+                      whole_tiles=8, part_rows=0, parts=0)),
+])
+def test_proj_cond_plan(p3d, n, D, cus, want):
+    """The documented tiling rule, worked by hand for each case."""
+    assert p3d.p3d_proj_cond_plan(n, D, cus) == want
+
+
+def test_proj_cond_plan_refusals(p3d):
+    for args, status, needle in (((-1, 8, 256), 1, "n must be"), (((1 << 30) + 1, 8, 256), 1, "n must be"),
+                                 ((10, 0, 256), 1, "out_dim"), ((10, (1 << 20) + 1, 256), 1, "out_dim"),
+                                 ((10, 8, 0), 1, "compute_units"),
+                                 ((1 << 30, 1 << 20, 256), 4, "tiles")):
+        with pytest.raises(p3d.P3DError) as e:
+            p3d.p3d_proj_cond_plan(*args)
+        assert e.value.status == status and needle in p3d.p3d_last_error(), args
+    assert p3d.lib.p3d_proj_cond_plan(10, 8, 256, None) == p3d.P3D_ERR_INVALID_ARG
 
 
 def test_stats_figures_closed_forms(p3d):

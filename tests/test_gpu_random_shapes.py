@@ -88,14 +88,14 @@ def _draw_half(i):
 
 
 def _regime(c):
-    """How a launch of T tiles (of 128 tokens) runs on CUS compute units."""
-    T = c["T"]
-    rem = T % CUS
-    tail = "quarters" if rem and 4 * rem <= CUS else "halves" if rem and 2 * rem <= CUS else ""
-    if c["bf16"] and not tail and T < CUS and -(-c["n"] // 96) * -(-c["D"] // 512) <= CUS:
-        return "round96"                 # one round of 96-token tiles
-    whole = T - rem if tail else T
-    return "+".join(x for x in (["whole"] if whole else []) + ([tail] if tail else []))
+    """How a launch of T tiles (of 128 tokens) runs on CUS compute units, by
+    the library's tiling rule (p3d_proj_cond_plan; the fp32 path has no
+    parts or 96-token tiles, so its cases are named by the same counts)."""
+    plan = p3d.p3d_proj_cond_plan(c["n"], c["D"], CUS)
+    if plan["tile_rows"] != 128:
+        return "round96" if c["bf16"] else "whole"
+    tail = {32: "quarters", 64: "halves"}.get(plan["part_rows"], "")
+    return "+".join(x for x in (["whole"] if plan["whole_tiles"] else []) + ([tail] if tail else []))
 
 
 CASES = [_draw(i) for i in range(40)] + [_draw_half(i) for i in range(40, 52)]

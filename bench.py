@@ -291,10 +291,13 @@ def config_line(p3d, synth, name, stream, reps):
             "map": "%dx%dx%dx%d" % tuple(feat.shape),
             "proj_linear": "%d->%d%s" % (w.channels, w.out_dim, " +bias" if bias is not None
                                          else ""),
-            "kernel": "proj_cond_bf16_kernel" if bf16 else "proj_cond_kernel",
+            "kernel": bf16_kernel_name(p3d, False, n, w.out_dim) if bf16 else "proj_cond_kernel",
             "mean_ms": ms, "tokens_per_s": n / (ms * 1e-3), "bound": "mfma",
             "flops_per_launch": flops, "achieved": flops / (ms * 1e-3) / 1e12, "peak": peak,
             "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / peak}
+    if bf16:
+        line["tiling"] = p3d.p3d_proj_cond_plan(
+            n, w.out_dim, torch.cuda.get_device_properties(0).multi_processor_count)
     if bf16 and coords is not None:
         order, run_order = make_order(p3d, coords, n, w.resolution, camarr, [feat], w.points)
         ordf = lambda: p3d.p3d_proj_cond(coords, n, w.resolution, camarr, feat, weight, out,

@@ -24,7 +24,8 @@ Prints ONE JSON line. Fields beyond the common ones:
   order_ms          the token order's share of the step (events likewise).
   cpu_baseline      the CPU oracle on a bounded prefix of the same tokens, on
                     every core of the affinity mask and on one thread.
-  gather            the standalone bilinear gather on the same points:
+  gather            the standalone bilinear gather on the same points, in
+                    the step's token order when the step has one:
                     algorithmic bytes / duration against peak HBM bandwidth
                     and against the measured copy ceiling.
   hbm_copy_ceiling  a streaming device copy (p3d_stream_copy, 16-byte
@@ -357,11 +358,11 @@ EXTRAS = ("configs", "variants", "channel_sweep", "cascade", "two_maps", "gemm_r
 
 
 def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
-              headline_flops=None, ordered_gather=None):
+              headline_flops=None, caller_order_gather=None):
     """Adjacent parts on their own workloads (the names in `which`):
       configs        the fused call on every other workload, own roofline;
-      variants       the headline's fused kernel without the token order, the
-                     standalone gather with it;
+      variants       the headline's fused kernel and its standalone gather
+                     without the token order (the caller's order);
       channel_sweep  the headline's fused kernel (token order, no null rows)
                      on maps of 512 .. 2048 channels: a line through the
                      means splits the launch into a fixed cost (tile starts
@@ -395,16 +396,16 @@ def run_extra(p3d, synth, stream, reps, lead_step, which, unordered_step=None,
             "frac": headline_flops / (ums * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "note": "the headline's fused call without the token order (p3d_proj_cond): "
                     "tokens in the caller's (x, y, z) order"}
-        if ordered_gather is not None:
-            g, gbytes = ordered_gather
+        if caller_order_gather is not None:
+            g, gbytes = caller_order_gather
             for _ in range(reps):
                 g()
             gms = time_events(g, reps, stream)
-            out["ordered_gather"] = {
+            out["caller_order_gather"] = {
                 "kernel": "sample_kernel", "mean_ms": gms,
                 "frac": gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                "note": "the standalone gather at the same points in the step's token order "
-                        "(p3d_bilinear_sample_ordered)"}
+                "note": "the standalone gather at the same points in the caller's (x, y, z) "
+                        "order (p3d_bilinear_sample)"}
     if "configs" in which:
         out["configs"] = [config_line(p3d, synth, w.name, stream, reps)
                           for w in synth.WORKLOADS if w.name != DEFAULT_WORKLOAD]
@@ -709,7 +710,18 @@ def main():
         p3d.p3d_proj_cond(coords_d, n, w.resolution, camarr, feat, weight, out, bias=bias,
                           n_null=n_null, mask=mask)
 
+    # An idle GPU takes tens of milliseconds of work to reach its working
+    # clocks: untimed steps run for a fixed 0.3 s before the side
+    # measurements and again before the timed steps.
+    def settle():
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < 0.3:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+
     # ---- side measurements first; the standalone gather on the same points
+    settle()
     grid = torch.empty((n, 2), device="cuda")
     pixel = torch.empty((n, 2), dtype=torch.int32, device="cuda")
     p3d.p3d_project_points(coords_d, n, w.resolution, camarr, w.height, w.width, grid=grid,
@@ -719,18 +731,19 @@ def main():
     bidx = dev(bidx_np)
     s_out = torch.empty((n, w.channels), dtype=dt, device="cuda")
 
-    # the standalone gather at the same points, in the caller's order (the
-    # same points in the step's token order, p3d_bilinear_sample_ordered, are
-    # timed with the adjacent parts)
+    # the standalone gather at the same points, in the step's token order
+    # (p3d_bilinear_sample_ordered; the same points in the caller's order,
+    # p3d_bilinear_sample, are timed with the adjacent parts)
     def gather_only():
         p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx)
 
     def gather_ordered():
         p3d.p3d_bilinear_sample(feat, grid, s_out, batch_index=bidx, order=order)
 
+    gather_line = gather_ordered if ordered else gather_only
     for _ in range(reps):
-        gather_only()
-    gather_ms = time_events(gather_only, reps, stream)
+        gather_line()
+    gather_ms = time_events(gather_line, reps, stream)
 
     # the null-branch fill alone (its own kernel when there are no tokens)
     out_null = out[n:]
@@ -747,14 +760,8 @@ def main():
     copy = hbm_copy_ceiling(p3d, stream, reps)
     torch.cuda.synchronize()
 
-    # ---- the timed steps. An idle GPU takes tens of milliseconds of work to
-    # reach its working clocks, so untimed steps run for a fixed 0.3 s before
-    # the W warmup steps.
-    t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < 0.3:
-        for _ in range(10):
-            step()
-        torch.cuda.synchronize()
+    # ---- the timed steps, after the clock settle and the W warmup steps
+    settle()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -823,7 +830,8 @@ def main():
                    "frac": gather_gbs / HBM_PEAK_GBS,
                    "frac_of_copy_ceiling": gather_gbs / copy["achieved"],
                    "kernel": "sample_kernel", "mean_ms": gather_ms,
-                   "call": "p3d_bilinear_sample",
+                   "call": ("p3d_bilinear_sample_ordered (the step's token order)" if ordered
+                            else "p3d_bilinear_sample"),
                    "traffic": recorded_traffic("sample_kernel", w.name),
                    "algorithmic_bytes_per_launch": gather_bytes},
         "hbm_copy_ceiling": copy,
@@ -836,7 +844,7 @@ def main():
     if not args.no_extra:
         line["extra"] = run_extra(p3d, synth, stream, reps, step, which,
                                   unordered_step if ordered else None, flops,
-                                  (gather_ordered, gather_bytes) if ordered else None)
+                                  (gather_only, gather_bytes) if ordered else None)
     if not args.no_cpu_baseline:
         import oracle
         o = oracle.get()

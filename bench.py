@@ -824,7 +824,10 @@ def main():
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": kname, "mean_ms": fused_ms,
                      "algorithmic_flops_per_launch": flops,
-                     "algorithmic_bytes_per_launch": fused_bytes},
+                     "algorithmic_bytes_per_launch": fused_bytes,
+                     "tiling": (p3d.p3d_proj_cond_plan(
+                         n, D, torch.cuda.get_device_properties(0).multi_processor_count)
+                                if bf16 else None)},
         "gather": {"bound": "hbm", "achieved": gather_gbs,
                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
                    "frac": gather_gbs / HBM_PEAK_GBS,

@@ -1,4 +1,4 @@
-"""The image-space token order over a seeded sweep of inputs.
+"""The image-space token order over a seeded sweep of 60 inputs.
 
 Each case draws (from one fixed seed) the grid resolution, the batch, the
 token count (1 to about 60000, so the 1024-token bin workgroups end ragged),
@@ -49,7 +49,7 @@ def _draw(i):
     return dict(i=i, R=R, B=B, n=n, kH=kH, kW=kW, spill=spill, pts=pts)
 
 
-CASES = [_draw(i) for i in range(30)]
+CASES = [_draw(i) for i in range(60)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=["%d_R%d_b%d_n%d_%dx%d_%s" % (

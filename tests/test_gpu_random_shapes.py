@@ -98,7 +98,8 @@ def _regime(c):
     return "+".join(x for x in (["whole"] if plan["whole_tiles"] else []) + ([tail] if tail else []))
 
 
-CASES = [_draw(i) for i in range(40)] + [_draw_half(i) for i in range(40, 52)]
+CASES = ([_draw(i) for i in range(40)] + [_draw_half(i) for i in range(40, 52)] +
+         [_draw(i) for i in range(1000, 1040)])
 
 
 @pytest.mark.parametrize("case", CASES, ids=["%d_%s_T%d" % (c["i"], _regime(c), c["T"])
